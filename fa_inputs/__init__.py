@@ -1,0 +1,232 @@
+"""Seeded synthetic inputs and workload accounting for the attention path.
+
+This module is shared by the tests, the benchmark and the smoke check.  It
+holds no attention arithmetic: it draws seeded normal tensors, rounds them
+to bf16 bit patterns, defines the five workloads and counts their credited
+FLOPs and minimum bytes.
+
+Workloads (all tensors [B, H, N, d], contiguous, entries iid N(0, 1)):
+  1  single head, N=256, d=64, fp32, non-causal, scale 1/8
+  2  B=4, H=32, N=2048, d=128, bf16, non-causal
+  3  B=1, H=32, N=8192, d=128, bf16, causal
+  4  B=8, H=32, padded N=32768, d=128, bf16, causal + per-sequence key
+     lengths (sequence 0 has length 0; the rest uniform in [1, N]);
+     Q drawn x30 before rounding so raw scores reach about +-90
+  5  B=2, H=32, N=8192, d=128, bf16, causal, forward + backward with dO
+
+The 8,192-token, d=128, 32-head shape is the running example of the source
+pages ("What is FlashAttention?" Step 1; "FlashAttention" byte-accounting
+panel; "Explain FlashAttention and why it is IO-aware", byte arithmetic);
+these seeded tensors stand in for real activations.
+
+Random streams: numpy default_rng([seed, tensor_id, b, h]) (PCG64 seeded via
+SeedSequence) with tensor_id Q=0, K=1, V=2, dO=3; lengths use
+default_rng([seed, 4]).  Draws are float32 standard normals; bf16 tensors
+are rounded to nearest-even from them.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+__all__ = [
+    "Config", "CONFIGS", "TENSOR_IDS",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "widen",
+    "make_lengths", "make_head", "make_tensor", "make_inputs",
+    "credited_flops", "useful_pairs", "useful_flops", "min_bytes",
+]
+
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3, "lengths": 4}
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    cid: int
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str            # "f32" or "bf16"
+    causal: bool
+    lengths: str | None   # None, or "zero_then_uniform"
+    q_mult: float = 1.0
+    backward: bool = False
+
+    @property
+    def scale(self) -> float:
+        """fp32 value of 1/sqrt(d), the scale every workload uses."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+
+CONFIGS = {
+    1: Config(1, "single-head N=256 d=64 fp32 non-causal", 1, 1, 256, 64, "f32", False, None),
+    2: Config(2, "B=4 H=32 N=2048 d=128 bf16 non-causal", 4, 32, 2048, 128, "bf16", False, None),
+    3: Config(3, "B=1 H=32 N=8192 d=128 bf16 causal", 1, 32, 8192, 128, "bf16", True, None),
+    4: Config(4, "B=8 H=32 N=32768 d=128 bf16 causal+key-lengths Qx30", 8, 32, 32768, 128,
+              "bf16", True, "zero_then_uniform", q_mult=30.0),
+    5: Config(5, "B=2 H=32 N=8192 d=128 bf16 causal fwd+bwd", 2, 32, 8192, 128, "bf16",
+              True, None, backward=True),
+}
+
+
+# ---------------------------------------------------------------------------
+# bf16 bit patterns
+# ---------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x):
+    """Round float32 values to bf16 (nearest, ties to even); uint16 bits.
+
+    NaN stays NaN (quiet); infinities and overflow to infinity follow IEEE
+    rounding.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    rounded = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+               >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        rounded = np.where(nan, ((u >> np.uint32(16)) | np.uint32(0x0040)).astype(np.uint16),
+                           rounded)
+    return rounded
+
+
+def bf16_bits_to_f32(bits):
+    """Exact widening of bf16 bit patterns to float32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def widen(arr, dtype):
+    """Exact float64 values of a device-format array (fp32, or bf16 bits)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(arr).astype(np.float64)
+    return np.asarray(arr, dtype=np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Seeded generation
+# ---------------------------------------------------------------------------
+
+def make_lengths(cfg: Config, seed: int = 0):
+    """Per-sequence key lengths (int32 [B]) or None."""
+    if cfg.lengths is None:
+        return None
+    if cfg.lengths != "zero_then_uniform":
+        raise ValueError(f"unknown lengths recipe {cfg.lengths!r}")
+    rng = np.random.default_rng([seed, TENSOR_IDS["lengths"]])
+    rest = rng.integers(1, cfg.N, endpoint=True, size=cfg.B - 1)
+    return np.concatenate([[0], rest]).astype(np.int32)
+
+
+def make_head(cfg: Config, name: str, b: int, h: int, seed: int = 0, N: int | None = None,
+              d: int | None = None):
+    """One head's [N, d] tensor in device format (float32, or bf16 bits)."""
+    N = cfg.N if N is None else N
+    d = cfg.d if d is None else d
+    rng = np.random.default_rng([seed, TENSOR_IDS[name], b, h])
+    x = rng.standard_normal(N * d, dtype=np.float32).reshape(N, d)
+    if name == "q" and cfg.q_mult != 1.0:
+        x = x * np.float32(cfg.q_mult)
+    if cfg.dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    return x
+
+
+def make_tensor(cfg: Config, name: str, seed: int = 0, threads: int | None = None,
+                B: int | None = None, H: int | None = None, N: int | None = None,
+                d: int | None = None):
+    """Full [B, H, N, d] tensor in device format, built head by head.
+
+    Heads are drawn in parallel threads (numpy releases the GIL while it
+    fills arrays); the result does not depend on the thread count.
+    """
+    B = cfg.B if B is None else B
+    H = cfg.H if H is None else H
+    N = cfg.N if N is None else N
+    d = cfg.d if d is None else d
+    out = np.empty((B, H, N, d), np.uint16 if cfg.dtype == "bf16" else np.float32)
+
+    def fill(bh):
+        b, h = divmod(bh, H)
+        out[b, h] = make_head(cfg, name, b, h, seed, N, d)
+
+    if threads is None:
+        threads = min(16, len(os.sched_getaffinity(0)))
+    if threads <= 1 or B * H == 1:
+        for bh in range(B * H):
+            fill(bh)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, range(B * H)))
+    return out
+
+
+def make_inputs(cfg: Config, seed: int = 0, with_grad: bool | None = None, **shape_overrides):
+    """Dict of device-format host arrays for a workload: q, k, v (and do),
+    lengths (int32 [B] or None) and scale (float)."""
+    with_grad = cfg.backward if with_grad is None else with_grad
+    names = ["q", "k", "v"] + (["do"] if with_grad else [])
+    res = {n: make_tensor(cfg, n, seed, **shape_overrides) for n in names}
+    res["lengths"] = make_lengths(cfg, seed)
+    res["scale"] = cfg.scale
+    return res
+
+
+# ---------------------------------------------------------------------------
+# Work accounting
+# ---------------------------------------------------------------------------
+
+def credited_flops(B, H, N, d, causal, backward=False):
+    """FLOPs credited to one call.
+
+    Forward: 4 N^2 d per head, halved for a causal model, the throughput
+    convention of "FlashAttention" (deepconcepts.dev), "Checking it on a real
+    system".  Backward: 10 N^2 d per head (five N x N x d contractions: the S
+    recompute, dP, dV, dK and dQ), halved when causal.
+    """
+    per_head = (10 if backward else 4) * N * N * d
+    total = per_head * B * H
+    return total // 2 if causal else total
+
+
+def useful_pairs(N, causal, lengths=None, B=1):
+    """Visible (query, key) pairs per head, summed over the batch: with key
+    length L (clamped to [0, N]) and the causal mask, row i sees min(i+1, L)
+    keys; without it, L keys."""
+    total = 0
+    for b in range(B):
+        L = N if lengths is None else int(min(max(int(lengths[b]), 0), N))
+        if causal:
+            total += L * (L + 1) // 2 + (N - L) * L
+        else:
+            total += N * L
+    return total
+
+
+def useful_flops(B, H, N, d, causal, lengths=None, backward=False):
+    """FLOPs on visible pairs only: 4d (forward) or 10d (backward) per pair."""
+    return (10 if backward else 4) * d * H * useful_pairs(N, causal, lengths, B)
+
+
+def min_bytes(B, H, N, d, es, backward=False):
+    """Minimum HBM bytes: every input read once, every output written once.
+
+    Forward: Q, K, V read and O written (es bytes each) plus one fp32 LSE per
+    row.  Backward: Q, K, V, O, dO read, dQ, dK, dV written, LSE read and the
+    fp32 row dot products D written and read once.
+    """
+    nd = B * H * N * d
+    rows = B * H * N
+    if not backward:
+        return 4 * nd * es + 4 * rows
+    return 8 * nd * es + 4 * rows + 8 * rows

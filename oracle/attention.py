@@ -1,0 +1,345 @@
+"""Float64 CPU oracle for exact scaled dot-product attention.
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.  Every function
+works on float64 NumPy arrays holding the exact values the GPU receives
+(bf16 or fp32 inputs widened without rounding); it shares no code with the
+HIP kernels.
+
+Layout: q, k, v, o, do are [B, H, N, d]; lse is [B, H, N]; lengths is a
+length-B integer array of key lengths (or None for "all N keys valid").
+
+Semantics (the plain definition the tiled method reaches exactly):
+  s_ij = scale * q_i . k_j, visible(i, j) = j < L_b and (not causal or j <= i);
+  for a row with a non-empty visible set V_i:
+      m_i = max_{j in V_i} s_ij,  l_i = sum_{j in V_i} exp(s_ij - m_i),
+      O_i = sum_{j in V_i} exp(s_ij - m_i) v_j / l_i,  LSE_i = m_i + ln l_i;
+  for a row with nothing visible: O_i = 0, LSE_i = -inf.
+
+Citations are to the three source pages:
+  [clozo]  "What is FlashAttention?" (interview.clozo.ai)
+  [deep]   "FlashAttention" (deepconcepts.dev)
+  [infra]  "Explain FlashAttention and why it is IO-aware"
+           (aiinfrainterviews.com)
+"""
+
+from __future__ import annotations
+
+
+import numpy as np
+
+__all__ = [
+    "visible_mask",
+    "scaled_scores",
+    "attention_materialised",
+    "attention_rows",
+    "online_row",
+    "attention_online",
+    "attention_backward",
+    "finite_difference_grads",
+]
+
+
+# ---------------------------------------------------------------------------
+# Masks and scores
+# ---------------------------------------------------------------------------
+
+def _clamp_length(length, n):
+    """Key length of one sequence, clamped to [0, n] (None means n)."""
+    if length is None:
+        return n
+    return int(min(max(int(length), 0), n))
+
+
+def visible_mask(rows, n_keys, causal, length=None, keys=None):
+    """Boolean [len(rows), len(keys)] mask of visible (query, key) pairs.
+
+    `keys` are absolute key positions (default: all n_keys of them).
+    Positions are absolute sequence positions, never tile-local ones
+    ([infra] "Executable recurrence, with an empty-state policy": the causal
+    mask uses global query and key positions across tile boundaries).  The
+    key-length mask hides keys j >= L_b; query rows are not masked.
+    """
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    keys = (np.arange(n_keys, dtype=np.int64) if keys is None
+            else np.asarray(keys, dtype=np.int64).reshape(-1))
+    vis = np.broadcast_to(keys[None, :] < _clamp_length(length, n_keys),
+                          (rows.size, keys.size)).copy()
+    if causal:
+        vis &= keys[None, :] <= rows[:, None]
+    return vis
+
+
+def scaled_scores(q_rows, k, scale):
+    """s = scale * q K^T for a block of query rows of one head.
+
+    [infra] "Keep only the state needed for the final weighted average":
+    scores are the query-key products times the scale, plus the mask.
+    """
+    return float(scale) * (np.asarray(q_rows, np.float64) @ np.asarray(k, np.float64).T)
+
+
+# ---------------------------------------------------------------------------
+# Route A: materialised stable softmax (the plain definition)
+# ---------------------------------------------------------------------------
+
+def _rows_materialised(q_rows, rows, k, v, scale, causal, length):
+    """O and LSE for the given absolute query rows of one head.
+
+    Stable softmax with the row maximum subtracted before exponentiation
+    ([deep] "Why it is allowed to be exact": subtracting the maximum keeps
+    exp representable without changing the ratio).
+    """
+    s = scaled_scores(q_rows, k, scale)
+    vis = visible_mask(rows, k.shape[0], causal, length)
+    s = np.where(vis, s, -np.inf)
+    nonempty = vis.any(axis=1)
+    m = np.where(nonempty, s.max(axis=1, initial=-np.inf), 0.0)
+    p = np.where(vis, np.exp(s - m[:, None]), 0.0)
+    l = p.sum(axis=1)
+    o = np.zeros((q_rows.shape[0], v.shape[1]), np.float64)
+    o[nonempty] = (p[nonempty] @ v) / l[nonempty, None]
+    lse = np.full(q_rows.shape[0], -np.inf)
+    lse[nonempty] = m[nonempty] + np.log(l[nonempty])
+    return o, lse
+
+
+def attention_materialised(q, k, v, scale, causal=False, lengths=None, row_block=512):
+    """Route A: exact attention by materialising each score row block.
+
+    This is the three-pass standard attention ([clozo] "Step 1: Why standard
+    attention is memory-bound"), done on the CPU in float64, blocked over
+    query rows only to bound host memory.  Returns (o, lse).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, v.shape[3]))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        length = None if lengths is None else lengths[b]
+        for h in range(H):
+            for r0 in range(0, N, row_block):
+                rows = np.arange(r0, min(N, r0 + row_block))
+                o[b, h, rows], lse[b, h, rows] = _rows_materialised(
+                    q[b, h, rows], rows, k[b, h], v[b, h], scale, causal, length)
+    return o, lse
+
+
+def attention_rows(q_head, k_head, v_head, rows, scale, causal=False, length=None):
+    """Route A restricted to selected absolute query rows of one head.
+
+    Used to check sampled outputs of full-size problems row by row.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    return _rows_materialised(np.asarray(q_head, np.float64)[rows], rows,
+                              np.asarray(k_head, np.float64),
+                              np.asarray(v_head, np.float64),
+                              scale, causal, length)
+
+
+# ---------------------------------------------------------------------------
+# Route B: the online recurrence
+# ---------------------------------------------------------------------------
+
+def online_row(scores, values, tile=2, *, dtype=np.float64,
+               subtract_max=True, rescale=True, return_state=False):
+    """Online softmax-weighted average of value rows for ONE query.
+
+    Re-written from the description of the recurrence in [infra] "Keep only
+    the state needed for the final weighted average" and the policy of
+    [infra] "Executable recurrence, with an empty-state policy":
+      * the state is (m, l, o): running maximum, running sum of exponentials
+        relative to m, and the value sum on the same scale;
+      * for each chunk of `tile` scores: m_new = max(m, max(chunk));
+        alpha = exp(m - m_new) (0 while the state is empty);
+        l = alpha*l + sum(exp(chunk - m_new)); o = alpha*o + exp(chunk - m_new) @ V;
+      * a chunk whose scores are all -inf (fully masked) is skipped, so
+        -inf - (-inf) is never evaluated;
+      * the result is o / l, or zeros when nothing was visible.
+
+    `scores` are already scaled and masked (-inf for masked keys).  Inputs
+    are validated as the page's reference does: one score per value row,
+    a positive integer tile, no NaN or +inf scores, finite values.
+
+    `subtract_max` and `rescale` exist ONLY so that negative tests can plant
+    the two classic mistakes ([deep] "Why it is allowed to be exact": drop
+    the rescale and the answer is wrong; drop the maximum subtraction and a
+    x30 magnitude overflows float32).  `dtype` selects the working precision
+    (float64 by default; float32 for the overflow demonstration).
+
+    Returns the output vector, or (output, trace) with return_state=True,
+    where trace lists (m, alpha, l, o) after every processed chunk.
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    if scores.ndim != 1 or values.ndim != 2 or scores.shape[0] != values.shape[0]:
+        raise ValueError("need exactly one score per value row")
+    if not isinstance(tile, int) or isinstance(tile, bool) or tile <= 0:
+        raise ValueError("tile must be a positive int")
+    if np.any(np.isnan(scores)) or np.any(np.isposinf(scores)):
+        raise ValueError("scores must be finite or -inf")
+    if not np.all(np.isfinite(values)):
+        raise ValueError("values must be finite")
+
+    f = np.dtype(dtype).type
+    s_all = scores.astype(dtype)
+    v_all = values.astype(dtype)
+    m = f(-np.inf)
+    l = f(0.0)
+    o = np.zeros(values.shape[1], dtype)
+    trace = []
+    with np.errstate(over="ignore", invalid="ignore"):
+        for start in range(0, s_all.shape[0], tile):
+            s = s_all[start:start + tile]
+            chunk_max = s.max()
+            if np.isneginf(chunk_max):
+                continue                      # fully masked chunk: state unchanged
+            m_new = max(m, chunk_max) if subtract_max else f(0.0)
+            if not rescale:
+                alpha = f(1.0)
+            elif np.isneginf(m):
+                alpha = f(0.0)                # empty state: nothing to rescale
+            else:
+                alpha = np.exp(m - m_new, dtype=dtype)
+            w = np.exp(s - m_new, dtype=dtype)
+            o = alpha * o + (w @ v_all[start:start + tile]).astype(dtype)
+            l = alpha * l + w.sum(dtype=dtype)
+            m = m_new
+            trace.append((float(m), float(alpha), float(l), o.astype(np.float64).copy()))
+        out = o / l if l != 0 else np.zeros_like(o)
+    if return_state:
+        return out.astype(np.float64), trace
+    return out.astype(np.float64)
+
+
+def attention_online(q, k, v, scale, causal=False, lengths=None, tile=64,
+                     return_state=False):
+    """Route B: the online recurrence over key chunks of width `tile`.
+
+    Vectorised over all query rows of a head; for each row the state (m, l, o)
+    follows [infra] "Keep only the state needed for the final weighted
+    average" and [deep] "Why it is allowed to be exact" (rescale both sums by
+    exp(m_old - m_new), divide by l after the last chunk).  Rows for which a
+    chunk is fully masked keep their state ([infra] "Executable recurrence,
+    with an empty-state policy").  Shares no code with route A beyond the
+    mask and score helpers.
+
+    Returns (o, lse) or, with return_state=True, (o, lse, m, l).
+    """
+    if not isinstance(tile, int) or isinstance(tile, bool) or tile <= 0:
+        raise ValueError("tile must be a positive int")
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    O = np.zeros((B, H, N, v.shape[3]))
+    LSE = np.empty((B, H, N))
+    M = np.empty((B, H, N))
+    L = np.empty((B, H, N))
+    rows = np.arange(N)
+    for b in range(B):
+        length = None if lengths is None else lengths[b]
+        for h in range(H):
+            m = np.full(N, -np.inf)
+            l = np.zeros(N)
+            o = np.zeros((N, v.shape[3]))
+            for j0 in range(0, Nk, tile):
+                cols = slice(j0, min(Nk, j0 + tile))
+                vis = visible_mask(rows, Nk, causal, length,
+                                   keys=np.arange(j0, min(Nk, j0 + tile)))
+                live = vis.any(axis=1)            # rows with something visible here
+                if not live.any():
+                    continue
+                s = scaled_scores(q[b, h, live], k[b, h, cols], scale)
+                s = np.where(vis[live], s, -np.inf)
+                m_old = m[live]
+                m_new = np.maximum(m_old, s.max(axis=1))
+                alpha = np.where(np.isneginf(m_old), 0.0,
+                                 np.exp(np.where(np.isneginf(m_old), 0.0, m_old - m_new)))
+                w = np.where(vis[live], np.exp(s - m_new[:, None]), 0.0)
+                o[live] = alpha[:, None] * o[live] + w @ v[b, h, cols]
+                l[live] = alpha * l[live] + w.sum(axis=1)
+                m[live] = m_new
+            done = l > 0
+            O[b, h, done] = o[done] / l[done, None]
+            LSE[b, h] = np.where(done, m + np.log(np.where(done, l, 1.0)), -np.inf)
+            M[b, h] = m
+            L[b, h] = l
+    if return_state:
+        return O, LSE, M, L
+    return O, LSE
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+
+def attention_backward(q, k, v, o, do, lse, scale, causal=False, lengths=None,
+                       row_block=512):
+    """Exact gradients of the scalar <dO, O> with respect to Q, K and V.
+
+    The pages fix only that the backward rebuilds S and P from Q, K, V and
+    the saved output and per-row statistics ([clozo] "Step 4: The backward
+    pass recomputes instead of storing"; [deep] "What it does not do").  The
+    formulas are the textbook softmax Jacobian, pinned by finite differences:
+        P_ij = exp(s_ij - LSE_i) on visible pairs, 0 elsewhere;
+        dV = P^T dO;  dP = dO V^T;  D_i = sum_t dO_it O_it;
+        dS = P * (dP - D);  dQ = scale dS K;  dK = scale dS^T Q.
+    Rows with nothing visible (LSE = -inf) contribute nothing.
+    Returns (dq, dk, dv).
+    """
+    q, k, v, o, do = (np.asarray(t, np.float64) for t in (q, k, v, o, do))
+    lse = np.asarray(lse, np.float64)
+    B, H, N, d = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        length = None if lengths is None else lengths[b]
+        for h in range(H):
+            for r0 in range(0, N, row_block):
+                rows = np.arange(r0, min(N, r0 + row_block))
+                s = scaled_scores(q[b, h, rows], k[b, h], scale)
+                vis = visible_mask(rows, k.shape[2], causal, length)
+                row_lse = lse[b, h, rows]
+                ok = vis & np.isfinite(row_lse)[:, None]
+                p = np.where(ok, np.exp(np.where(ok, s - row_lse[:, None], 0.0)), 0.0)
+                g = do[b, h, rows]
+                dv[b, h] += p.T @ g
+                dp = g @ v[b, h].T
+                D = np.sum(g * o[b, h, rows], axis=1)
+                ds = p * (dp - D[:, None])
+                dq[b, h, rows] = scale * (ds @ k[b, h])
+                dk[b, h] += scale * (ds.T @ q[b, h, rows])
+    return dq, dk, dv
+
+
+def finite_difference_grads(q, k, v, do, scale, causal=False, lengths=None, eps=1e-6):
+    """Central finite differences of <dO, O(q, k, v)> for every input element.
+
+    Brute-force check of attention_backward on tiny inputs; the forward used
+    is route A.  Cost is 2 * (#elements) forward passes.
+    """
+    q, k, v, do = (np.array(t, np.float64) for t in (q, k, v, do))
+
+    def loss(qq, kk, vv):
+        o, _ = attention_materialised(qq, kk, vv, scale, causal, lengths)
+        return float(np.sum(o * do))
+
+    grads = []
+    for which in range(3):
+        base = [q, k, v]
+        g = np.zeros_like(base[which])
+        it = np.nditer(base[which], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = [t.copy() for t in base]
+            minus = [t.copy() for t in base]
+            plus[which][idx] += eps
+            minus[which][idx] -= eps
+            g[idx] = (loss(*plus) - loss(*minus)) / (2.0 * eps)
+        grads.append(g)
+    return tuple(grads)

@@ -1,0 +1,87 @@
+"""Plant plausible mistakes in the oracle and check that its pins catch them.
+
+Each mutant patches the oracle on the CPU for the duration of one test and
+runs a pin from test_oracle_pins; the pin must fail.  This shows that the
+pins can see a dropped term, a wrong sign or index, or a transposed operand.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as oa
+from tests import test_oracle_pins as pins
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except (AssertionError, ValueError, FloatingPointError):
+        return True
+    return False
+
+
+def test_dropped_scale_is_caught(monkeypatch):
+    monkeypatch.setattr(oa, "scaled_scores",
+                        lambda q_rows, k, scale: np.asarray(q_rows) @ np.asarray(k).T)
+    assert _fails(pins.test_single_visible_key_closed_form)
+    assert _fails(pins.test_brute_force_every_mask_combination_tiny)
+
+
+def test_transposed_operand_is_caught(monkeypatch):
+    # S^T = k q^T in place of S = q k^T (shapes agree for square problems)
+    monkeypatch.setattr(oa, "scaled_scores",
+                        lambda q_rows, k, scale: float(scale) * (np.asarray(k) @ np.asarray(q_rows).T)
+                        if np.asarray(q_rows).shape == np.asarray(k).shape
+                        else float(scale) * np.asarray(q_rows) @ np.asarray(k).T)
+    assert _fails(pins.test_brute_force_every_mask_combination_tiny)
+
+
+def test_causal_off_by_one_is_caught(monkeypatch):
+    real = oa.visible_mask
+
+    def strict(rows, n_keys, causal, length=None, keys=None):
+        vis = real(rows, n_keys, causal, length, keys)
+        if causal:
+            rows_a = np.asarray(rows).reshape(-1)
+            keys_a = np.arange(n_keys) if keys is None else np.asarray(keys).reshape(-1)
+            vis &= keys_a[None, :] < rows_a[:, None]
+        return vis
+
+    monkeypatch.setattr(oa, "visible_mask", strict)
+    assert _fails(pins.test_single_visible_key_closed_form)
+    assert _fails(pins.test_brute_force_every_mask_combination_tiny)
+
+
+def test_length_off_by_one_is_caught(monkeypatch):
+    real = oa.visible_mask
+
+    def loose(rows, n_keys, causal, length=None, keys=None):
+        return real(rows, n_keys, causal, None if length is None else int(length) + 1, keys)
+
+    monkeypatch.setattr(oa, "visible_mask", loose)
+    assert _fails(pins.test_brute_force_every_mask_combination_tiny)
+    assert _fails(pins.test_empty_rows_return_zeros_and_neg_inf_lse)
+
+
+def test_wrong_backward_scale_is_caught(monkeypatch):
+    real = oa.attention_backward
+
+    def no_scale_in_dq(q, k, v, o, do, lse, scale, causal=False, lengths=None, row_block=512):
+        dq, dk, dv = real(q, k, v, o, do, lse, scale, causal, lengths, row_block)
+        return dq / scale, dk, dv
+
+    monkeypatch.setattr(oracle, "attention_backward", no_scale_in_dq)
+    assert _fails(pins.test_backward_matches_finite_differences, True, None)
+
+
+def test_swapped_backward_outputs_are_caught(monkeypatch):
+    real = oa.attention_backward
+
+    def swapped(*a, **kw):
+        dq, dk, dv = real(*a, **kw)
+        return dq, dv, dk
+
+    monkeypatch.setattr(oracle, "attention_backward", swapped)
+    assert _fails(pins.test_backward_matches_finite_differences, False, None)
+    assert _fails(pins.test_backward_invariants)
