@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Throughput of the exact-attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config C] [--gpus 1]
+
+A step is one pass of the whole path over one batch of seeded synthetic
+input: fa_forward (O and LSE), then the backward's three launches
+(row dot products, dK/dV, dQ) when the workload trains.  The default
+workload is the training step at N=8192, d=128 (B=2, H=32, bf16, causal);
+--config 3 times the causal forward alone.  Inputs are resident in HBM
+before the timed region starts.
+
+Prints ONE JSON line with the throughput in credited TFLOP/s (forward
+4 N^2 d per head, backward 10 N^2 d, halved for causal), the roofline of the
+dominant kernel (its credited FLOPs per launch over its average duration,
+timed with HIP events on the stream it runs on), and the fp64 CPU oracle
+timed on a bounded sample of the same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s at N=8192,d=128 bf16; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+PEAK_F32_TFLOPS = 157.3          # MI355X fp32 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("fa_common.hpp", "fa_fwd.hip", "fa_bwd.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_io_aware_41_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, config_id: int):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when they are missing or were taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    entry = data.get("kernels", {}).get(f"{kernel}@config{config_id}")
+    if not entry:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time for the oracle baseline sample (0 disables it)")
+    return p.parse_args()
+
+
+def cpu_baseline(cfg, inputs, budget_s):
+    """Time the fp64 oracle (forward, plus backward when the workload trains)
+    on whole heads of the workload until about budget_s seconds have passed."""
+    import numpy as np
+
+    import fa_inputs as fi
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
+    except Exception:  # noqa: BLE001 - report what we can
+        threads = 1
+    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    lengths = inputs.get("lengths")
+    flops = 0
+    elapsed = 0.0
+    done = 0
+    for (b, h) in heads:
+        w = {n: fi.widen(inputs[n][b:b + 1, h:h + 1], cfg.dtype)
+             for n in ("q", "k", "v", "do") if n in inputs}
+        lb = None if lengths is None else np.asarray(lengths)[b:b + 1]
+        t0 = time.perf_counter()
+        o, lse = oracle.attention_materialised(w["q"], w["k"], w["v"], cfg.scale, cfg.causal, lb)
+        if cfg.backward:
+            oracle.attention_backward(w["q"], w["k"], w["v"], o, w["do"], lse, cfg.scale,
+                                      cfg.causal, lb)
+        elapsed += time.perf_counter() - t0
+        flops += step_flops(cfg, lb, heads=1)
+        done += 1
+        if elapsed >= budget_s:
+            break
+    what = "forward+backward" if cfg.backward else "forward"
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads ({what}, fp64 materialised route), "
+                      f"{elapsed:.1f} s",
+            "seconds": round(elapsed, 2)}
+
+
+def step_flops(cfg, lengths=None, heads=None):
+    """Credited FLOPs of one step (all heads, or `heads` heads)."""
+    import fa_inputs as fi
+    H = cfg.H if heads is None else 1
+    B = cfg.B if heads is None else heads
+    if lengths is not None:
+        f = fi.useful_flops(B, H, cfg.N, cfg.d, cfg.causal, lengths)
+        if cfg.backward:
+            f += fi.useful_flops(B, H, cfg.N, cfg.d, cfg.causal, lengths, backward=True)
+        return f
+    f = fi.credited_flops(B, H, cfg.N, cfg.d, cfg.causal)
+    if cfg.backward:
+        f += fi.credited_flops(B, H, cfg.N, cfg.d, cfg.causal, backward=True)
+    return f
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the attention path has no cross-GPU step "
+              "(heads and batch shard with zero communication); run it with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_io_aware_41_amd as fa
+    import fa_inputs as fi
+
+    fa.load_library()                     # no library, no benchmark: fail loudly
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    cfg = fi.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.perf_counter()
+    inputs = fi.make_inputs(cfg)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s: {cfg.name}")
+
+    def up(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = up(inputs["q"]), up(inputs["k"]), up(inputs["v"])
+    do = up(inputs["do"]) if cfg.backward else None
+    lens = None if inputs["lengths"] is None else torch.from_numpy(inputs["lengths"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev)
+    if cfg.backward:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        delta = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev)
+
+    n_ev = 5 if cfg.backward else 2
+
+    def step(ev):
+        ev[0].record()
+        fa.forward(q, k, v, scale=cfg.scale, causal=cfg.causal, seqlens_k=lens, out=o, lse=lse)
+        ev[1].record()
+        if cfg.backward:
+            fa.backward_phases(q, k, v, o, do, lse, scale=cfg.scale, causal=cfg.causal,
+                               seqlens_k=lens, dq=dq, dk=dk, dv=dv, delta=delta,
+                               events=ev[1:5])
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+
+    events = [mk() for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(events[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"][:n_ev - 1]
+    per_kernel = {n: sum(e[i].elapsed_time(e[i + 1]) for e in events) / args.steps
+                  for i, n in enumerate(names)}
+    log("per-launch ms: " + ", ".join(f"{n}={t:.4f}" for n, t in per_kernel.items())
+        + f"; wall {wall * 1e3 / args.steps:.4f} ms/step")
+
+    lengths = inputs["lengths"]
+    flops = step_flops(cfg, lengths)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    # credited FLOPs per launch of each compute kernel
+    if lengths is None:
+        fwd_f = fi.credited_flops(cfg.B, cfg.H, cfg.N, cfg.d, cfg.causal)
+    else:
+        fwd_f = fi.useful_flops(cfg.B, cfg.H, cfg.N, cfg.d, cfg.causal, lengths)
+    kernel_flops = {"fwd": fwd_f}
+    if cfg.backward:
+        kernel_flops["bwd_dkdv"] = 2 * fwd_f       # S recompute, dP, dV, dK
+        kernel_flops["bwd_dq"] = fwd_f // 2        # dQ (its S/dP recompute is not credited)
+    dominant = max(kernel_flops, key=lambda n: per_kernel[n])
+    achieved = kernel_flops[dominant] / (per_kernel[dominant] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(dominant, args.config)}
+
+    extra = {
+        "per_launch_ms": {n: round(t, 4) for n, t in per_kernel.items()},
+        "kernel_tflops": {n: round(kernel_flops[n] / (per_kernel[n] * 1e-3) / 1e12, 1)
+                          for n in kernel_flops},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+    }
+    if cfg.backward:
+        fwd_ms = per_kernel["fwd"]
+        bwd_ms = sum(per_kernel[n] for n in names[1:])
+        extra["fwd_tflops"] = round(fwd_f / (fwd_ms * 1e-3) / 1e12, 1)
+        extra["bwd_tflops"] = round((flops - fwd_f) / (bwd_ms * 1e-3) / 1e12, 1)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("timing the fp64 CPU oracle on a sample ...")
+        cpu = cpu_baseline(cfg, inputs, args.cpu_seconds)
+
+    workload = {1: "single-head non-causal forward", 2: "non-causal forward",
+                3: "causal forward", 4: "causal forward with key lengths, Q x30",
+                5: "causal training step (forward + backward)"}[cfg.cid]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded iid N(0,1) inputs)",
+        "config": {"workload": workload, "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d,
+                   "causal": cfg.causal,
+                   "key_lengths": None if lengths is None else [int(x) for x in lengths],
+                   "credited_flops_per_step": flops},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

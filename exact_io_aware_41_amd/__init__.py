@@ -1,0 +1,274 @@
+"""Python binding of the gfx950 exact-attention library (libfa_mi355x.so).
+
+Two layers, both argument marshalling only (every step of the computation
+runs in the HIP kernels behind the C ABI of include/fa.h):
+
+* ``fa_forward``, ``fa_backward``, ``fa_backward_workspace_size``,
+  ``fa_status_string``, ``fa_abi_version``: the C entry points under the same
+  names, taking raw device addresses (ints) and returning status codes.
+* ``forward`` / ``backward``: the same calls on torch tensors (PyTorch
+  provides device memory and the current stream), raising ``FAError`` on any
+  non-success status.
+
+There is no fallback: if the shared library is missing, ``load_library``
+raises ``FALibraryMissing``; build it with ``python -m exact_io_aware_41_amd.build``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FA_SUCCESS", "FA_ERROR_INVALID_VALUE", "FA_ERROR_UNSUPPORTED", "FA_ERROR_LAUNCH",
+    "FA_DTYPE_F32", "FA_DTYPE_BF16", "EXPORTED_SYMBOLS",
+    "FAError", "FALibraryMissing", "LIB_PATH", "load_library",
+    "fa_abi_version", "fa_status_string", "fa_forward", "fa_backward",
+    "fa_backward_workspace_size", "fa_backward_preprocess", "fa_backward_dkdv",
+    "fa_backward_dq", "forward", "backward", "backward_phases",
+]
+
+FA_SUCCESS = 0
+FA_ERROR_INVALID_VALUE = 1
+FA_ERROR_UNSUPPORTED = 2
+FA_ERROR_LAUNCH = 3
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+
+EXPORTED_SYMBOLS = ("fa_abi_version", "fa_status_string", "fa_forward",
+                    "fa_backward_workspace_size", "fa_backward", "fa_backward_preprocess",
+                    "fa_backward_dkdv", "fa_backward_dq")
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_mi355x.so")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A non-success status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__(f"{where} failed: {fa_status_string(status)} ({status})")
+
+
+class FALibraryMissing(ImportError):
+    pass
+
+
+def load_library():
+    """Load libfa_mi355x.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FALibraryMissing(
+            f"{LIB_PATH} is not built; run `python -m exact_io_aware_41_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_abi_version.restype = i32
+    lib.fa_abi_version.argtypes = []
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [i32]
+    lib.fa_forward.restype = i32
+    lib.fa_forward.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, f32, i32, vp, vp, vp]
+    lib.fa_backward_workspace_size.restype = sz
+    lib.fa_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.fa_backward.restype = i32
+    lib.fa_backward.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, i32,
+                                vp, vp, vp, vp, sz, vp]
+    lib.fa_backward_preprocess.restype = i32
+    lib.fa_backward_preprocess.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.fa_backward_dkdv.restype = i32
+    lib.fa_backward_dkdv.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32,
+                                     i32, vp, vp, vp]
+    lib.fa_backward_dq.restype = i32
+    lib.fa_backward_dq.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, i32,
+                                   vp, vp]
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# C entry points (raw addresses)
+# ---------------------------------------------------------------------------
+
+def fa_abi_version() -> int:
+    return load_library().fa_abi_version()
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_forward(dtype, B, H, N, d, q, k, v, seqlens_k, scale, causal, o, lse, stream=0) -> int:
+    return load_library().fa_forward(dtype, B, H, N, d, q, k, v, seqlens_k, scale, causal, o,
+                                     lse, stream)
+
+
+def fa_backward_workspace_size(dtype, B, H, N, d) -> int:
+    return load_library().fa_backward_workspace_size(dtype, B, H, N, d)
+
+
+def fa_backward(dtype, B, H, N, d, q, k, v, o, dout, lse, seqlens_k, scale, causal, dq, dk, dv,
+                workspace, workspace_bytes, stream=0) -> int:
+    return load_library().fa_backward(dtype, B, H, N, d, q, k, v, o, dout, lse, seqlens_k, scale,
+                                      causal, dq, dk, dv, workspace, workspace_bytes, stream)
+
+
+def fa_backward_preprocess(dtype, B, H, N, d, o, dout, delta, stream=0) -> int:
+    return load_library().fa_backward_preprocess(dtype, B, H, N, d, o, dout, delta, stream)
+
+
+def fa_backward_dkdv(dtype, B, H, N, d, q, k, v, dout, lse, delta, seqlens_k, scale, causal, dk,
+                     dv, stream=0) -> int:
+    return load_library().fa_backward_dkdv(dtype, B, H, N, d, q, k, v, dout, lse, delta,
+                                           seqlens_k, scale, causal, dk, dv, stream)
+
+
+def fa_backward_dq(dtype, B, H, N, d, q, k, v, dout, lse, delta, seqlens_k, scale, causal, dq,
+                   stream=0) -> int:
+    return load_library().fa_backward_dq(dtype, B, H, N, d, q, k, v, dout, lse, delta, seqlens_k,
+                                         scale, causal, dq, stream)
+
+
+# ---------------------------------------------------------------------------
+# torch tensor wrappers
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    raise FAError(FA_ERROR_UNSUPPORTED, f"dtype {t.dtype}")
+
+
+def _check_like(name, t, ref):
+    if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+        raise ValueError(f"{name} must match q in shape, dtype and device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _lengths(seqlens_k, q):
+    import torch
+    if seqlens_k is None:
+        return None
+    if (seqlens_k.dtype != torch.int32 or seqlens_k.device != q.device
+            or seqlens_k.shape != (q.shape[0],) or not seqlens_k.is_contiguous()):
+        raise ValueError("seqlens_k must be a contiguous int32 [B] tensor on q's device")
+    return seqlens_k
+
+
+def forward(q, k, v, scale=None, causal=False, seqlens_k=None, out=None, lse=None):
+    """O, LSE = attention(q, k, v) for [B, H, N, d] CUDA tensors.
+
+    ``scale`` defaults to 1/sqrt(d); ``seqlens_k`` is an optional int32 [B]
+    tensor of key lengths.  Returns (o, lse) with lse fp32 [B, H, N].
+    """
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_like(name, t, q)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    seqlens_k = _lengths(seqlens_k, q)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_like("out", out, q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    st = fa_forward(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens_k),
+                    float(scale), int(bool(causal)), _ptr(out), _ptr(lse), _stream(q.device))
+    if st != FA_SUCCESS:
+        raise FAError(st, "fa_forward")
+    return out, lse
+
+
+def backward(q, k, v, o, do, lse, scale=None, causal=False, seqlens_k=None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV of <dO, O> for the tensors of a previous ``forward`` call."""
+    import torch
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_like(name, t, q)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    seqlens_k = _lengths(seqlens_k, q)
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_like(name, t, q)
+    code = _dtype_code(q)
+    ws_bytes = fa_backward_workspace_size(code, B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    st = fa_backward(code, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                     _ptr(seqlens_k), float(scale), int(bool(causal)), _ptr(dq), _ptr(dk),
+                     _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                     _stream(q.device))
+    if st != FA_SUCCESS:
+        raise FAError(st, "fa_backward")
+    return dq, dk, dv
+
+
+def backward_phases(q, k, v, o, do, lse, scale=None, causal=False, seqlens_k=None,
+                    dq=None, dk=None, dv=None, delta=None, events=None):
+    """``backward`` issued as its three launches (preprocess, dK/dV, dQ).
+
+    If ``events`` is a list of four torch.cuda.Event objects they are recorded
+    on the current stream before, between and after the launches, so each
+    launch can be timed on the stream it runs on.
+    """
+    import torch
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_like(name, t, q)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    seqlens_k = _lengths(seqlens_k, q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    code = _dtype_code(q)
+    stream = _stream(q.device)
+    rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+    rec(0)
+    st = fa_backward_preprocess(code, B, H, N, d, _ptr(o), _ptr(do), _ptr(delta), stream)
+    if st != FA_SUCCESS:
+        raise FAError(st, "fa_backward_preprocess")
+    rec(1)
+    st = fa_backward_dkdv(code, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+                          _ptr(delta), _ptr(seqlens_k), float(scale), int(bool(causal)), _ptr(dk),
+                          _ptr(dv), stream)
+    if st != FA_SUCCESS:
+        raise FAError(st, "fa_backward_dkdv")
+    rec(2)
+    st = fa_backward_dq(code, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+                        _ptr(delta), _ptr(seqlens_k), float(scale), int(bool(causal)), _ptr(dq),
+                        stream)
+    if st != FA_SUCCESS:
+        raise FAError(st, "fa_backward_dq")
+    rec(3)
+    return dq, dk, dv

@@ -1,0 +1,85 @@
+"""Build the gfx950 attention library in-tree with hipcc.
+
+    python -m exact_io_aware_41_amd.build
+
+produces exact_io_aware_41_amd/libfa_mi355x.so from csrc/ and include/.
+Every HIP translation unit is compiled for gfx950 only, with packed fp32
+VALU instructions disabled.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libfa_mi355x.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def common_flags() -> list[str]:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE, "-I", CSRC,
+        "-Wall", "-Wno-unused-function",
+    ]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
+                    if "packed-fp32-ops" not in line)
+    if res.returncode != 0:
+        raise RuntimeError(f"command failed ({res.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link the shared library.
+
+    Always recompiles.  The library is written to a temporary name and moved
+    into place, so a concurrent reader never sees a partial file.
+    """
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
+        objs = []
+        cmds = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            lang = ["-x", "hip"] if src.endswith(".hip") else []
+            cmds.append([cc, *common_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+            objs.append(obj)
+        with ThreadPoolExecutor(len(cmds)) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        tmp_lib = os.path.join(tmp, LIB_NAME)
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], verbose)
+        staged = LIB_PATH + ".tmp"
+        shutil.copyfile(tmp_lib, staged)
+        os.replace(staged, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    path = build(verbose="-v" in sys.argv)
+    print(path)

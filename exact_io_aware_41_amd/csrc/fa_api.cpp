@@ -1,0 +1,175 @@
+// fa_api.cpp - the C ABI declared in include/fa.h: argument validation,
+// dispatch on (dtype, d), and status codes.  Every check runs before any HIP
+// call, so an invalid call enqueues nothing and works without a GPU.
+
+#include "fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr long long kMaxGrid = 0x7fffffffLL;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool fwd_supported(fa_dtype dtype, int d) {
+  if (dtype == FA_DTYPE_F32) return d == 64 || d == 128;
+  if (dtype == FA_DTYPE_BF16) return d == 64 || d == 128;
+  return false;
+}
+
+bool bwd_supported(fa_dtype dtype, int d) { return dtype == FA_DTYPE_BF16 && (d == 64 || d == 128); }
+
+bool known_dtype(fa_dtype dtype) { return dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_BF16; }
+
+// Shared size/scale/flag checks.  Returns FA_SUCCESS when the problem is
+// well formed; *empty is set when there is nothing to compute.
+fa_status check_common(fa_dtype dtype, int B, int H, int N, int d, float scale, int causal,
+                       bool* empty) {
+  *empty = false;
+  if (!known_dtype(dtype)) return FA_ERROR_INVALID_VALUE;
+  if (B < 0 || H < 0 || N < 0 || d <= 0) return FA_ERROR_INVALID_VALUE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERROR_INVALID_VALUE;
+  if (causal != 0 && causal != 1) return FA_ERROR_INVALID_VALUE;
+  if (B == 0 || H == 0 || N == 0) *empty = true;
+  return FA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return kAbiVersion; }
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_SUCCESS: return "FA_SUCCESS";
+    case FA_ERROR_INVALID_VALUE: return "FA_ERROR_INVALID_VALUE";
+    case FA_ERROR_UNSUPPORTED: return "FA_ERROR_UNSUPPORTED";
+    case FA_ERROR_LAUNCH: return "FA_ERROR_LAUNCH";
+  }
+  return "FA_ERROR_UNKNOWN";
+}
+
+fa_status fa_forward(fa_dtype dtype, int B, int H, int N, int d, const void* q, const void* k,
+                     const void* v, const int32_t* seqlens_k, float scale, int causal, void* o,
+                     float* lse, hipStream_t stream) {
+  bool empty = false;
+  fa_status st = check_common(dtype, B, H, N, d, scale, causal, &empty);
+  if (st != FA_SUCCESS) return st;
+  if (!fwd_supported(dtype, d)) return FA_ERROR_UNSUPPORTED;
+  if (empty) return FA_SUCCESS;
+  if (!q || !k || !v || !o || !lse) return FA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERROR_INVALID_VALUE;
+  if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
+  const long long grid = dtype == FA_DTYPE_BF16 ? fa::fwd_bf16_grid(B, H, N, d)
+                                                : fa::fwd_f32_grid(B, H, N, d);
+  if (grid > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+
+  fa::FwdArgs a{B, H, N, d, q, k, v, seqlens_k, scale, causal, o, lse, stream};
+  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a) : fa::launch_fwd_f32(a);
+  return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+}
+
+size_t fa_backward_workspace_size(fa_dtype dtype, int B, int H, int N, int d) {
+  (void)dtype;
+  (void)d;
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+}
+
+fa_status fa_backward(fa_dtype dtype, int B, int H, int N, int d, const void* q, const void* k,
+                      const void* v, const void* o, const void* dout, const float* lse,
+                      const int32_t* seqlens_k, float scale, int causal, void* dq, void* dk,
+                      void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bool empty = false;
+  fa_status st = check_common(dtype, B, H, N, d, scale, causal, &empty);
+  if (st != FA_SUCCESS) return st;
+  if (!bwd_supported(dtype, d)) return FA_ERROR_UNSUPPORTED;
+  if (empty) return FA_SUCCESS;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return FA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(workspace))
+    return FA_ERROR_INVALID_VALUE;
+  if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < fa_backward_workspace_size(dtype, B, H, N, d)) return FA_ERROR_INVALID_VALUE;
+  if (fa::bwd_bf16_grid(B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+
+  fa::BwdArgs a{B,     H,       N,          d,      q,  k,  v,  o,  dout,
+                lse,   seqlens_k, scale,    causal, dq, dk, dv, static_cast<float*>(workspace),
+                stream};
+  const hipError_t e = fa::launch_bwd_bf16(a);
+  return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+}
+
+fa_status fa_backward_preprocess(fa_dtype dtype, int B, int H, int N, int d, const void* o,
+                                 const void* dout, float* delta, hipStream_t stream) {
+  bool empty = false;
+  // scale and causal do not enter this step; pass valid placeholders
+  fa_status st = check_common(dtype, B, H, N, d, 1.f, 0, &empty);
+  if (st != FA_SUCCESS) return st;
+  if (!bwd_supported(dtype, d)) return FA_ERROR_UNSUPPORTED;
+  if (empty) return FA_SUCCESS;
+  if (!o || !dout || !delta) return FA_ERROR_INVALID_VALUE;
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return FA_ERROR_INVALID_VALUE;
+  if (fa::bwd_bf16_grid(B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  fa::BwdArgs a{B, H, N, d, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, 1.f, 0,
+                nullptr, nullptr, nullptr, delta, stream};
+  return fa::launch_bwd_preprocess_bf16(a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+}
+
+namespace {
+fa_status check_bwd_phase(fa_dtype dtype, int B, int H, int N, int d, const void* q,
+                          const void* k, const void* v, const void* dout, const float* lse,
+                          const float* delta, const int32_t* seqlens_k, float scale, int causal,
+                          const void* out0, const void* out1, bool* empty) {
+  fa_status st = check_common(dtype, B, H, N, d, scale, causal, empty);
+  if (st != FA_SUCCESS) return st;
+  if (!bwd_supported(dtype, d)) return FA_ERROR_UNSUPPORTED;
+  if (*empty) return FA_SUCCESS;
+  if (!q || !k || !v || !dout || !lse || !delta || !out0 || !out1) return FA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
+      !aligned16(delta) || !aligned16(out0) || !aligned16(out1))
+    return FA_ERROR_INVALID_VALUE;
+  if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
+  if (fa::bwd_bf16_grid(B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  return FA_SUCCESS;
+}
+}  // namespace
+
+fa_status fa_backward_dkdv(fa_dtype dtype, int B, int H, int N, int d, const void* q,
+                           const void* k, const void* v, const void* dout, const float* lse,
+                           const float* delta, const int32_t* seqlens_k, float scale, int causal,
+                           void* dk, void* dv, hipStream_t stream) {
+  bool empty = false;
+  fa_status st = check_bwd_phase(dtype, B, H, N, d, q, k, v, dout, lse, delta, seqlens_k, scale,
+                                 causal, dk, dv, &empty);
+  if (st != FA_SUCCESS || empty) return st;
+  fa::BwdArgs a{B,     H,         N,     d,      q,       k,  v,  nullptr, dout,
+                lse,   seqlens_k, scale, causal, nullptr, dk, dv, const_cast<float*>(delta),
+                stream};
+  return fa::launch_bwd_dkdv_bf16(a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+}
+
+fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int N, int d, const void* q, const void* k,
+                         const void* v, const void* dout, const float* lse, const float* delta,
+                         const int32_t* seqlens_k, float scale, int causal, void* dq,
+                         hipStream_t stream) {
+  bool empty = false;
+  fa_status st = check_bwd_phase(dtype, B, H, N, d, q, k, v, dout, lse, delta, seqlens_k, scale,
+                                 causal, dq, dq, &empty);
+  if (st != FA_SUCCESS || empty) return st;
+  fa::BwdArgs a{B,     H,         N,     d,      q,  k,       v,       nullptr, dout,
+                lse,   seqlens_k, scale, causal, dq, nullptr, nullptr, const_cast<float*>(delta),
+                stream};
+  return fa::launch_bwd_dq_bf16(a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+}
+
+}  // extern "C"

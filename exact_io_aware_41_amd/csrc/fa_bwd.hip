@@ -1,0 +1,570 @@
+// fa_bwd.hip - backward kernels: gradients of <dO, O> by recomputation.
+//
+// Method ("What is FlashAttention?", Step 4; "FlashAttention", section "What
+// it does not do"; "Explain FlashAttention and why it is IO-aware", section
+// "Exact attention, finite precision and backward"): the forward keeps only
+// O and one statistic per row (here LSE); the backward rebuilds the score
+// and probability tiles on chip, P_ij = exp(s_ij - LSE_i), and never writes
+// an N x N matrix.  With D_i = sum_t dO_it O_it and dS = P * (dP - D):
+//   dV = P^T dO,  dP = dO V^T,  dK = scale dS^T Q,  dQ = scale dS K.
+//
+// Three launches on the caller's stream, no atomics (deterministic):
+//  1. row dot products D (memory-bound, one pass over O and dO);
+//  2. dK/dV: a work-group owns NW*32 keys of one (batch, head); each wave keeps
+//     its 32 keys' K and V rows in VGPRs (B operands) and its dK/dV
+//     accumulators resident, and loops over query tiles staged in LDS both
+//     row-major (A operands of S and dP) and transposed with a permuted query
+//     order (B operands of dV and dK).  S and dP come out with one key per
+//     lane, so P and dS feed the next MFMA straight from registers;
+//  3. dQ: a work-group owns query rows (like the forward) and loops over key
+//     tiles; S^T and dP^T come out with one query per lane, so LSE_i and D_i
+//     are one register each, and dS^T feeds dQ^T = K^T dS^T from registers.
+// Kernels 2 and 3 recompute S and P each, so the backward executes 14 N^2 d
+// flops per head (7 contractions) for the 10 N^2 d it is credited with.
+
+#include "fa_common.hpp"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kPerm4[4] = {0, 2, 1, 3};
+
+// Position of element (4*grp + r) of a 4-element group inside the permuted
+// order used for transposed LDS copies: within each 16-element group the
+// middle two 4-element chunks are swapped, so that the 8 elements a lane
+// feeds into one 32x32x16 MFMA (rows 16u + 8*(i/4) + 4*hi + i%4 of a C tile)
+// are contiguous.
+__device__ __forceinline__ int perm_pos(int grp) { return 16 * (grp >> 2) + 4 * kPerm4[grp & 3]; }
+
+// Write 4 rows x 8 features (four 16-byte row chunks) transposed into a
+// [feature][row] LDS array at column `pos`.
+__device__ __forceinline__ void store_transposed(__bf16* dst, int pitch, int feat0, int pos,
+                                                 const u32x4 (&rows)[4]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int w = j >> 1;
+    const int sh = (j & 1) * 16;
+    u32x2 pk;
+    pk[0] = ((rows[0][w] >> sh) & 0xffffu) | (((rows[1][w] >> sh) & 0xffffu) << 16);
+    pk[1] = ((rows[2][w] >> sh) & 0xffffu) | (((rows[3][w] >> sh) & 0xffffu) << 16);
+    *reinterpret_cast<u32x2*>(dst + (feat0 + j) * pitch + pos) = pk;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1. D_i = sum_t dO_it O_it (fp32), one row per D/8 threads
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void fa_bwd_rowdot_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO,
+                          float* __restrict__ Dout, long long rows) {
+  constexpr int TPR = D / 8;  // threads per row
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = gid / TPR;
+  const int part = (int)(gid % TPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(O + row * D + part * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * D + part * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc += __uint_as_float(a[w] << 16) * __uint_as_float(b[w] << 16);
+      acc += __uint_as_float(a[w] & 0xffff0000u) * __uint_as_float(b[w] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) Dout[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK / dV
+// ---------------------------------------------------------------------------
+template <int D, int NW, int BQ>
+struct DkdvCfg {
+  static constexpr int BK = NW * 32;       // keys per work-group
+  static constexpr int NT = NW * 64;
+  static constexpr int KS = D / 16;
+  static constexpr int NQB = BQ / 32;      // 32-query blocks per tile
+  static constexpr int NG = BQ / 16;       // 16-query groups per tile
+  static constexpr int NDB = D / 32;
+  static constexpr int RPITCH = D + 8;     // row-major copies (bf16 per row)
+  static constexpr int TPITCH = BQ + 8;    // transposed copies (bf16 per feature row)
+  static constexpr int UNITS = (BQ / 4) * (D / 8);
+  static constexpr int UPT = (UNITS + NT - 1) / NT;
+};
+
+template <int D, int NW, int BQ>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                        const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                        const float* __restrict__ LSE, const float* __restrict__ Dlt,
+                        const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
+                        int causal, __bf16* __restrict__ dK, __bf16* __restrict__ dV, int B,
+                        int H, int N, int n_ktiles) {
+  using C = DkdvCfg<D, NW, BQ>;
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * C::RPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 dOs[2][BQ * C::RPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 Qt[2][D * C::TPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 dOt[2][D * C::TPITCH];
+  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // key tiles in increasing order: under a causal mask the first key tiles see
+  // the most query rows, so the longest work-groups are issued first
+  const int bh_count = B * H;
+  const int kt = blockIdx.x / bh_count;
+  const int bh = blockIdx.x - kt * bh_count;
+  const int b = bh / H;
+  const int h = bh - b * H;
+  const size_t head = (size_t)b * H + h;
+  const __bf16* Qh = Q + head * (size_t)N * D;
+  const __bf16* Kh = K + head * (size_t)N * D;
+  const __bf16* Vh = V + head * (size_t)N * D;
+  const __bf16* dOh = dO + head * (size_t)N * D;
+  const float* Lh = LSE + head * (size_t)N;
+  const float* Dh = Dlt + head * (size_t)N;
+  __bf16* dKh = dK + head * (size_t)N * D;
+  __bf16* dVh = dV + head * (size_t)N * D;
+
+  const int kv_len = key_length(seqlens_k, b, N);
+  const int k0 = kt * C::BK;
+  const int kw0 = k0 + wave * 32;
+  const int my_key = kw0 + l32;
+
+  // query tiles: all rows, or (causal) rows from the first key of this group
+  const int q_begin = (causal ? (k0 / BQ) * BQ : 0);
+  const int n_qt = (k0 < kv_len) ? (N - q_begin + BQ - 1) / BQ : 0;
+
+  // this wave's K and V rows (B operands of S = Q K^T and dP = dO V^T)
+  bf16x8 kf[C::KS], vf[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    if (my_key < N) {
+      kf[ks] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)my_key * D + ks * 16 + hi * 8);
+      vf[ks] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)my_key * D + ks * 16 + hi * 8);
+    } else {
+      kf[ks] = bf16x8{};
+      vf[ks] = bf16x8{};
+    }
+  }
+
+  f32x16 dkacc[C::NDB], dvacc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+
+  u32x4 qreg[C::UPT][4], oreg[C::UPT][4];
+  float lreg = 0.f, dreg = 0.f;
+
+  auto load_tile = [&](int qi) {
+    const int qt0 = q_begin + qi * BQ;
+#pragma unroll
+    for (int i = 0; i < C::UPT; ++i) {
+      const int u = tid + i * C::NT;
+      const int qg = u % (BQ / 4);
+      const int dc = u / (BQ / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = qt0 + 4 * qg + r;
+        const bool ok = (u < C::UNITS) && row < N;
+        qreg[i][r] = ok ? *reinterpret_cast<const u32x4*>(Qh + (size_t)row * D + dc * 8) : u32x4{};
+        oreg[i][r] = ok ? *reinterpret_cast<const u32x4*>(dOh + (size_t)row * D + dc * 8) : u32x4{};
+      }
+    }
+    if (tid < BQ) {
+      const int row = qt0 + tid;
+      // rows past N, and rows that see no key, get +inf so that P = 0
+      float lse = row < N ? Lh[row] : __builtin_huge_valf();
+      lreg = (lse == kNegInf) ? __builtin_huge_valf() : lse * kLog2e;
+      dreg = row < N ? Dh[row] : 0.f;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::UPT; ++i) {
+      const int u = tid + i * C::NT;
+      if (u < C::UNITS) {
+        const int qg = u % (BQ / 4);
+        const int dc = u / (BQ / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          *reinterpret_cast<u32x4*>(&Qs[buf][(4 * qg + r) * C::RPITCH + dc * 8]) = qreg[i][r];
+          *reinterpret_cast<u32x4*>(&dOs[buf][(4 * qg + r) * C::RPITCH + dc * 8]) = oreg[i][r];
+        }
+        const int pos = perm_pos(qg);
+        store_transposed(Qt[buf], C::TPITCH, dc * 8, pos, qreg[i]);
+        store_transposed(dOt[buf], C::TPITCH, dc * 8, pos, oreg[i]);
+      }
+    }
+    if (tid < BQ) {
+      Ls[buf][tid] = lreg;
+      Ds[buf][tid] = dreg;
+    }
+  };
+
+  if (n_qt > 0) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+  }
+
+  const bool wave_keys_valid = kw0 < kv_len;
+  for (int qi = 0; qi < n_qt; ++qi) {
+    const int buf = qi & 1;
+    if (qi + 1 < n_qt) load_tile(qi + 1);
+    const int qt0 = q_begin + qi * BQ;
+    const bool wave_active = wave_keys_valid && (!causal || qt0 + BQ - 1 >= kw0);
+    if (wave_active) {
+      // ---- S = Q K^T and dP = dO V^T (C: one key per lane, rows = queries)
+      f32x16 sacc[C::NQB], pacc[C::NQB];
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        sacc[qb] = f32x16{};
+        pacc[qb] = f32x16{};
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(
+              &Qs[buf][(qb * 32 + l32) * C::RPITCH + ks * 16 + hi * 8]);
+          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(
+              &dOs[buf][(qb * 32 + l32) * C::RPITCH + ks * 16 + hi * 8]);
+          sacc[qb] = mfma_bf16(qa, kf[ks], sacc[qb]);
+          pacc[qb] = mfma_bf16(oa, vf[ks], pacc[qb]);
+        }
+
+      const bool need_mask = (kw0 + 31 >= kv_len) || (causal && qt0 < kw0 + 31);
+      // ---- P = exp2(s*scale*log2e - LSE*log2e); dS = P (dP - D)
+      bf16x8 pa[C::NG], dsa[C::NG];
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int r0 = qb * 32 + 8 * a4 + 4 * hi;
+          const f32x4 lq = *reinterpret_cast<const f32x4*>(&Ls[buf][r0]);
+          const f32x4 dq = *reinterpret_cast<const f32x4*>(&Ds[buf][r0]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * a4 + e;
+            float p = fast_exp2(__builtin_fmaf(sacc[qb][v], scale_log2, -lq[e]));
+            if (need_mask) {
+              const int query = qt0 + r0 + e;
+              const bool vis = my_key < kv_len && (!causal || my_key <= query);
+              if (!vis) p = 0.f;
+            }
+            const float ds = p * (pacc[qb][v] - dq[e]);
+            pa[2 * qb + (v >> 3)][v & 7] = to_bf16(p);
+            dsa[2 * qb + (v >> 3)][v & 7] = to_bf16(ds);
+          }
+        }
+      }
+
+      // ---- dV += P^T dO ; dK += dS^T Q   (B operands from the transposed copies)
+#pragma unroll
+      for (int g = 0; g < C::NG; ++g)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          const bf16x8 ob = *reinterpret_cast<const bf16x8*>(
+              &dOt[buf][(db * 32 + l32) * C::TPITCH + g * 16 + hi * 8]);
+          const bf16x8 qbv = *reinterpret_cast<const bf16x8*>(
+              &Qt[buf][(db * 32 + l32) * C::TPITCH + g * 16 + hi * 8]);
+          dvacc[db] = mfma_bf16(pa[g], ob, dvacc[db]);
+          dkacc[db] = mfma_bf16(dsa[g], qbv, dkacc[db]);
+        }
+    }
+    if (qi + 1 < n_qt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- write dK = scale * acc, dV = acc  (C: lane = feature, rows = keys)
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = kw0 + c_row(v, lane);
+      if (key < N) {
+        dKh[(size_t)key * D + db * 32 + l32] = to_bf16(dkacc[db][v] * scale);
+        dVh[(size_t)key * D + db * 32 + l32] = to_bf16(dvacc[db][v]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ
+// ---------------------------------------------------------------------------
+template <int D, int NW, int BC>
+struct DqCfg {
+  static constexpr int BR = NW * 32;
+  static constexpr int NT = NW * 64;
+  static constexpr int KS = D / 16;
+  static constexpr int NCB = BC / 32;
+  static constexpr int NG = BC / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int RPITCH = D + 8;
+  static constexpr int TPITCH = BC + 8;
+  static constexpr int UNITS = (BC / 4) * (D / 8);
+  static constexpr int UPT = (UNITS + NT - 1) / NT;
+};
+
+template <int D, int NW, int BC>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+__attribute__((amdgpu_waves_per_eu(1, 2)))
+void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                      const float* __restrict__ LSE, const float* __restrict__ Dlt,
+                      const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
+                      int causal, __bf16* __restrict__ dQ, int B, int H, int N, int n_qtiles) {
+  using C = DqCfg<D, NW, BC>;
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * C::RPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BC * C::RPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 Kt[2][D * C::TPITCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
+  const size_t head = (size_t)tc.b * H + tc.h;
+  const __bf16* Qh = Q + head * (size_t)N * D;
+  const __bf16* Kh = K + head * (size_t)N * D;
+  const __bf16* Vh = V + head * (size_t)N * D;
+  const __bf16* dOh = dO + head * (size_t)N * D;
+  __bf16* dQh = dQ + head * (size_t)N * D;
+
+  const int kv_len = key_length(seqlens_k, tc.b, N);
+  const int q0 = tc.qt * C::BR;
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + l32;
+  int kv_end = kv_len;
+  if (causal) kv_end = min(kv_end, min(q0 + C::BR, N));
+  const int n_kt = (kv_end + BC - 1) / BC;
+
+  bf16x8 qf[C::KS], of[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    if (qrow < N) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + ks * 16 + hi * 8);
+      of[ks] = *reinterpret_cast<const bf16x8*>(dOh + (size_t)qrow * D + ks * 16 + hi * 8);
+    } else {
+      qf[ks] = bf16x8{};
+      of[ks] = bf16x8{};
+    }
+  }
+  float lse2 = __builtin_huge_valf(), drow = 0.f;
+  if (qrow < N) {
+    const float lse = LSE[head * (size_t)N + qrow];
+    lse2 = (lse == kNegInf) ? __builtin_huge_valf() : lse * kLog2e;
+    drow = Dlt[head * (size_t)N + qrow];
+  }
+
+  f32x16 dqacc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) dqacc[db] = f32x16{};
+
+  u32x4 kreg[C::UPT][4], vreg[C::UPT][4];
+  auto load_tile = [&](int kt) {
+    const int key0 = kt * BC;
+#pragma unroll
+    for (int i = 0; i < C::UPT; ++i) {
+      const int u = tid + i * C::NT;
+      const int kg = u % (BC / 4);
+      const int dc = u / (BC / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = key0 + 4 * kg + r;
+        const bool ok = (u < C::UNITS) && key < kv_len;
+        kreg[i][r] = ok ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + dc * 8) : u32x4{};
+        vreg[i][r] = ok ? *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + dc * 8) : u32x4{};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::UPT; ++i) {
+      const int u = tid + i * C::NT;
+      if (u < C::UNITS) {
+        const int kg = u % (BC / 4);
+        const int dc = u / (BC / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          *reinterpret_cast<u32x4*>(&Ks[buf][(4 * kg + r) * C::RPITCH + dc * 8]) = kreg[i][r];
+          *reinterpret_cast<u32x4*>(&Vs[buf][(4 * kg + r) * C::RPITCH + dc * 8]) = vreg[i][r];
+        }
+        store_transposed(Kt[buf], C::TPITCH, dc * 8, perm_pos(kg), kreg[i]);
+      }
+    }
+  };
+
+  if (n_kt > 0) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+  }
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) load_tile(kt + 1);
+    const int key0 = kt * BC;
+    const bool wave_active = (qw0 < N) && (!causal || key0 <= qw0 + 31);
+    if (wave_active) {
+      // ---- S^T = K Q^T, dP^T = V dO^T (C: one query per lane, rows = keys)
+      f32x16 sacc[C::NCB], pacc[C::NCB];
+#pragma unroll
+      for (int c = 0; c < C::NCB; ++c) {
+        sacc[c] = f32x16{};
+        pacc[c] = f32x16{};
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int c = 0; c < C::NCB; ++c) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+              &Ks[buf][(c * 32 + l32) * C::RPITCH + ks * 16 + hi * 8]);
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(
+              &Vs[buf][(c * 32 + l32) * C::RPITCH + ks * 16 + hi * 8]);
+          sacc[c] = mfma_bf16(ka, qf[ks], sacc[c]);
+          pacc[c] = mfma_bf16(va, of[ks], pacc[c]);
+        }
+      const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0);
+      bf16x8 dsb[C::NG];
+#pragma unroll
+      for (int c = 0; c < C::NCB; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float p = fast_exp2(__builtin_fmaf(sacc[c][v], scale_log2, -lse2));
+          if (need_mask) {
+            const int key = key0 + c * 32 + c_row(v, lane);
+            const bool vis = key < kv_len && (!causal || key <= qrow);
+            if (!vis) p = 0.f;
+          }
+          dsb[2 * c + (v >> 3)][v & 7] = to_bf16(p * (pacc[c][v] - drow));
+        }
+      // ---- dQ^T += K^T dS^T
+#pragma unroll
+      for (int g = 0; g < C::NG; ++g)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+              &Kt[buf][(db * 32 + l32) * C::TPITCH + g * 16 + hi * 8]);
+          dqacc[db] = mfma_bf16(ka, dsb[g], dqacc[db]);
+        }
+    }
+    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qrow < N) {
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int d0 = db * 32 + 8 * v4 + 4 * hi;
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = to_bf16(dqacc[db][4 * v4 + e] * scale);
+        *reinterpret_cast<bf16x4*>(dQh + (size_t)qrow * D + d0) = w;
+      }
+  }
+}
+
+constexpr int kDkdvNW = 4, kDkdvBQ = 64;
+constexpr int kDqNW = 4, kDqBC = 64;
+
+template <int D>
+hipError_t launch_preprocess_d(const BwdArgs& a) {
+  const long long rows = (long long)a.B * a.H * a.N;
+  const long long threads = rows * (D / 8);
+  hipLaunchKernelGGL((fa_bwd_rowdot_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                     0, a.stream, static_cast<const __bf16*>(a.o),
+                     static_cast<const __bf16*>(a.dout), a.delta, rows);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dkdv_d(const BwdArgs& a) {
+  using CK = DkdvCfg<D, kDkdvNW, kDkdvBQ>;
+  const int n_ktiles = (a.N + CK::BK - 1) / CK::BK;
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, kDkdvNW, kDkdvBQ>),
+                     dim3((unsigned)((long long)n_ktiles * a.B * a.H)), dim3(CK::NT), 0, a.stream,
+                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dout), a.lse,
+                     a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
+                     static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.B, a.H, a.N,
+                     n_ktiles);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dq_d(const BwdArgs& a) {
+  using CQ = DqCfg<D, kDqNW, kDqBC>;
+  const int n_qtiles = (a.N + CQ::BR - 1) / CQ::BR;
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, kDqNW, kDqBC>),
+                     dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(CQ::NT), 0, a.stream,
+                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dout), a.lse,
+                     a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
+                     static_cast<__bf16*>(a.dq), a.B, a.H, a.N, n_qtiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+long long bwd_bf16_grid(int B, int H, int N, int d) {
+  (void)d;
+  const long long kt = (N + kDkdvNW * 32 - 1) / (kDkdvNW * 32);
+  const long long qt = (N + kDqNW * 32 - 1) / (kDqNW * 32);
+  const long long rows_wg = ((long long)B * H * N * 16 + 255) / 256;
+  long long m = kt * B * H;
+  if (qt * B * H > m) m = qt * B * H;
+  if (rows_wg > m) m = rows_wg;
+  return m;
+}
+
+hipError_t launch_bwd_preprocess_bf16(const BwdArgs& a) {
+  switch (a.d) {
+    case 64: return launch_preprocess_d<64>(a);
+    case 128: return launch_preprocess_d<128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a) {
+  switch (a.d) {
+    case 64: return launch_dkdv_d<64>(a);
+    case 128: return launch_dkdv_d<128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
+  switch (a.d) {
+    case 64: return launch_dq_d<64>(a);
+    case 128: return launch_dq_d<128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a) {
+  hipError_t e = launch_bwd_preprocess_bf16(a);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_dkdv_bf16(a);
+  if (e != hipSuccess) return e;
+  return launch_bwd_dq_bf16(a);
+}
+
+}  // namespace fa

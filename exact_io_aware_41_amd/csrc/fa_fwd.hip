@@ -1,0 +1,542 @@
+// fa_fwd.hip - forward kernels: exact attention with the online softmax.
+//
+// Method ("FlashAttention", section "Why it is allowed to be exact";
+// "Explain FlashAttention and why it is IO-aware", section "Keep only the
+// state needed for the final weighted average"): for every query row keep
+// the running maximum m, the running sum l of exp(s - m) and the unnormalised
+// output o; when a key tile raises the maximum, multiply l and o by
+// exp(m_old - m_new) before adding the tile; divide o by l after the last
+// tile.  Query-outer loop order ("What is FlashAttention?", Step 3): a
+// work-group keeps its query tile, its o accumulators and its statistics on
+// chip and writes O and one LSE per row once.
+//
+// gfx950 mapping (bf16 kernel):
+//  * a work-group of NW waves owns BR = NW*QB*32 consecutive query rows of one
+//    (batch, head); each wave owns QB blocks of 32 queries, one query per lane
+//    (lanes l and l^32 share a query).
+//  * Q stays in VGPRs as the B operand of S^T = K Q^T (32x32x16 bf16 MFMA).
+//  * K and V tiles of BC keys are loaded from HBM with 16-byte coalesced loads
+//    into registers one tile ahead, then written to a double-buffered LDS
+//    ring: K row-major (padded rows), V transposed to [d][key] with the key
+//    order permuted inside each 16-key group so that every MFMA A fragment is
+//    one 16-byte LDS read.
+//  * scores are handled in the log2 domain: x = s * scale * log2(e), so the
+//    exponentials are single v_exp_f32 instructions.
+//  * P^T leaves the S^T accumulators as bf16 (round to nearest even) and is
+//    the B operand of O^T = V^T P^T, whose accumulators hold one query per
+//    lane, so the rescale by alpha is lane-local.
+//  * key tiles beyond the last visible key of the work-group (causal
+//    diagonal, or the sequence's key length) are never loaded; a wave skips
+//    the arithmetic of tiles that lie entirely above its own diagonal; only
+//    tiles that cross the diagonal or the key length apply the mask, on
+//    absolute positions.
+
+#include "fa_common.hpp"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kVPerm[4] = {0, 2, 1, 3};
+
+template <int D, int QB, int NW, int BC>
+struct FwdBf16Cfg {
+  static constexpr int BR = NW * QB * 32;  // query rows per work-group
+  static constexpr int NT = NW * 64;       // threads per work-group
+  static constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
+  static constexpr int NCB = BC / 32;      // 32-key blocks per tile
+  static constexpr int NG = BC / 16;       // 16-key groups per tile
+  static constexpr int NDB = D / 32;       // 32-row blocks of O^T
+  static constexpr int KPITCH = D + 8;     // bf16 per K row in LDS
+  static constexpr int VPITCH = BC + 8;    // bf16 per V^T row in LDS
+  static constexpr int KU = BC * D / 8 / NT;        // 16-byte K chunks per thread
+  static constexpr int VU = (BC / 4) * (D / 8) / NT;  // 4-key x 8-feature V units per thread
+  static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
+  static_assert(KU * NT * 8 == BC * D, "K tile must split evenly over threads");
+  static_assert(VU * NT == (BC / 4) * (D / 8), "V tile must split evenly over threads");
+};
+
+template <int D, int QB, int NW, int BC>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                        const __bf16* __restrict__ V, const int32_t* __restrict__ seqlens_k,
+                        float scale_log2, int causal, __bf16* __restrict__ O,
+                        float* __restrict__ LSE, int B, int H, int N, int n_qtiles) {
+  using C = FwdBf16Cfg<D, QB, NW, BC>;
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * C::KPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D * C::VPITCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
+  const size_t head = (size_t)tc.b * H + tc.h;
+  const __bf16* Qh = Q + head * (size_t)N * D;
+  const __bf16* Kh = K + head * (size_t)N * D;
+  const __bf16* Vh = V + head * (size_t)N * D;
+  __bf16* Oh = O + head * (size_t)N * D;
+  float* Lh = LSE + head * (size_t)N;
+
+  const int kv_len = key_length(seqlens_k, tc.b, N);
+  const int q0 = tc.qt * C::BR;
+  const int qw0 = q0 + wave * QB * 32;
+  // last key any row of this work-group can see
+  int kv_end = kv_len;
+  if (causal) kv_end = min(kv_end, min(q0 + C::BR, N));
+  const int n_kt = (kv_end + BC - 1) / BC;
+
+  // ---- Q fragments (B operand of S^T = K Q^T): query l32, features 8*hi + [0..7]
+  bf16x8 qf[QB][C::KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = qw0 + qb * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      if (qrow < N)
+        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + ks * 16 + hi * 8);
+      else
+        qf[qb][ks] = bf16x8{};
+    }
+  }
+
+  f32x16 oacc[C::NDB][QB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x16{};
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = kNegInf;
+    l[qb] = 0.f;
+  }
+
+  // ---- staging registers for the next K/V tile
+  u32x4 kreg[C::KU];
+  u32x4 vreg[C::VU][4];
+
+  auto load_tile = [&](int kt) {
+    const int key0 = kt * BC;
+#pragma unroll
+    for (int i = 0; i < C::KU; ++i) {
+      const int u = tid + i * C::NT;
+      const int r = u / (D / 8);
+      const int c8 = u % (D / 8);
+      const int key = key0 + r;
+      kreg[i] = key < kv_len ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + c8 * 8)
+                             : u32x4{};
+    }
+#pragma unroll
+    for (int i = 0; i < C::VU; ++i) {
+      const int u = tid + i * C::NT;
+      const int kg = u % (BC / 4);
+      const int dc = u / (BC / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = key0 + 4 * kg + r;
+        vreg[i][r] = key < kv_len
+                         ? *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + dc * 8)
+                         : u32x4{};
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::KU; ++i) {
+      const int u = tid + i * C::NT;
+      const int r = u / (D / 8);
+      const int c8 = u % (D / 8);
+      *reinterpret_cast<u32x4*>(&Ks[buf][r * C::KPITCH + c8 * 8]) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::VU; ++i) {
+      const int u = tid + i * C::NT;
+      const int kg = u % (BC / 4);
+      const int dc = u / (BC / 4);
+      // keys 4kg..4kg+3 sit at positions 16g + 4*perm(a) of each V^T row
+      const int pos = 16 * (kg >> 2) + 4 * kVPerm[kg & 3];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int w = j >> 1;
+        const int sh = (j & 1) * 16;
+        const uint32_t x0 = (vreg[i][0][w] >> sh) & 0xffffu;
+        const uint32_t x1 = (vreg[i][1][w] >> sh) & 0xffffu;
+        const uint32_t x2 = (vreg[i][2][w] >> sh) & 0xffffu;
+        const uint32_t x3 = (vreg[i][3][w] >> sh) & 0xffffu;
+        u32x2 pk;
+        pk[0] = x0 | (x1 << 16);
+        pk[1] = x2 | (x3 << 16);
+        *reinterpret_cast<u32x2*>(&Vt[buf][(dc * 8 + j) * C::VPITCH + pos]) = pk;
+      }
+    }
+  };
+
+  if (n_kt > 0) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+  }
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) load_tile(kt + 1);
+
+    const int key0 = kt * BC;
+    const bool wave_active = (qw0 < N) && (!causal || key0 <= qw0 + QB * 32 - 1);
+    if (wave_active) {
+      // ---- S^T = K Q^T for this tile
+      f32x16 sacc[C::NCB][QB];
+#pragma unroll
+      for (int c = 0; c < C::NCB; ++c)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[c][qb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int c = 0; c < C::NCB; ++c) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+              &Ks[buf][(c * 32 + l32) * C::KPITCH + ks * 16 + hi * 8]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) sacc[c][qb] = mfma_bf16(kf, qf[qb][ks], sacc[c][qb]);
+        }
+      }
+
+      // ---- mask (only tiles crossing the key length or this wave's diagonal)
+      const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0);
+      if (need_mask) {
+#pragma unroll
+        for (int c = 0; c < C::NCB; ++c)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const int query = qw0 + qb * 32 + l32;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int key = key0 + c * 32 + c_row(v, lane);
+              const bool vis = key < kv_len && (!causal || key <= query);
+              if (!vis) sacc[c][qb][v] = kNegInf;
+            }
+          }
+      }
+
+      // ---- online softmax update (log2 domain)
+      bf16x8 pf[C::NG][QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int c = 0; c < C::NCB; ++c)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[c][qb][v]);
+        mx = halfwave_max(mx);
+        const float m_new = fmaxf(m[qb], mx * scale_log2);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = fast_exp2(m[qb] - m_use);
+        m[qb] = m_new;
+        float rs = 0.f;
+#pragma unroll
+        for (int c = 0; c < C::NCB; ++c)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float p = fast_exp2(__builtin_fmaf(sacc[c][qb][v], scale_log2, -m_use));
+            rs += p;
+            pf[2 * c + (v >> 3)][qb][v & 7] = to_bf16(p);
+          }
+        l[qb] = l[qb] * alpha + rs;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) oacc[db][qb] *= alpha;
+      }
+
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int g = 0; g < C::NG; ++g) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+              &Vt[buf][(db * 32 + l32) * C::VPITCH + g * 16 + hi * 8]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma_bf16(vf, pf[g][qb], oacc[db][qb]);
+        }
+      }
+    }
+
+    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = o / l (zeros for empty rows), LSE = (m + log2 l) ln 2
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = halfwave_sum(l[qb]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int q = qw0 + qb * 32 + l32;
+    if (q < N) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int d0 = db * 32 + 8 * v4 + 4 * hi;
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = to_bf16(oacc[db][qb][4 * v4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(Oh + (size_t)q * D + d0) = w;
+        }
+      if (hi == 0)
+        Lh[q] = lt > 0.f ? (m[qb] + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: the same algorithm on 32x32x2 fp32 MFMA.  Each lane supplies one
+// fp32 per operand, so V needs no transposition: the A fragment of V^T is a
+// plain row-major read.  Row pitches are padded so that the two half-waves hit
+// disjoint LDS banks.
+// ---------------------------------------------------------------------------
+
+template <int D, int NW, int BC>
+struct FwdF32Cfg {
+  static constexpr int BR = NW * 32;
+  static constexpr int NT = NW * 64;
+  static constexpr int KS = D / 2;
+  static constexpr int NCB = BC / 32;
+  static constexpr int NDB = D / 32;
+  static constexpr int KPITCH = D + 2;   // floats per K row (halves on odd/even banks)
+  static constexpr int VPITCH = D + 8;   // floats per V row (key+4 rows 32 banks apart)
+  static constexpr int KU = BC * D / 4 / NT;  // 16-byte chunks per thread
+  static_assert(KU * NT * 4 == BC * D, "tile must split evenly over threads");
+};
+
+template <int D, int NW, int BC>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                       const float* __restrict__ V, const int32_t* __restrict__ seqlens_k,
+                       float scale_log2, int causal, float* __restrict__ O,
+                       float* __restrict__ LSE, int B, int H, int N, int n_qtiles) {
+  using C = FwdF32Cfg<D, NW, BC>;
+  __shared__ __attribute__((aligned(16))) float Ks[2][BC * C::KPITCH];
+  __shared__ __attribute__((aligned(16))) float Vs[2][BC * C::VPITCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
+  const size_t head = (size_t)tc.b * H + tc.h;
+  const float* Qh = Q + head * (size_t)N * D;
+  const float* Kh = K + head * (size_t)N * D;
+  const float* Vh = V + head * (size_t)N * D;
+  float* Oh = O + head * (size_t)N * D;
+  float* Lh = LSE + head * (size_t)N;
+
+  const int kv_len = key_length(seqlens_k, tc.b, N);
+  const int q0 = tc.qt * C::BR;
+  const int qw0 = q0 + wave * 32;
+  int kv_end = kv_len;
+  if (causal) kv_end = min(kv_end, min(q0 + C::BR, N));
+  const int n_kt = (kv_end + BC - 1) / BC;
+
+  const int qrow = qw0 + l32;
+  float qf[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) qf[ks] = qrow < N ? Qh[(size_t)qrow * D + 2 * ks + hi] : 0.f;
+
+  f32x16 oacc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16{};
+  float m = kNegInf, l = 0.f;
+
+  f32x4 kreg[C::KU], vreg[C::KU];
+  auto load_tile = [&](int kt) {
+    const int key0 = kt * BC;
+#pragma unroll
+    for (int i = 0; i < C::KU; ++i) {
+      const int u = tid + i * C::NT;
+      const int r = u / (D / 4);
+      const int c4 = u % (D / 4);
+      const int key = key0 + r;
+      const bool ok = key < kv_len;
+      kreg[i] = ok ? *reinterpret_cast<const f32x4*>(Kh + (size_t)key * D + c4 * 4) : f32x4{};
+      vreg[i] = ok ? *reinterpret_cast<const f32x4*>(Vh + (size_t)key * D + c4 * 4) : f32x4{};
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::KU; ++i) {
+      const int u = tid + i * C::NT;
+      const int r = u / (D / 4);
+      const int c4 = u % (D / 4);
+      float* kd = &Ks[buf][r * C::KPITCH + c4 * 4];
+      kd[0] = kreg[i][0];
+      kd[1] = kreg[i][1];
+      kd[2] = kreg[i][2];
+      kd[3] = kreg[i][3];
+      *reinterpret_cast<f32x4*>(&Vs[buf][r * C::VPITCH + c4 * 4]) = vreg[i];
+    }
+  };
+
+  if (n_kt > 0) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+  }
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) load_tile(kt + 1);
+    const int key0 = kt * BC;
+    const bool wave_active = (qw0 < N) && (!causal || key0 <= qw0 + 31);
+    if (wave_active) {
+      f32x16 sacc[C::NCB];
+#pragma unroll
+      for (int c = 0; c < C::NCB; ++c) sacc[c] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int c = 0; c < C::NCB; ++c)
+          sacc[c] = mfma_f32(Ks[buf][(c * 32 + l32) * C::KPITCH + 2 * ks + hi], qf[ks], sacc[c]);
+
+      const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0);
+      if (need_mask) {
+#pragma unroll
+        for (int c = 0; c < C::NCB; ++c)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = key0 + c * 32 + c_row(v, lane);
+            const bool vis = key < kv_len && (!causal || key <= qrow);
+            if (!vis) sacc[c][v] = kNegInf;
+          }
+      }
+
+      float mx = kNegInf;
+#pragma unroll
+      for (int c = 0; c < C::NCB; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[c][v]);
+      mx = halfwave_max(mx);
+      const float m_new = fmaxf(m, mx * scale_log2);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m - m_use);
+      m = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int c = 0; c < C::NCB; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(__builtin_fmaf(sacc[c][v], scale_log2, -m_use));
+          sacc[c][v] = p;
+          rs += p;
+        }
+      l = l * alpha + rs;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha;
+
+      // O^T += V^T P^T: one MFMA per key pair (lane halves supply keys k and k+4)
+#pragma unroll
+      for (int c = 0; c < C::NCB; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = c * 32 + c_row(v, lane);
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+            oacc[db] = mfma_f32(Vs[buf][key * C::VPITCH + db * 32 + l32], sacc[c][v], oacc[db]);
+        }
+    }
+    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float lt = halfwave_sum(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qrow < N) {
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int d0 = db * 32 + 8 * v4 + 4 * hi;
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * v4 + e] * inv;
+        *reinterpret_cast<f32x4*>(Oh + (size_t)qrow * D + d0) = w;
+      }
+    if (hi == 0) Lh[qrow] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+  }
+}
+
+// Tile choices per head dimension.
+constexpr int kBf16QB = 2, kBf16NW = 4;
+template <int D>
+struct Bf16Tile;
+template <>
+struct Bf16Tile<128> {
+  static constexpr int BC = 64;
+};
+template <>
+struct Bf16Tile<64> {
+  static constexpr int BC = 128;
+};
+constexpr int kF32NW = 2, kF32BC = 32;
+
+template <int D>
+hipError_t launch_bf16_d(const FwdArgs& a) {
+  constexpr int BC = Bf16Tile<D>::BC;
+  using C = FwdBf16Cfg<D, kBf16QB, kBf16NW, BC>;
+  const int n_qtiles = (a.N + C::BR - 1) / C::BR;
+  const dim3 grid((unsigned)((long long)n_qtiles * a.B * a.H));
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, kBf16QB, kBf16NW, BC>), grid, dim3(C::NT), 0,
+                     a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                     static_cast<const __bf16*>(a.v), a.seqlens_k, a.scale * kLog2e, a.causal,
+                     static_cast<__bf16*>(a.o), a.lse, a.B, a.H, a.N, n_qtiles);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32_d(const FwdArgs& a) {
+  using C = FwdF32Cfg<D, kF32NW, kF32BC>;
+  const int n_qtiles = (a.N + C::BR - 1) / C::BR;
+  const dim3 grid((unsigned)((long long)n_qtiles * a.B * a.H));
+  hipLaunchKernelGGL((fa_fwd_f32_kernel<D, kF32NW, kF32BC>), grid, dim3(C::NT), 0, a.stream,
+                     static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                     static_cast<const float*>(a.v), a.seqlens_k, a.scale * kLog2e, a.causal,
+                     static_cast<float*>(a.o), a.lse, a.B, a.H, a.N, n_qtiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+long long fwd_bf16_grid(int B, int H, int N, int d) {
+  const int BR = kBf16NW * kBf16QB * 32;
+  (void)d;
+  return (long long)((N + BR - 1) / BR) * B * H;
+}
+
+long long fwd_f32_grid(int B, int H, int N, int d) {
+  const int BR = kF32NW * 32;
+  (void)d;
+  return (long long)((N + BR - 1) / BR) * B * H;
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a) {
+  switch (a.d) {
+    case 64: return launch_bf16_d<64>(a);
+    case 128: return launch_bf16_d<128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fwd_f32(const FwdArgs& a) {
+  switch (a.d) {
+    case 64: return launch_f32_d<64>(a);
+    case 128: return launch_f32_d<128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,58 @@
+// fa_internal.h - host-side declarations shared by the C ABI and the kernel
+// translation units.  Launchers assume their arguments were validated by
+// fa_api.cpp and only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  int B, H, N, d;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seqlens_k;
+  float scale;
+  int causal;
+  void* o;
+  float* lse;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  int B, H, N, d;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  const int32_t* seqlens_k;
+  float scale;
+  int causal;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // [B][H][N] fp32 row dot products, from the workspace
+  hipStream_t stream;
+};
+
+// Each launcher returns hipSuccess or the error hipGetLastError reported
+// after enqueueing; it never synchronises.
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_bwd_bf16(const BwdArgs& a);
+hipError_t launch_bwd_preprocess_bf16(const BwdArgs& a);
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a);
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a);
+
+// Number of work-groups a launch of the given geometry needs; the ABI
+// rejects problems whose grid would not fit in a signed 32-bit count.
+long long fwd_bf16_grid(int B, int H, int N, int d);
+long long fwd_f32_grid(int B, int H, int N, int d);
+long long bwd_bf16_grid(int B, int H, int N, int d);
+
+}  // namespace fa

@@ -1,0 +1,183 @@
+/*
+ * fa.h - C ABI of the exact, IO-aware attention library for MI355X (gfx950).
+ *
+ * The library computes exact scaled dot-product attention tile by tile with
+ * the online-softmax recurrence, so the N x N score and probability matrices
+ * never reach device memory, and its backward pass rebuilds those tiles on
+ * chip from Q, K, V, the saved output and one statistic per row.
+ *
+ * Sources (the web pages the method is taken from):
+ *   "What is FlashAttention?" (interview.clozo.ai): Step 2 (online softmax),
+ *     Step 3 (tiling; the query-outer loop that keeps O and the statistics on
+ *     chip until one final write), Step 4 (the backward recomputes instead of
+ *     storing).
+ *   "FlashAttention" (deepconcepts.dev): "Why it is allowed to be exact"
+ *     (max, sum, rescale by exp(m_old - m_new), divide by l at the end),
+ *     "What it does not do" (the backward rebuilds S and P), "Checking it on
+ *     a real system" (a backend that cannot serve a shape must refuse it
+ *     rather than fall back silently).
+ *   "Explain FlashAttention and why it is IO-aware" (aiinfrainterviews.com):
+ *     "Keep only the state needed for the final weighted average" (scaled
+ *     scores plus mask; state m, l, o), "Executable recurrence, with an
+ *     empty-state policy" (fully masked rows return zeros; causal masks use
+ *     absolute positions).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, contiguous, row-major [B][H][N][d] (batch, head,
+ *    position, feature).  Q, K and V share N (self-attention).
+ *  - lse is fp32 [B][H][N]: the natural-log log-sum-exp of the visible scaled
+ *    scores of each query row, LSE_i = m_i + ln(l_i).
+ *  - Scores are s_ij = scale * q_i . k_j.  A pair (i, j) of sequence b is
+ *    visible iff j < L_b and (causal == 0 or j <= i), with absolute positions
+ *    i, j in [0, N).  L_b = seqlens_k[b] clamped to [0, N], or N when
+ *    seqlens_k is NULL.  Query rows are never masked: row i >= L_b still
+ *    attends to keys 0..L_b-1.
+ *  - A row with no visible key gets O = 0 and LSE = -inf (explicit empty-row
+ *    policy); its gradients are 0.
+ *  - Every pointer is a device pointer owned by the caller.  The library
+ *    allocates and frees nothing, keeps no state between calls, and only
+ *    enqueues work on `stream` (calls return without synchronising).  Calls
+ *    are re-entrant.  Outputs must not alias inputs.
+ *  - Data pointers must be 16-byte aligned.
+ *  - Inputs must be finite; NaN or infinite inputs propagate unchecked.
+ *  - B, H or N equal to 0 is an empty problem: FA_SUCCESS, nothing is
+ *    launched and pointers are not inspected.
+ *
+ * Errors are returned as fa_status codes, never thrown.  Argument checks
+ * run before any HIP call, so an invalid call launches nothing.
+ *  FA_ERROR_INVALID_VALUE  NULL data pointer, negative size, misaligned
+ *                          pointer, scale not finite or not > 0, causal not
+ *                          0/1, workspace missing or too small, or a problem
+ *                          too large for the launch grid.
+ *  FA_ERROR_UNSUPPORTED    (dtype, d) pair outside the compiled set (see
+ *                          below); there is no fallback path.
+ *  FA_ERROR_LAUNCH         the HIP runtime reported an error when the kernel
+ *                          was enqueued (hipGetLastError).  Faults inside a
+ *                          kernel surface at the caller's next synchronise.
+ *
+ * Compiled (dtype, d) set:
+ *  forward : FA_DTYPE_F32 with d in {64, 128}; FA_DTYPE_BF16 with d in {64, 128}
+ *  backward: FA_DTYPE_BF16 with d in {64, 128}
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_SUCCESS = 0,
+  FA_ERROR_INVALID_VALUE = 1,
+  FA_ERROR_UNSUPPORTED = 2,
+  FA_ERROR_LAUNCH = 3
+} fa_status;
+
+typedef enum {
+  FA_DTYPE_F32 = 0,  /* IEEE binary32 inputs and outputs                 */
+  FA_DTYPE_BF16 = 1  /* bfloat16 inputs and outputs, fp32 accumulation   */
+} fa_dtype;
+
+/* Version of this ABI; bumped on any incompatible change. */
+int fa_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_string(fa_status s);
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T restricted to visible pairs) V and
+ * LSE, computed tile by tile with the running maximum m, running sum l and an
+ * output accumulator rescaled by exp(m_old - m_new) and divided by l after
+ * the last tile ("FlashAttention", "Why it is allowed to be exact";
+ * "Explain FlashAttention and why it is IO-aware", "Keep only the state
+ * needed for the final weighted average").  Key tiles that are entirely
+ * masked for a query tile are skipped, never loaded.
+ *
+ *   dtype      element type of q, k, v and o
+ *   B, H, N, d batch, heads, sequence length, head dimension (d in the
+ *              compiled set)
+ *   q, k, v    [B][H][N][d] inputs (read only)
+ *   seqlens_k  [B] int32 key lengths on the device, or NULL for all N;
+ *              each value is clamped to [0, N] inside the kernel
+ *   scale      multiplier of q . k; finite and > 0 (1/sqrt(d) is usual)
+ *   causal     0 or 1; 1 masks keys j > i (absolute positions)
+ *   o          [B][H][N][d] output, same dtype as q, rounded to nearest even
+ *   lse        [B][H][N] fp32 output (natural log); the backward needs it
+ *   stream     HIP stream the work is enqueued on (0 = default stream)
+ */
+fa_status fa_forward(fa_dtype dtype, int B, int H, int N, int d,
+                     const void* q, const void* k, const void* v,
+                     const int32_t* seqlens_k, float scale, int causal,
+                     void* o, float* lse, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_backward needs for this problem (0 for an
+ * empty problem).  The workspace holds the fp32 row dot products
+ * D_i = sum_t dO_it O_it, one per query row.
+ */
+size_t fa_backward_workspace_size(fa_dtype dtype, int B, int H, int N, int d);
+
+/*
+ * Backward pass: gradients of the scalar <dO, O> with respect to Q, K and V.
+ * S and P are recomputed tile by tile from Q, K, V and the saved per-row
+ * LSE instead of being stored ("What is FlashAttention?", Step 4; "FlashAttention",
+ * "What it does not do"):  P_ij = exp(s_ij - LSE_i) on visible pairs,
+ * dV = P^T dO, dP = dO V^T, D_i = sum_t dO_it O_it, dS = P * (dP - D),
+ * dQ = scale dS K, dK = scale dS^T Q, all accumulated in fp32.
+ *
+ *   q, k, v, o, dout   [B][H][N][d] (o and lse as written by fa_forward)
+ *   lse                [B][H][N] fp32
+ *   seqlens_k, scale, causal  exactly as passed to fa_forward
+ *   dq, dk, dv         [B][H][N][d] outputs, same dtype as q
+ *   workspace          device buffer of at least
+ *                      fa_backward_workspace_size(...) bytes, 16-byte
+ *                      aligned; its contents on entry do not matter
+ *   workspace_bytes    size of that buffer
+ * The result is deterministic: it does not depend on scheduling order.
+ */
+fa_status fa_backward(fa_dtype dtype, int B, int H, int N, int d,
+                      const void* q, const void* k, const void* v,
+                      const void* o, const void* dout, const float* lse,
+                      const int32_t* seqlens_k, float scale, int causal,
+                      void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/*
+ * The three launches fa_backward makes, callable one by one (same arguments,
+ * same validation, same results).  Issued in this order on one stream they
+ * are exactly fa_backward; dkdv and dq only read `delta` and may run
+ * concurrently on two streams once preprocess has finished.
+ *
+ * fa_backward_preprocess: delta[b][h][i] = sum_t dout_it o_it in fp32 (the
+ *   row term D of dS = P * (dP - D)); delta is [B][H][N] fp32, 16-byte aligned.
+ * fa_backward_dkdv: dk and dv.  Each work-group keeps a block of keys and
+ *   their gradient accumulators on chip and streams query tiles past them,
+ *   recomputing S and P per tile.
+ * fa_backward_dq: dq.  Each work-group keeps a block of query rows on chip
+ *   and streams key tiles past them, recomputing S and P per tile.
+ */
+fa_status fa_backward_preprocess(fa_dtype dtype, int B, int H, int N, int d,
+                                 const void* o, const void* dout, float* delta,
+                                 hipStream_t stream);
+fa_status fa_backward_dkdv(fa_dtype dtype, int B, int H, int N, int d,
+                           const void* q, const void* k, const void* v,
+                           const void* dout, const float* lse, const float* delta,
+                           const int32_t* seqlens_k, float scale, int causal,
+                           void* dk, void* dv, hipStream_t stream);
+fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int N, int d,
+                         const void* q, const void* k, const void* v,
+                         const void* dout, const float* lse, const float* delta,
+                         const int32_t* seqlens_k, float scale, int causal,
+                         void* dq, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */

@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/fa.h declares, and rejects invalid calls before any HIP call."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_io_aware_41_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.LIB_PATH),
+                                reason="library not built (run __graft_entry__.build())")
+
+BF16, F32 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_F32
+A = 0x10000          # aligned fake address: never dereferenced by these calls
+MIS = 0x10004        # 4-byte aligned, not 16-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported():
+    names = declared_functions()
+    assert names == sorted(fa.EXPORTED_SYMBOLS)
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings():
+    assert fa.fa_abi_version() == 1
+    assert fa.fa_status_string(fa.FA_SUCCESS) == "FA_SUCCESS"
+    assert fa.fa_status_string(fa.FA_ERROR_INVALID_VALUE) == "FA_ERROR_INVALID_VALUE"
+    assert fa.fa_status_string(fa.FA_ERROR_UNSUPPORTED) == "FA_ERROR_UNSUPPORTED"
+    assert fa.fa_status_string(fa.FA_ERROR_LAUNCH) == "FA_ERROR_LAUNCH"
+    assert fa.fa_status_string(99) == "FA_ERROR_UNKNOWN"
+
+
+def fwd(dtype=BF16, B=1, H=1, N=16, d=128, q=A, k=A, v=A, lens=None, scale=0.1, causal=0, o=A,
+        lse=A):
+    return fa.fa_forward(dtype, B, H, N, d, q, k, v, lens, scale, causal, o, lse, None)
+
+
+def bwd(dtype=BF16, B=1, H=1, N=16, d=128, scale=0.1, causal=0, ws=A, ws_bytes=1 << 20,
+        **ptrs):
+    p = dict(q=A, k=A, v=A, o=A, do=A, lse=A, lens=None, dq=A, dk=A, dv=A)
+    p.update(ptrs)
+    return fa.fa_backward(dtype, B, H, N, d, p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"],
+                          p["lens"], scale, causal, p["dq"], p["dk"], p["dv"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=7), dict(B=-1), dict(H=-2), dict(N=-1), dict(d=0), dict(d=-128),
+    dict(scale=0.0), dict(scale=-0.5), dict(scale=math.nan), dict(scale=math.inf),
+    dict(causal=2), dict(causal=-1),
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None),
+    dict(q=MIS), dict(k=MIS), dict(v=MIS), dict(o=MIS), dict(lse=MIS), dict(lens=A + 2),
+])
+def test_forward_rejects_invalid_arguments(kw):
+    assert fwd(**kw) == fa.FA_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("dtype,d", [(BF16, 96), (BF16, 256), (BF16, 32), (F32, 96), (F32, 16)])
+def test_forward_unsupported_shapes_fail_loudly(dtype, d):
+    assert fwd(dtype=dtype, d=d) == fa.FA_ERROR_UNSUPPORTED
+
+
+def test_forward_empty_problems_succeed_without_pointers():
+    for B, H, N in ((0, 4, 16), (2, 0, 16), (2, 4, 0)):
+        assert fwd(B=B, H=H, N=N, q=None, k=None, v=None, o=None, lse=None) == fa.FA_SUCCESS
+    # an empty problem with an unsupported head dim still reports it
+    assert fwd(N=0, d=96) == fa.FA_ERROR_UNSUPPORTED
+
+
+def test_forward_grid_too_large_is_rejected():
+    assert fwd(B=65535, H=65535, N=1 << 20) == fa.FA_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=9), dict(B=-1), dict(scale=0.0), dict(scale=math.nan), dict(causal=3),
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(do=None), dict(lse=None),
+    dict(dq=None), dict(dk=None), dict(dv=None), dict(ws=None),
+    dict(dq=MIS), dict(do=MIS), dict(ws=MIS), dict(lens=A + 1),
+    dict(ws_bytes=16 * 4 - 1),
+])
+def test_backward_rejects_invalid_arguments(kw):
+    assert bwd(**kw) == fa.FA_ERROR_INVALID_VALUE
+
+
+def test_backward_unsupported_and_workspace_size():
+    assert bwd(dtype=F32, d=64) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert fa.fa_backward_workspace_size(BF16, 2, 32, 8192, 128) == 2 * 32 * 8192 * 4
+    assert fa.fa_backward_workspace_size(BF16, 0, 32, 8192, 128) == 0
+    assert fa.fa_backward_workspace_size(BF16, -1, 32, 8192, 128) == 0
+    assert bwd(B=0, q=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
+
+
+def test_torch_wrappers_validate_before_calling():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 128, dtype=torch.float16)
+    with pytest.raises(fa.FAError) as e:
+        fa.forward(q, q, q)
+    assert e.value.status == fa.FA_ERROR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        fa.forward(q[0], q[0], q[0])
+    b = torch.zeros(1, 1, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(b, b.float(), b)
+
+
+def test_backward_phase_entry_points_validate():
+    pre = lambda o=A, do=A, delta=A, **kw: fa.fa_backward_preprocess(
+        kw.get("dtype", BF16), kw.get("B", 1), kw.get("H", 1), kw.get("N", 16), kw.get("d", 128),
+        o, do, delta, None)
+    assert pre(o=None) == fa.FA_ERROR_INVALID_VALUE
+    assert pre(delta=MIS) == fa.FA_ERROR_INVALID_VALUE
+    assert pre(d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert pre(dtype=F32, d=64) == fa.FA_ERROR_UNSUPPORTED
+    assert pre(N=0, o=None, do=None, delta=None) == fa.FA_SUCCESS
+
+    def dkdv(q=A, dk=A, dv=A, delta=A, scale=0.1, causal=0, d=128, N=16):
+        return fa.fa_backward_dkdv(BF16, 1, 1, N, d, q, A, A, A, A, delta, None, scale, causal,
+                                   dk, dv, None)
+
+    def dq(q=A, out=A, delta=A, scale=0.1, causal=0, d=128, N=16):
+        return fa.fa_backward_dq(BF16, 1, 1, N, d, q, A, A, A, A, delta, None, scale, causal,
+                                 out, None)
+
+    for f in (dkdv, dq):
+        assert f(q=None) == fa.FA_ERROR_INVALID_VALUE
+        assert f(delta=None) == fa.FA_ERROR_INVALID_VALUE
+        assert f(scale=-1.0) == fa.FA_ERROR_INVALID_VALUE
+        assert f(causal=5) == fa.FA_ERROR_INVALID_VALUE
+        assert f(d=80) == fa.FA_ERROR_UNSUPPORTED
+        assert f(N=0, q=None, delta=None) == fa.FA_SUCCESS
+    assert dkdv(dk=None) == fa.FA_ERROR_INVALID_VALUE
+    assert dkdv(dv=MIS) == fa.FA_ERROR_INVALID_VALUE
+    assert dq(out=None) == fa.FA_ERROR_INVALID_VALUE

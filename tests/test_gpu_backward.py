@@ -1,0 +1,124 @@
+"""Backward parity on the GPU: fa_backward through the C ABI against the fp64
+oracle's exact gradients of <dO, O>.
+
+The GPU backward consumes the GPU forward's O and LSE (its own saved state);
+the oracle's gradients use its own fp64 forward.  Tolerance: dQ, dK, dV
+max-abs <= 5e-2 (bf16 inputs, fp32 accumulation) on the training-step
+workload.  Edge-case shapes can make a gradient large (with key length 1,
+dV of key 0 sums dO over every row), and above |x| = 16 one bf16 half-ulp
+alone exceeds 5e-2; there the bound is 5e-2 plus one bf16 ulp of |ref|.
+"""
+
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+import oracle
+from tests.gpu_helpers import custom, device_inputs, from_device, lib, log_case, max_abs, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+G_TOL = 5e-2
+O_TOL = 2e-2
+
+
+def run_fwd_bwd(torch, cfg, inputs, lengths=None):
+    fa = lib()
+    dev = device_inputs(torch, cfg, inputs)
+    lens = dev["lengths"]
+    o, lse = fa.forward(dev["q"], dev["k"], dev["v"], scale=cfg.scale, causal=cfg.causal,
+                        seqlens_k=lens)
+    dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, scale=cfg.scale,
+                             causal=cfg.causal, seqlens_k=lens)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+def oracle_grads(cfg, inputs, heads=None):
+    """fp64 forward + backward on the selected (b, h) heads."""
+    w = {n: fi.widen(inputs[n], cfg.dtype) for n in ("q", "k", "v", "do")}
+    lengths = inputs.get("lengths")
+    out = []
+    for (b, h) in heads:
+        sl = lambda x: x[b:b + 1, h:h + 1]
+        lb = None if lengths is None else np.asarray(lengths)[b:b + 1]
+        o, lse = oracle.attention_materialised(sl(w["q"]), sl(w["k"]), sl(w["v"]), cfg.scale,
+                                               cfg.causal, lb)
+        g = oracle.attention_backward(sl(w["q"]), sl(w["k"]), sl(w["v"]), o, sl(w["do"]), lse,
+                                      cfg.scale, cfg.causal, lb)
+        out.append((o, g))
+    return out
+
+
+def compare_heads(cfg, inputs, o, dq, dk, dv, heads, strict=False):
+    worst = 0.0
+    for (b, h), (ref_o, (rq, rk, rv)) in zip(heads, oracle_grads(cfg, inputs, heads)):
+        got_o = from_device(o[b:b + 1, h:h + 1], "bf16")
+        assert max_abs(got_o, ref_o) <= O_TOL
+        for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            g = from_device(got[b:b + 1, h:h + 1], "bf16")
+            assert not np.any(np.isnan(g)), name
+            err = max_abs(g, ref)
+            if strict:
+                assert err <= G_TOL, f"{name} head {(b, h)} max abs error {err:.3e}"
+            else:
+                bound = G_TOL + 2.0 ** -8 * np.abs(ref)
+                assert np.all(np.abs(g - ref) <= bound), f"{name} head {(b, h)} err {err:.3e}"
+            worst = max(worst, err)
+    return worst
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_shapes_all_heads(d, causal):
+    torch = torch_cuda()
+    for N in (1, 17, 64, 65, 129, 200, 257):
+        for lens_kind in ("none", "edges"):
+            lengths = None if lens_kind == "none" else np.array([0, 1, N, max(N - 3, 0)], np.int32)
+            B = 2 if lengths is None else 4
+            cfg = custom(5, B=B, H=2, N=N, d=d, causal=causal)
+            log_case(test="bwd-small", N=N, d=d, causal=causal, lengths=lens_kind)
+            inputs = fi.make_inputs(cfg, seed=100 + N)
+            inputs["lengths"] = lengths
+            o, lse, dq, dk, dv = run_fwd_bwd(torch, cfg, inputs)
+            heads = [(b, h) for b in range(B) for h in range(2)]
+            compare_heads(cfg, inputs, o, dq, dk, dv, heads)
+            if lengths is not None:
+                # keys past the length and every key of the empty sequence get zero gradient
+                for b in range(B):
+                    Lb = int(lengths[b])
+                    assert torch.count_nonzero(dk[b, :, Lb:].view(torch.int16)).item() == 0
+                    assert torch.count_nonzero(dv[b, :, Lb:].view(torch.int16)).item() == 0
+                assert torch.count_nonzero(dq[0].view(torch.int16)).item() == 0
+
+
+def test_config5_training_step():
+    torch = torch_cuda()
+    cfg = fi.CONFIGS[5]
+    log_case(test="config5", shape=cfg.shape)
+    inputs = fi.make_inputs(cfg)
+    o, lse, dq, dk, dv = run_fwd_bwd(torch, cfg, inputs)
+    for t in (o, dq, dk, dv):
+        assert not torch.isnan(t).any().item()
+    worst = compare_heads(cfg, inputs, o, dq, dk, dv, [(0, 0), (0, 31), (1, 0), (1, 17)],
+                          strict=True)
+    print(f"config5 grads max abs err {worst:.3e}", flush=True)
+    # invariants on all 64 heads: every row of dS sums to zero, so sum_j dK_j = 0;
+    # sum_j dV_j = sum_i dO_i (every causal row sees key 0); dQ of row 0 is 0.
+    # Bound: each bf16 output carries at most a half-ulp (2^-9 relative) rounding.
+    dk64 = dk.double()
+    assert (dk64.sum(dim=2).abs() <= dk64.abs().sum(dim=2) * 2.0 ** -8 + 1e-2).all().item()
+    do_sum = torch.from_numpy(fi.widen(inputs["do"], "bf16").sum(axis=2)).cuda()
+    dv64 = dv.double()
+    assert ((dv64.sum(dim=2) - do_sum).abs() <= dv64.abs().sum(dim=2) * 2.0 ** -8 + 1e-2).all().item()
+    assert dq[:, :, 0].float().abs().max().item() <= 1e-2
+
+
+def test_backward_is_deterministic():
+    torch = torch_cuda()
+    cfg = custom(5, B=1, H=3, N=700)
+    inputs = fi.make_inputs(cfg, seed=8)
+    r1 = run_fwd_bwd(torch, cfg, inputs)
+    r2 = run_fwd_bwd(torch, cfg, inputs)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)

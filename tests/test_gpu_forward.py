@@ -1,0 +1,244 @@
+"""Forward parity on the GPU: fa_forward through the C ABI against the fp64
+oracle on the same seeded inputs.
+
+Tolerances: O max-abs <= 1e-5 for fp32 inputs and <= 2e-2 for bf16 inputs;
+LSE <= 1e-5 abs for fp32 and <= 1e-3 + 1e-5 |LSE| for bf16; empty rows must
+give O == 0 and LSE == -inf exactly.
+"""
+
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+import oracle
+from tests.gpu_helpers import (check_lse, custom, device_inputs, from_device, lib, log_case,
+                               max_abs, torch_cuda)
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = {"f32": 1e-5, "bf16": 2e-2}
+LSE_TOL = {"f32": (1e-5, 0.0), "bf16": (1e-3, 1e-5)}
+
+
+def run_forward(torch, cfg, inputs, stream=None):
+    fa = lib()
+    dev = device_inputs(torch, cfg, inputs)
+    if stream is None:
+        o, lse = fa.forward(dev["q"], dev["k"], dev["v"], scale=cfg.scale, causal=cfg.causal,
+                            seqlens_k=dev["lengths"])
+    else:
+        with torch.cuda.stream(stream):
+            o, lse = fa.forward(dev["q"], dev["k"], dev["v"], scale=cfg.scale,
+                                causal=cfg.causal, seqlens_k=dev["lengths"])
+    torch.cuda.synchronize()
+    return from_device(o, cfg.dtype), lse.cpu().numpy().astype(np.float64)
+
+
+def widen_all(cfg, inputs):
+    return [fi.widen(inputs[n], cfg.dtype) for n in ("q", "k", "v")]
+
+
+def assert_forward_close(cfg, o, lse, ref_o, ref_lse):
+    assert not np.any(np.isnan(o))
+    err = max_abs(o, ref_o)
+    assert err <= O_TOL[cfg.dtype], f"O max abs error {err:.3e}"
+    check_lse(lse, ref_lse, *LSE_TOL[cfg.dtype])
+    empty = np.isneginf(ref_lse)
+    assert np.all(o[empty] == 0.0)
+    return err
+
+
+def test_config1_fp32_full_against_both_routes():
+    torch = torch_cuda()
+    cfg = fi.CONFIGS[1]
+    log_case(test="config1", shape=cfg.shape, dtype=cfg.dtype)
+    inputs = fi.make_inputs(cfg)
+    o, lse = run_forward(torch, cfg, inputs)
+    q, k, v = widen_all(cfg, inputs)
+    ra_o, ra_l = oracle.attention_materialised(q, k, v, cfg.scale)
+    rb_o, rb_l = oracle.attention_online(q, k, v, cfg.scale, tile=64)
+    assert_forward_close(cfg, o, lse, ra_o, ra_l)
+    assert_forward_close(cfg, o, lse, rb_o, rb_l)
+
+
+SMALL_N = [1, 2, 63, 65, 127, 129, 256, 300, 513]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_shapes_all_rows(d, causal, dtype):
+    """Ragged N across several tiles, every length edge case, every row."""
+    torch = torch_cuda()
+    for N in SMALL_N:
+        for lens_kind in ("none", "edges", "random"):
+            if lens_kind == "none":
+                lengths = None
+            elif lens_kind == "edges":
+                lengths = np.array([0, 1, N, max(N - 1, 0)], np.int32)
+            else:
+                lengths = np.random.default_rng(N).integers(0, N + 1, 4).astype(np.int32)
+            B = 4 if lengths is not None else 2
+            cfg = custom(2, B=B, H=3, N=N, d=d, dtype=dtype, causal=causal)
+            log_case(test="small", N=N, d=d, causal=causal, dtype=dtype, lengths=lens_kind)
+            inputs = fi.make_inputs(cfg, seed=N)
+            inputs["lengths"] = lengths
+            o, lse = run_forward(torch, cfg, inputs)
+            q, k, v = widen_all(cfg, inputs)
+            ref_o, ref_l = oracle.attention_materialised(q, k, v, cfg.scale, causal, lengths)
+            assert_forward_close(cfg, o, lse, ref_o, ref_l)
+
+
+def test_lengths_clamped_to_range():
+    torch = torch_cuda()
+    cfg = custom(2, B=3, H=2, N=130, causal=True)
+    inputs = fi.make_inputs(cfg, seed=5)
+    inputs["lengths"] = np.array([-7, 500, 64], np.int32)
+    o, lse = run_forward(torch, cfg, inputs)
+    q, k, v = widen_all(cfg, inputs)
+    ref_o, ref_l = oracle.attention_materialised(q, k, v, cfg.scale, True,
+                                                 np.array([0, 130, 64]))
+    assert_forward_close(cfg, o, lse, ref_o, ref_l)
+
+
+def test_config2_full():
+    torch = torch_cuda()
+    cfg = fi.CONFIGS[2]
+    log_case(test="config2", shape=cfg.shape)
+    inputs = fi.make_inputs(cfg)
+    o, lse = run_forward(torch, cfg, inputs)
+    q, k, v = widen_all(cfg, inputs)
+    ref_o, ref_l = oracle.attention_materialised(q, k, v, cfg.scale, False)
+    err = assert_forward_close(cfg, o, lse, ref_o, ref_l)
+    print(f"config2 O max abs err {err:.3e}", flush=True)
+
+
+def _sampled_rows(rng, N, extra=()):
+    rows = set(rng.choice(N, size=min(N, 64), replace=False).tolist())
+    for t in (64, 128, 256):
+        for base in range(0, N, 1024):
+            for r in (base + t - 1, base + t):
+                if 0 <= r < N:
+                    rows.add(r)
+    rows.update(r for r in extra if 0 <= r < N)
+    rows.update({0, N - 1})
+    return np.array(sorted(rows))
+
+
+def test_config3_full_heads_and_sampled_rows():
+    torch = torch_cuda()
+    cfg = fi.CONFIGS[3]
+    log_case(test="config3", shape=cfg.shape)
+    inputs = fi.make_inputs(cfg)
+    o, lse = run_forward(torch, cfg, inputs)
+    assert not np.any(np.isnan(o)) and not np.any(np.isnan(lse))
+    q, k, v = widen_all(cfg, inputs)
+    rng = np.random.default_rng(3)
+    worst = 0.0
+    for h in range(cfg.H):
+        if h in (0, 31):
+            ref_o, ref_l = oracle.attention_materialised(q[:, h:h + 1], k[:, h:h + 1],
+                                                         v[:, h:h + 1], cfg.scale, True)
+            worst = max(worst, assert_forward_close(cfg, o[:, h:h + 1], lse[:, h:h + 1],
+                                                    ref_o, ref_l))
+        else:
+            rows = _sampled_rows(rng, cfg.N)
+            ref_o, ref_l = oracle.attention_rows(q[0, h], k[0, h], v[0, h], rows, cfg.scale, True)
+            worst = max(worst, assert_forward_close(cfg, o[0, h, rows], lse[0, h, rows],
+                                                    ref_o, ref_l))
+    print(f"config3 O max abs err {worst:.3e}", flush=True)
+
+
+def test_config4_lengths_x30_sampled():
+    torch = torch_cuda()
+    fa = lib()
+    cfg = fi.CONFIGS[4]
+    log_case(test="config4", shape=cfg.shape)
+    inputs = fi.make_inputs(cfg)
+    L = inputs["lengths"]
+    dev = device_inputs(torch, cfg, inputs)
+    o_dev, lse_dev = fa.forward(dev["q"], dev["k"], dev["v"], scale=cfg.scale, causal=True,
+                                seqlens_k=dev["lengths"])
+    torch.cuda.synchronize()
+    del dev
+    lse = lse_dev.cpu().numpy().astype(np.float64)
+    assert not np.any(np.isnan(lse))
+    # the length-0 sequence: every row empty, O exactly zero
+    assert np.all(np.isneginf(lse[0]))
+    assert torch.count_nonzero(o_dev[0].view(torch.int16)).item() == 0
+    assert not np.any(np.isneginf(lse[1:]))
+    assert not torch.isnan(o_dev).any().item()
+    rng = np.random.default_rng(4)
+    b_small = int(np.argmin(np.where(L > 0, L, cfg.N + 1)))
+    b_large = int(np.argmax(L))
+    worst = 0.0
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            focus = b in (b_small, b_large) and h in (0, 31)
+            if not focus and rng.random() > 0.1:
+                continue
+            Lb = int(L[b])
+            extra = [Lb - 2, Lb - 1, Lb, Lb + 1] if focus else [Lb - 1, Lb]
+            rows = _sampled_rows(rng, cfg.N, extra)
+            qh = fi.widen(inputs["q"][b, h], "bf16")
+            kh = fi.widen(inputs["k"][b, h], "bf16")
+            vh = fi.widen(inputs["v"][b, h], "bf16")
+            ref_o, ref_l = oracle.attention_rows(qh, kh, vh, rows, cfg.scale, True, Lb)
+            got = from_device(o_dev[b, h][torch.from_numpy(rows).cuda()], "bf16")
+            worst = max(worst, assert_forward_close(cfg, got, lse[b, h, rows], ref_o, ref_l))
+    assert np.max(np.abs(lse[1:])) > 60.0      # the x30 scores really are large
+    print(f"config4 O max abs err {worst:.3e}", flush=True)
+
+
+def test_forward_is_deterministic_and_stream_aware():
+    torch = torch_cuda()
+    cfg = custom(3, B=1, H=4, N=1000)
+    inputs = fi.make_inputs(cfg, seed=9)
+    o1, l1 = run_forward(torch, cfg, inputs)
+    s = torch.cuda.Stream()
+    o2, l2 = run_forward(torch, cfg, inputs, stream=s)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_forward_writes_nothing_outside_outputs():
+    torch = torch_cuda()
+    fa = lib()
+    cfg = custom(3, B=2, H=2, N=77)
+    inputs = fi.make_inputs(cfg, seed=2)
+    dev = device_inputs(torch, cfg, inputs)
+    n = cfg.B * cfg.H * cfg.N * cfg.d
+    pad = 4096
+    o_buf = torch.full((n + pad,), -7.0, dtype=torch.bfloat16, device="cuda")
+    l_buf = torch.full((cfg.B * cfg.H * cfg.N + pad,), -7.0, dtype=torch.float32, device="cuda")
+    o = o_buf[:n].view(cfg.shape)
+    lse = l_buf[:cfg.B * cfg.H * cfg.N].view(cfg.B, cfg.H, cfg.N)
+    fa.forward(dev["q"], dev["k"], dev["v"], scale=cfg.scale, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(o_buf[n:] == -7.0).item()
+    assert torch.all(l_buf[cfg.B * cfg.H * cfg.N:] == -7.0).item()
+    ref_o, ref_l = oracle.attention_materialised(*(fi.widen(inputs[x], "bf16") for x in "qkv"),
+                                                 cfg.scale, True)
+    assert_forward_close(cfg, from_device(o, "bf16"), lse.cpu().numpy().astype(np.float64),
+                         ref_o, ref_l)
+
+
+def test_peak_memory_grows_linearly():
+    """Only the I/O tensors are allocated: doubling N doubles peak memory."""
+    torch = torch_cuda()
+    fa = lib()
+    peaks = []
+    for N in (8192, 16384):
+        torch.cuda.empty_cache()
+        q = torch.randn(1, 8, N, 128, device="cuda").to(torch.bfloat16)
+        k = torch.randn_like(q)
+        v = torch.randn_like(q)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        fa.forward(q, k, v, causal=True)
+        torch.cuda.synchronize()
+        peaks.append(torch.cuda.max_memory_allocated() - base)
+        del q, k, v
+    # O (N*d*2 B per head) plus LSE (4 B per row): exactly linear in N
+    assert peaks[1] <= 2.05 * peaks[0]
+    assert peaks[0] <= 8 * 8192 * (128 * 2 + 4) * 1.1
