@@ -74,6 +74,9 @@ def parse_args():
     p.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time for the oracle baseline sample (0 disables it)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="after timing, run one device-to-device copy of MIB MiB so that HBM "
+                        "byte counters can be scaled against a kernel of known traffic")
     return p.parse_args()
 
 
@@ -241,6 +244,16 @@ def main():
         bwd_ms = sum(per_kernel[n] for n in names[1:])
         extra["fwd_tflops"] = round(fwd_f / (fwd_ms * 1e-3) / 1e12, 1)
         extra["bwd_tflops"] = round((flops - fwd_f) / (bwd_ms * 1e-3) / 1e12, 1)
+
+    if args.calibrate_copy > 0:
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {nbytes} bytes read and {nbytes} bytes written")
+        del src, dst
 
     cpu = None
     if args.cpu_seconds > 0:
