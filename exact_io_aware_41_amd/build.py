@@ -24,6 +24,9 @@ LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+# per-source code-generation options: the backward kernels keep their MFMA
+# results in VGPRs rather than accumulation registers (fewer register copies)
+EXTRA_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 
@@ -68,7 +71,8 @@ def build(verbose: bool = False) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmds.append([cc, *common_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+            cmds.append([cc, *common_flags(), *EXTRA_FLAGS.get(src, []), *lang, "-c",
+                         os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
         with ThreadPoolExecutor(len(cmds)) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))

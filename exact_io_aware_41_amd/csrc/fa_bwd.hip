@@ -22,6 +22,8 @@
 // Kernels 2 and 3 recompute S and P each, so the backward executes 14 N^2 d
 // flops per head (7 contractions) for the 10 N^2 d it is credited with.
 
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_internal.h"
 
@@ -98,7 +100,7 @@ struct DkdvCfg {
 
 template <int D, int NW, int BQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1)))
 void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                         const float* __restrict__ LSE, const float* __restrict__ Dlt,
@@ -115,7 +117,7 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -165,24 +167,33 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     dvacc[db] = f32x16{};
   }
 
-  u32x4 qreg[C::UPT][4], oreg[C::UPT][4];
+  // staging: with at least two threads per unit, half the threads stage Q and
+  // half stage dO; otherwise every thread stages both
+  constexpr bool kSplit = C::NT >= 2 * C::UNITS;
+  constexpr int kRegsets = kSplit ? 1 : 2;
+  constexpr int kUpt = kSplit ? 1 : C::UPT;
+  u32x4 sreg[kRegsets][kUpt][4];
   float lreg = 0.f, dreg = 0.f;
 
-  auto load_tile = [&](int qi) {
+  auto load_tile = [&](int qi) FA_INLINE {
     const int qt0 = q_begin + qi * BQ;
 #pragma unroll
-    for (int i = 0; i < C::UPT; ++i) {
-      const int u = tid + i * C::NT;
-      const int qg = u % (BQ / 4);
-      const int dc = u / (BQ / 4);
+    for (int set = 0; set < kRegsets; ++set)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = qt0 + 4 * qg + r;
-        const bool ok = (u < C::UNITS) && row < N;
-        qreg[i][r] = ok ? *reinterpret_cast<const u32x4*>(Qh + (size_t)row * D + dc * 8) : u32x4{};
-        oreg[i][r] = ok ? *reinterpret_cast<const u32x4*>(dOh + (size_t)row * D + dc * 8) : u32x4{};
+      for (int i = 0; i < kUpt; ++i) {
+        const int u = kSplit ? tid % C::UNITS : tid + i * C::NT;
+        const bool is_q = kSplit ? (tid < C::UNITS) : (set == 0);
+        const __bf16* src = is_q ? Qh : dOh;
+        const int qg = u % (BQ / 4);
+        const int dc = u / (BQ / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = qt0 + 4 * qg + r;
+          const bool ok = (kSplit ? tid < 2 * C::UNITS : u < C::UNITS) && row < N;
+          sreg[set][i][r] = ok ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + dc * 8)
+                               : u32x4{};
+        }
       }
-    }
     if (tid < BQ) {
       const int row = qt0 + tid;
       // rows past N, and rows that see no key, get +inf so that P = 0
@@ -191,23 +202,24 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       dreg = row < N ? Dh[row] : 0.f;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf) FA_INLINE {
 #pragma unroll
-    for (int i = 0; i < C::UPT; ++i) {
-      const int u = tid + i * C::NT;
-      if (u < C::UNITS) {
+    for (int set = 0; set < kRegsets; ++set)
+#pragma unroll
+      for (int i = 0; i < kUpt; ++i) {
+        const int u = kSplit ? tid % C::UNITS : tid + i * C::NT;
+        const bool active = kSplit ? tid < 2 * C::UNITS : u < C::UNITS;
+        if (!active) continue;
+        const bool is_q = kSplit ? (tid < C::UNITS) : (set == 0);
+        __bf16* rm = is_q ? Qs[buf] : dOs[buf];
+        __bf16* tr = is_q ? Qt[buf] : dOt[buf];
         const int qg = u % (BQ / 4);
         const int dc = u / (BQ / 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          *reinterpret_cast<u32x4*>(&Qs[buf][(4 * qg + r) * C::RPITCH + dc * 8]) = qreg[i][r];
-          *reinterpret_cast<u32x4*>(&dOs[buf][(4 * qg + r) * C::RPITCH + dc * 8]) = oreg[i][r];
-        }
-        const int pos = perm_pos(qg);
-        store_transposed(Qt[buf], C::TPITCH, dc * 8, pos, qreg[i]);
-        store_transposed(dOt[buf], C::TPITCH, dc * 8, pos, oreg[i]);
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<u32x4*>(&rm[(4 * qg + r) * C::RPITCH + dc * 8]) = sreg[set][i][r];
+        store_transposed(tr, C::TPITCH, dc * 8, perm_pos(qg), sreg[set][i]);
       }
-    }
     if (tid < BQ) {
       Ls[buf][tid] = lreg;
       Ds[buf][tid] = dreg;
@@ -246,31 +258,38 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
           pacc[qb] = mfma_bf16(oa, vf[ks], pacc[qb]);
         }
 
-      const bool need_mask = (kw0 + 31 >= kv_len) || (causal && qt0 < kw0 + 31);
-      // ---- P = exp2(s*scale*log2e - LSE*log2e); dS = P (dP - D)
+      // ---- P = exp2(s*scale*log2e - LSE*log2e); dS = P (dP - D); the mask is
+      // applied only on tiles that cross the diagonal or the key length
       bf16x8 pa[C::NG], dsa[C::NG];
+      auto p_and_ds = [&](auto masked_tag) FA_INLINE {
+        constexpr bool kMasked = decltype(masked_tag)::value;
 #pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) {
+        for (int qb = 0; qb < C::NQB; ++qb) {
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int r0 = qb * 32 + 8 * a4 + 4 * hi;
-          const f32x4 lq = *reinterpret_cast<const f32x4*>(&Ls[buf][r0]);
-          const f32x4 dq = *reinterpret_cast<const f32x4*>(&Ds[buf][r0]);
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const int r0 = qb * 32 + 8 * a4 + 4 * hi;
+            const f32x4 lq = *reinterpret_cast<const f32x4*>(&Ls[buf][r0]);
+            const f32x4 dq = *reinterpret_cast<const f32x4*>(&Ds[buf][r0]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int v = 4 * a4 + e;
-            float p = fast_exp2(__builtin_fmaf(sacc[qb][v], scale_log2, -lq[e]));
-            if (need_mask) {
-              const int query = qt0 + r0 + e;
-              const bool vis = my_key < kv_len && (!causal || my_key <= query);
-              if (!vis) p = 0.f;
+            for (int e = 0; e < 4; ++e) {
+              const int v = 4 * a4 + e;
+              float p = fast_exp2(__builtin_fmaf(sacc[qb][v], scale_log2, -lq[e]));
+              if (kMasked) {
+                const int query = qt0 + r0 + e;
+                const bool vis = my_key < kv_len && (!causal || my_key <= query);
+                p = vis ? p : 0.f;
+              }
+              const float ds = p * (pacc[qb][v] - dq[e]);
+              pa[2 * qb + (v >> 3)][v & 7] = to_bf16(p);
+              dsa[2 * qb + (v >> 3)][v & 7] = to_bf16(ds);
             }
-            const float ds = p * (pacc[qb][v] - dq[e]);
-            pa[2 * qb + (v >> 3)][v & 7] = to_bf16(p);
-            dsa[2 * qb + (v >> 3)][v & 7] = to_bf16(ds);
           }
         }
-      }
+      };
+      if ((kw0 + 31 >= kv_len) || (causal && qt0 < kw0 + 31))
+        p_and_ds(std::true_type{});
+      else
+        p_and_ds(std::false_type{});
 
       // ---- dV += P^T dO ; dK += dS^T Q   (B operands from the transposed copies)
 #pragma unroll
@@ -303,6 +322,250 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// 2b. dK / dV with paired waves (two waves per SIMD)
+//
+// Eight waves; waves w and w+4 (a pair, same SIMD) share 32 keys of the
+// work-group's 128.  For each 64-query tile, wave w computes S and dP for
+// query rows 0..31 and wave w+4 for rows 32..63 (full head dimension), both
+// turn them into bf16 P and dS, and swap them through a small LDS exchange
+// area.  Then each wave accumulates dV = P^T dO and dK = dS^T Q for all 64
+// rows but only its half of the head dimension.  Per wave this halves the
+// dK/dV accumulators, so a wave fits in 256 VGPRs and two waves share each
+// SIMD, without any duplicated MFMA work.
+// ---------------------------------------------------------------------------
+template <int D, int BQ>
+struct DkdvPairCfg {
+  static constexpr int NW = 8;
+  static constexpr int BK = 128;           // keys per work-group (4 pairs x 32)
+  static constexpr int NT = NW * 64;
+  static constexpr int KS = D / 16;
+  static constexpr int NG = BQ / 16;       // 16-query groups per tile
+  static constexpr int NDB = D / 32;
+  static constexpr int HDB = NDB / 2;      // 32-feature blocks per wave (its half)
+  static constexpr int RPITCH = D + 8;
+  static constexpr int TPITCH = BQ + 8;
+  static constexpr int UNITS = (BQ / 4) * (D / 8);  // 4-row x 8-feature units per tensor
+  static_assert(BQ == 64, "two 32-row halves per tile");
+  static_assert(NDB % 2 == 0, "head dimension splits in two halves of 32-feature blocks");
+  static_assert(2 * UNITS <= NT, "one staging unit per thread");
+};
+
+template <int D, int BQ>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                             const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                             const float* __restrict__ LSE, const float* __restrict__ Dlt,
+                             const int32_t* __restrict__ seqlens_k, float scale,
+                             float scale_log2, int causal, __bf16* __restrict__ dK,
+                             __bf16* __restrict__ dV, int B, int H, int N, int n_ktiles) {
+  using C = DkdvPairCfg<D, BQ>;
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * C::RPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 dOs[2][BQ * C::RPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 Qt[D * C::TPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 dOt[D * C::TPITCH];
+  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+  // P and dS fragments handed to the partner wave: [wave][slot][lane]
+  __shared__ __attribute__((aligned(16))) bf16x8 Xs[C::NW][4][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int pr = wave & 3;      // key block of the pair
+  const int half = wave >> 2;   // query half for S/dP, feature half for dK/dV
+
+  const int bh_count = B * H;
+  const int kt = blockIdx.x / bh_count;
+  const int bh = blockIdx.x - kt * bh_count;
+  const int b = bh / H;
+  const int h = bh - b * H;
+  const size_t head = (size_t)b * H + h;
+  const __bf16* Qh = Q + head * (size_t)N * D;
+  const __bf16* Kh = K + head * (size_t)N * D;
+  const __bf16* Vh = V + head * (size_t)N * D;
+  const __bf16* dOh = dO + head * (size_t)N * D;
+  const float* Lh = LSE + head * (size_t)N;
+  const float* Dh = Dlt + head * (size_t)N;
+  __bf16* dKh = dK + head * (size_t)N * D;
+  __bf16* dVh = dV + head * (size_t)N * D;
+
+  const int kv_len = key_length(seqlens_k, b, N);
+  const int k0 = kt * C::BK;
+  const int kw0 = k0 + pr * 32;
+  const int my_key = kw0 + l32;
+  const int q_begin = causal ? (k0 / BQ) * BQ : 0;
+  const int n_qt = (k0 < kv_len) ? (N - q_begin + BQ - 1) / BQ : 0;
+
+  // the pair's K and V rows (B operands of S = Q K^T and dP = dO V^T)
+  bf16x8 kf[C::KS], vf[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    if (my_key < N) {
+      kf[ks] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)my_key * D + ks * 16 + hi * 8);
+      vf[ks] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)my_key * D + ks * 16 + hi * 8);
+    } else {
+      kf[ks] = bf16x8{};
+      vf[ks] = bf16x8{};
+    }
+  }
+  f32x16 dkacc[C::HDB], dvacc[C::HDB];
+#pragma unroll
+  for (int j = 0; j < C::HDB; ++j) {
+    dkacc[j] = f32x16{};
+    dvacc[j] = f32x16{};
+  }
+
+  // staging: threads [0, UNITS) stage Q, [UNITS, 2 UNITS) stage dO
+  u32x4 sreg[4];
+  float lreg = 0.f, dreg = 0.f;
+  const bool stager = tid < 2 * C::UNITS;
+  const bool stage_q = tid < C::UNITS;
+  const int su = tid % C::UNITS;
+  const int sqg = su % (BQ / 4);
+  const int sdc = su / (BQ / 4);
+  auto load_tile = [&](int qi) FA_INLINE {
+    const int qt0 = q_begin + qi * BQ;
+    if (stager) {
+      const __bf16* src = stage_q ? Qh : dOh;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = qt0 + 4 * sqg + r;
+        sreg[r] = row < N ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + sdc * 8)
+                          : u32x4{};
+      }
+    }
+    if (tid < BQ) {
+      const int row = qt0 + tid;
+      // rows past N, and rows that see no key, get +inf so that P = 0
+      const float lse = row < N ? Lh[row] : __builtin_huge_valf();
+      lreg = (lse == kNegInf) ? __builtin_huge_valf() : lse * kLog2e;
+      dreg = row < N ? Dh[row] : 0.f;
+    }
+  };
+  auto store_rowmajor = [&](int buf) FA_INLINE {
+    if (stager) {
+      __bf16* rm = stage_q ? Qs[buf] : dOs[buf];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<u32x4*>(&rm[(4 * sqg + r) * C::RPITCH + sdc * 8]) = sreg[r];
+    }
+    if (tid < BQ) {
+      Ls[buf][tid] = lreg;
+      Ds[buf][tid] = dreg;
+    }
+  };
+  auto store_transposed_copy = [&]() FA_INLINE {
+    if (stager) store_transposed(stage_q ? Qt : dOt, C::TPITCH, sdc * 8, perm_pos(sqg), sreg);
+  };
+
+  if (n_qt > 0) {
+    load_tile(0);
+    store_rowmajor(0);
+    store_transposed_copy();
+    __syncthreads();
+  }
+
+  const bool pair_keys_valid = kw0 < kv_len;
+  for (int qi = 0; qi < n_qt; ++qi) {
+    const int buf = qi & 1;
+    const int qt0 = q_begin + qi * BQ;
+    const bool more = qi + 1 < n_qt;
+    if (more) load_tile(qi + 1);
+    const bool pair_active = pair_keys_valid && (!causal || qt0 + BQ - 1 >= kw0);
+
+    bf16x8 pa[2], dsa[2];
+    if (pair_active) {
+      // ---- phase 1: S and dP for this wave's 32 query rows (one key per lane)
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const int ro = (32 * half + l32) * C::RPITCH + ks * 16 + hi * 8;
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[buf][ro]);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&dOs[buf][ro]);
+        sacc = mfma_bf16(qa, kf[ks], sacc);
+        pacc = mfma_bf16(oa, vf[ks], pacc);
+      }
+      auto p_and_ds = [&](auto masked_tag) FA_INLINE {
+        constexpr bool kMasked = decltype(masked_tag)::value;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int r0 = 32 * half + 8 * a4 + 4 * hi;
+          const f32x4 lq = *reinterpret_cast<const f32x4*>(&Ls[buf][r0]);
+          const f32x4 dq = *reinterpret_cast<const f32x4*>(&Ds[buf][r0]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * a4 + e;
+            float p = fast_exp2(__builtin_fmaf(sacc[v], scale_log2, -lq[e]));
+            if (kMasked) {
+              const int query = qt0 + r0 + e;
+              const bool vis = my_key < kv_len && (!causal || my_key <= query);
+              p = vis ? p : 0.f;
+            }
+            pa[v >> 3][v & 7] = to_bf16(p);
+            dsa[v >> 3][v & 7] = to_bf16(p * (pacc[v] - dq[e]));
+          }
+        }
+      };
+      if ((kw0 + 31 >= kv_len) || (causal && qt0 + 32 * half < kw0 + 31))
+        p_and_ds(std::true_type{});
+      else
+        p_and_ds(std::false_type{});
+      Xs[wave][0][lane] = pa[0];
+      Xs[wave][1][lane] = pa[1];
+      Xs[wave][2][lane] = dsa[0];
+      Xs[wave][3][lane] = dsa[1];
+    }
+    __syncthreads();
+    // the next tile's row-major copies go to the other buffer while phase 2 runs
+    if (more) store_rowmajor(buf ^ 1);
+    if (pair_active) {
+      // ---- phase 2: dV += P^T dO, dK += dS^T Q over all 64 rows, own feature half
+      const int partner = wave ^ 4;
+      bf16x8 po[2], dso[2];
+      po[0] = Xs[partner][0][lane];
+      po[1] = Xs[partner][1][lane];
+      dso[0] = Xs[partner][2][lane];
+      dso[1] = Xs[partner][3][lane];
+#pragma unroll
+      for (int g = 0; g < C::NG; ++g) {
+        // groups 2*half, 2*half+1 are this wave's rows; the others the partner's
+        const bool own = (g >> 1) == half;
+        const bf16x8 pfrag = own ? pa[g & 1] : po[g & 1];
+        const bf16x8 dsfrag = own ? dsa[g & 1] : dso[g & 1];
+#pragma unroll
+        for (int j = 0; j < C::HDB; ++j) {
+          const int db = half * C::HDB + j;
+          const int to = (db * 32 + l32) * C::TPITCH + g * 16 + hi * 8;
+          const bf16x8 ob = *reinterpret_cast<const bf16x8*>(&dOt[to]);
+          const bf16x8 qbv = *reinterpret_cast<const bf16x8*>(&Qt[to]);
+          dvacc[j] = mfma_bf16(pfrag, ob, dvacc[j]);
+          dkacc[j] = mfma_bf16(dsfrag, qbv, dkacc[j]);
+        }
+      }
+    }
+    __syncthreads();
+    if (more) store_transposed_copy();
+  }
+
+  // ---- write dK = scale * acc, dV = acc for this wave's feature half
+#pragma unroll
+  for (int j = 0; j < C::HDB; ++j) {
+    const int db = half * C::HDB + j;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = kw0 + c_row(v, lane);
+      if (key < N) {
+        dKh[(size_t)key * D + db * 32 + l32] = to_bf16(dkacc[j][v] * scale);
+        dVh[(size_t)key * D + db * 32 + l32] = to_bf16(dvacc[j][v]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 3. dQ
 // ---------------------------------------------------------------------------
 template <int D, int NW, int BC>
@@ -321,7 +584,7 @@ struct DqCfg {
 
 template <int D, int NW, int BC>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(1, 2)))
+__attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1)))
 void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                       const float* __restrict__ LSE, const float* __restrict__ Dlt,
@@ -334,7 +597,7 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -376,38 +639,49 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) dqacc[db] = f32x16{};
 
-  u32x4 kreg[C::UPT][4], vreg[C::UPT][4];
-  auto load_tile = [&](int kt) {
+  // staging: with at least two threads per unit, half the threads stage K and
+  // half stage V; otherwise every thread stages both
+  constexpr bool kSplit = C::NT >= 2 * C::UNITS;
+  constexpr int kRegsets = kSplit ? 1 : 2;
+  constexpr int kUpt = kSplit ? 1 : C::UPT;
+  u32x4 sreg[kRegsets][kUpt][4];
+  auto load_tile = [&](int kt) FA_INLINE {
     const int key0 = kt * BC;
 #pragma unroll
-    for (int i = 0; i < C::UPT; ++i) {
-      const int u = tid + i * C::NT;
-      const int kg = u % (BC / 4);
-      const int dc = u / (BC / 4);
+    for (int set = 0; set < kRegsets; ++set)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + 4 * kg + r;
-        const bool ok = (u < C::UNITS) && key < kv_len;
-        kreg[i][r] = ok ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + dc * 8) : u32x4{};
-        vreg[i][r] = ok ? *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + dc * 8) : u32x4{};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::UPT; ++i) {
-      const int u = tid + i * C::NT;
-      if (u < C::UNITS) {
+      for (int i = 0; i < kUpt; ++i) {
+        const int u = kSplit ? tid % C::UNITS : tid + i * C::NT;
+        const bool is_k = kSplit ? (tid < C::UNITS) : (set == 0);
+        const __bf16* src = is_k ? Kh : Vh;
         const int kg = u % (BC / 4);
         const int dc = u / (BC / 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          *reinterpret_cast<u32x4*>(&Ks[buf][(4 * kg + r) * C::RPITCH + dc * 8]) = kreg[i][r];
-          *reinterpret_cast<u32x4*>(&Vs[buf][(4 * kg + r) * C::RPITCH + dc * 8]) = vreg[i][r];
+          const int key = key0 + 4 * kg + r;
+          const bool ok = (kSplit ? tid < 2 * C::UNITS : u < C::UNITS) && key < kv_len;
+          sreg[set][i][r] = ok ? *reinterpret_cast<const u32x4*>(src + (size_t)key * D + dc * 8)
+                               : u32x4{};
         }
-        store_transposed(Kt[buf], C::TPITCH, dc * 8, perm_pos(kg), kreg[i]);
       }
-    }
+  };
+  auto store_tile = [&](int buf) FA_INLINE {
+#pragma unroll
+    for (int set = 0; set < kRegsets; ++set)
+#pragma unroll
+      for (int i = 0; i < kUpt; ++i) {
+        const int u = kSplit ? tid % C::UNITS : tid + i * C::NT;
+        const bool active = kSplit ? tid < 2 * C::UNITS : u < C::UNITS;
+        if (!active) continue;
+        const bool is_k = kSplit ? (tid < C::UNITS) : (set == 0);
+        __bf16* rm = is_k ? Ks[buf] : Vs[buf];
+        const int kg = u % (BC / 4);
+        const int dc = u / (BC / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<u32x4*>(&rm[(4 * kg + r) * C::RPITCH + dc * 8]) = sreg[set][i][r];
+        if (is_k) store_transposed(Kt[buf], C::TPITCH, dc * 8, perm_pos(kg), sreg[set][i]);
+      }
   };
 
   if (n_kt > 0) {
@@ -482,8 +756,24 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   }
 }
 
-constexpr int kDkdvNW = 4, kDkdvBQ = 64;
-constexpr int kDqNW = 4, kDqBC = 64;
+// Tile choices (compile-time).
+#ifndef FA_DKDV_NW
+#define FA_DKDV_NW 4
+#endif
+#ifndef FA_DKDV_BQ
+#define FA_DKDV_BQ 64
+#endif
+#ifndef FA_DQ_NW
+#define FA_DQ_NW 8
+#endif
+#ifndef FA_DKDV_PAIR
+#define FA_DKDV_PAIR 0
+#endif
+#ifndef FA_DQ_BC
+#define FA_DQ_BC 64
+#endif
+constexpr int kDkdvNW = FA_DKDV_NW, kDkdvBQ = FA_DKDV_BQ;
+constexpr int kDqNW = FA_DQ_NW, kDqBC = FA_DQ_BC;
 
 template <int D>
 hipError_t launch_preprocess_d(const BwdArgs& a) {
@@ -497,6 +787,17 @@ hipError_t launch_preprocess_d(const BwdArgs& a) {
 
 template <int D>
 hipError_t launch_dkdv_d(const BwdArgs& a) {
+#if FA_DKDV_PAIR
+  using CK = DkdvPairCfg<D, 64>;
+  const int n_ktiles = (a.N + CK::BK - 1) / CK::BK;
+  hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<D, 64>),
+                     dim3((unsigned)((long long)n_ktiles * a.B * a.H)), dim3(CK::NT), 0, a.stream,
+                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dout), a.lse,
+                     a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
+                     static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.B, a.H, a.N,
+                     n_ktiles);
+#else
   using CK = DkdvCfg<D, kDkdvNW, kDkdvBQ>;
   const int n_ktiles = (a.N + CK::BK - 1) / CK::BK;
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, kDkdvNW, kDkdvBQ>),
@@ -506,6 +807,7 @@ hipError_t launch_dkdv_d(const BwdArgs& a) {
                      a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
                      static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.B, a.H, a.N,
                      n_ktiles);
+#endif
   return hipGetLastError();
 }
 

@@ -21,6 +21,10 @@
 
 namespace fa {
 
+// Lambdas inside kernels must be inlined: an outlined call passes the
+// captured register state through scratch memory.
+#define FA_INLINE __attribute__((always_inline))
+
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
@@ -28,6 +32,10 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+// s_waitcnt immediate that waits for every outstanding vector-memory access
+// (vmcnt = 0) and leaves the other counters unconstrained.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -31,8 +31,34 @@
 //    tiles that cross the diagonal or the key length apply the mask, on
 //    absolute positions.
 
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_internal.h"
+
+// Tile choices (compile-time; the defaults are the tuned gfx950 configuration).
+// 32 queries per wave keep a wave within 256
+// VGPRs, so an 8-wave work-group (256 query rows) runs two waves per SIMD and
+// one wave's MFMAs overlap the other's softmax.
+#ifndef FA_FWD_QB
+#define FA_FWD_QB 1
+#endif
+#ifndef FA_FWD_NW
+#define FA_FWD_NW 8
+#endif
+#ifndef FA_FWD_BC
+#define FA_FWD_BC 64
+#endif
+#ifndef FA_FWD_PREFETCH
+#define FA_FWD_PREFETCH 6
+#endif
+#ifndef FA_FWD_SCHED
+#define FA_FWD_SCHED 2
+#endif
+#ifndef FA_FWD_DIRECT
+#define FA_FWD_DIRECT 0
+#endif
+
 
 namespace fa {
 
@@ -50,29 +76,52 @@ struct FwdBf16Cfg {
   static constexpr int NDB = D / 32;       // 32-row blocks of O^T
   static constexpr int KPITCH = D + 8;     // bf16 per K row in LDS
   static constexpr int VPITCH = BC + 8;    // bf16 per V^T row in LDS
-  static constexpr int KU = BC * D / 8 / NT;        // 16-byte K chunks per thread
-  static constexpr int VU = (BC / 4) * (D / 8) / NT;  // 4-key x 8-feature V units per thread
+  static constexpr int KUNITS = BC * D / 8;          // 16-byte K chunks per tile
+  static constexpr int KU = (KUNITS + NT - 1) / NT;
+  static constexpr int VUNITS = (BC / 4) * (D / 8);  // 4-key x 8-feature V units per tile
+  static constexpr int VU = (VUNITS + NT - 1) / NT;
   static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
-  static_assert(KU * NT * 8 == BC * D, "K tile must split evenly over threads");
-  static_assert(VU * NT == (BC / 4) * (D / 8), "V tile must split evenly over threads");
 };
+
+// Lazy rescaling threshold (log2 units).  The reference maximum m used for
+// exponentiation only moves when a tile's maximum exceeds it by more than
+// this, so every p = 2^(x - m) stays <= 2^8: the arithmetic is still exact
+// (numerator and denominator share m), finite in fp32 and bf16, and the O
+// accumulators are rescaled only when the maximum really jumps.
+constexpr float kRescaleThreshold = 8.0f;
 
 template <int D, int QB, int NW, int BC>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                         const __bf16* __restrict__ V, const int32_t* __restrict__ seqlens_k,
                         float scale_log2, int causal, __bf16* __restrict__ O,
                         float* __restrict__ LSE, int B, int H, int N, int n_qtiles) {
   using C = FwdBf16Cfg<D, QB, NW, BC>;
+  // Two groups of NW/2 waves; the waves of a SIMD (w and w + NW/2) sit in
+  // different groups.  The second group runs one stage behind: it multiplies
+  // P(t-1) V(t-1) before computing S(t), so while one wave of a SIMD is in its
+  // MFMA phase the other is in its softmax phase.  V therefore lives in a
+  // three-slot ring (group 2 still reads V(t-1) while V(t+1) is written).
+  constexpr bool kPingPong = (NW >= 8);
+  constexpr int kVSlots = kPingPong ? 3 : 2;
+#if FA_FWD_DIRECT
+  // K and V tiles arrive straight from HBM (one 16-byte chunk per lane per
+  // load) as unpadded rows whose 16-byte chunks are XOR-swizzled by row, so
+  // both the row reads of K and the transposed reads of V are conflict-free.
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[kVSlots][BC * D];
+#else
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * C::KPITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D * C::VPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[kVSlots][D * C::VPITCH];
+#endif
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const bool lagging = kPingPong && wave >= NW / 2;
 
   const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
   const size_t head = (size_t)tc.b * H + tc.h;
@@ -85,10 +134,16 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   const int kv_len = key_length(seqlens_k, tc.b, N);
   const int q0 = tc.qt * C::BR;
   const int qw0 = q0 + wave * QB * 32;
-  // last key any row of this work-group can see
+  const int qw_last = qw0 + QB * 32 - 1;
+  // key tiles the work-group loads: up to its last visible key
   int kv_end = kv_len;
   if (causal) kv_end = min(kv_end, min(q0 + C::BR, N));
   const int n_kt = (kv_end + BC - 1) / BC;
+  // key tiles this wave computes (a prefix): under the causal mask a tile whose
+  // first key lies past the wave's last query is skipped
+  int n_act = n_kt;
+  if (qw0 >= N) n_act = 0;
+  else if (causal) n_act = min(n_kt, qw_last / BC + 1);
 
   // ---- Q fragments (B operand of S^T = K Q^T): query l32, features 8*hi + [0..7]
   bf16x8 qf[QB][C::KS];
@@ -109,53 +164,64 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x16{};
-  float m[QB], l[QB];
+  float m[QB], l[QB], alpha[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = kNegInf;
     l[qb] = 0.f;
+    alpha[qb] = 1.f;
   }
 
-  // ---- staging registers for the next K/V tile
+  // ---- staging of the next K/V tile through registers
   u32x4 kreg[C::KU];
   u32x4 vreg[C::VU][4];
-
-  auto load_tile = [&](int kt) {
+  auto load_tile = [&](int kt) FA_INLINE {
     const int key0 = kt * BC;
+    const bool full = key0 + BC <= kv_len;  // uniform: no row of this tile is past the length
 #pragma unroll
     for (int i = 0; i < C::KU; ++i) {
       const int u = tid + i * C::NT;
       const int r = u / (D / 8);
       const int c8 = u % (D / 8);
       const int key = key0 + r;
-      kreg[i] = key < kv_len ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + c8 * 8)
-                             : u32x4{};
+      const bool unit = (C::KUNITS % C::NT == 0) || (u < C::KUNITS);
+      const __bf16* src = Kh + (size_t)key * D + c8 * 8;
+      if (full && unit)
+        kreg[i] = *reinterpret_cast<const u32x4*>(src);
+      else
+        kreg[i] = (unit && key < kv_len) ? *reinterpret_cast<const u32x4*>(src) : u32x4{};
     }
 #pragma unroll
     for (int i = 0; i < C::VU; ++i) {
+      // whole waves own V units, so this test is uniform
+      if ((C::VUNITS % C::NT != 0) && (wave * 64 + i * C::NT >= C::VUNITS)) continue;
       const int u = tid + i * C::NT;
       const int kg = u % (BC / 4);
       const int dc = u / (BC / 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = key0 + 4 * kg + r;
-        vreg[i][r] = key < kv_len
-                         ? *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + dc * 8)
-                         : u32x4{};
+        const __bf16* src = Vh + (size_t)key * D + dc * 8;
+        if (full)
+          vreg[i][r] = *reinterpret_cast<const u32x4*>(src);
+        else
+          vreg[i][r] = key < kv_len ? *reinterpret_cast<const u32x4*>(src) : u32x4{};
       }
     }
   };
 
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int kbuf, int vbuf) FA_INLINE {
 #pragma unroll
     for (int i = 0; i < C::KU; ++i) {
       const int u = tid + i * C::NT;
+      if ((C::KUNITS % C::NT != 0) && u >= C::KUNITS) continue;
       const int r = u / (D / 8);
       const int c8 = u % (D / 8);
-      *reinterpret_cast<u32x4*>(&Ks[buf][r * C::KPITCH + c8 * 8]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&Ks[kbuf][r * C::KPITCH + c8 * 8]) = kreg[i];
     }
 #pragma unroll
     for (int i = 0; i < C::VU; ++i) {
+      if ((C::VUNITS % C::NT != 0) && (wave * 64 + i * C::NT >= C::VUNITS)) continue;
       const int u = tid + i * C::NT;
       const int kg = u % (BC / 4);
       const int dc = u / (BC / 4);
@@ -165,109 +231,261 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       for (int j = 0; j < 8; ++j) {
         const int w = j >> 1;
         const int sh = (j & 1) * 16;
-        const uint32_t x0 = (vreg[i][0][w] >> sh) & 0xffffu;
-        const uint32_t x1 = (vreg[i][1][w] >> sh) & 0xffffu;
-        const uint32_t x2 = (vreg[i][2][w] >> sh) & 0xffffu;
-        const uint32_t x3 = (vreg[i][3][w] >> sh) & 0xffffu;
         u32x2 pk;
-        pk[0] = x0 | (x1 << 16);
-        pk[1] = x2 | (x3 << 16);
-        *reinterpret_cast<u32x2*>(&Vt[buf][(dc * 8 + j) * C::VPITCH + pos]) = pk;
+        pk[0] = ((vreg[i][0][w] >> sh) & 0xffffu) | (((vreg[i][1][w] >> sh) & 0xffffu) << 16);
+        pk[1] = ((vreg[i][2][w] >> sh) & 0xffffu) | (((vreg[i][3][w] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<u32x2*>(&Vt[vbuf][(dc * 8 + j) * C::VPITCH + pos]) = pk;
       }
     }
   };
 
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-  }
-
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
-
+#if FA_FWD_DIRECT
+  constexpr int kChunks = D / 8;                       // 16-byte chunks per row
+  constexpr int kRowsPerLoad = 64 / kChunks;           // rows one wave load covers
+  constexpr int kLoads = BC / kRowsPerLoad;            // wave loads per tile per tensor
+  static_assert(kLoads % NW == 0, "direct tile loads must split evenly over waves");
+  // issue this wave's share of tile kt into K buffer kbuf and V slot vbuf
+  auto load_direct = [&](int kt, int kbuf, int vbuf) FA_INLINE {
     const int key0 = kt * BC;
-    const bool wave_active = (qw0 < N) && (!causal || key0 <= qw0 + QB * 32 - 1);
-    if (wave_active) {
-      // ---- S^T = K Q^T for this tile
-      f32x16 sacc[C::NCB][QB];
+#pragma unroll
+    for (int i = 0; i < kLoads / NW; ++i) {
+      const int blk = wave + i * NW;
+      const int row = blk * kRowsPerLoad + lane / kChunks;
+      const int chunk = (lane % kChunks) ^ (row % kChunks);
+      // rows past the key length are masked out of S and carry P = 0; they are
+      // loaded from the last valid row so that V holds finite values
+      const int key = min(key0 + row, kv_len - 1);
+      const size_t goff = (size_t)key * D + chunk * 8;
+      __builtin_amdgcn_global_load_lds(Kh + goff, (__attribute__((address_space(3))) void*)&Ks[kbuf][blk * 512], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Vh + goff, (__attribute__((address_space(3))) void*)&Vt[vbuf][blk * 512], 16, 0, 0);
+    }
+  };
+  // byte offsets of this lane's reads inside a tile (the tile base is added later)
+  // K fragment (row c*32 + l32, chunk 2ks + hi); rows of different c share the swizzle
+  int koff[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = l32 * D * 2 + 16 * ((2 * ks + hi) ^ (l32 % kChunks));
+  // V^T fragment (g, db) = two transposed 8-byte reads r = 0, 1: lane l of group
+  // G = l/16 reads row 16g + 8r + 4(G/2) + (l%16)/4 at feature 32db + 16(G%2) + 4(l%4)
+  int voff[C::NDB][2];
+  {
+    const int G = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = 8 * r + 4 * (G >> 1) + (sl >> 2);
+        const int d = 32 * db + 16 * (G & 1) + 4 * (sl & 3);
+        voff[db][r] = row * D * 2 + 16 * ((d >> 3) ^ (row % kChunks)) + 2 * (d & 7);
+      }
+  }
+#endif
+
+  f32x16 sacc[C::NCB][QB];
+  bf16x8 pf[C::NG][QB];
+
+  // S^T(t) = K(t) Q^T.  The K fragments are read from LDS kPre reads ahead of
+  // the MFMA that consumes them, so LDS latency overlaps the MFMA pipeline.
+  constexpr int kPre = FA_FWD_PREFETCH;
+  auto stage_S = [&](int kbuf) FA_INLINE {
+    constexpr int NF = C::KS * C::NCB;   // fragments per tile, ordered (ks, c)
+#if FA_FWD_DIRECT
+    const char* kbase = reinterpret_cast<const char*>(&Ks[kbuf][0]);
+    auto kfrag = [&](int f) FA_INLINE {
+      const int ks = f / C::NCB, c = f % C::NCB;
+      return *reinterpret_cast<const bf16x8*>(kbase + koff[ks] + c * 32 * D * 2);
+    };
+#else
+    const __bf16* kbase = &Ks[kbuf][l32 * C::KPITCH + hi * 8];
+    auto kfrag = [&](int f) FA_INLINE {
+      const int ks = f / C::NCB, c = f % C::NCB;
+      return *reinterpret_cast<const bf16x8*>(kbase + c * 32 * C::KPITCH + ks * 16);
+    };
+#endif
+    bf16x8 ring[kPre];
+#pragma unroll
+    for (int f = 0; f < kPre && f < NF; ++f) ring[f] = kfrag(f);
+#pragma unroll
+    for (int c = 0; c < C::NCB; ++c)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[c][qb] = f32x16{};
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int ks = f / C::NCB, c = f % C::NCB;
+      const bf16x8 kf = ring[f % kPre];
+      if (f + kPre < NF) ring[f % kPre] = kfrag(f + kPre);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[c][qb] = mfma_bf16(kf, qf[qb][ks], sacc[c][qb]);
+    }
+#if FA_FWD_SCHED
+    // keep the fragment reads kPre ahead of the MFMAs that consume them
+    __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+    for (int f = 0; f < NF - kPre; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kPre * QB, 0);
+#endif
+  };
+
+  // O^T += V^T(t) P^T(t), V^T fragments prefetched the same way
+  auto stage_PV = [&](int vbuf) FA_INLINE {
+    constexpr int NF = C::NG * C::NDB;   // fragments per tile, ordered (g, db)
+#if FA_FWD_DIRECT
+    const char* vbase = reinterpret_cast<const char*>(&Vt[vbuf][0]);
+    auto vfrag = [&](int f) FA_INLINE {
+      const int g = f / C::NDB, db = f % C::NDB;
+      typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(vbase + voff[db][0] + g * 16 * D * 2));
+      const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(vbase + voff[db][1] + g * 16 * D * 2));
+      typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+      const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, ab);
+    };
+#else
+    const __bf16* vbase = &Vt[vbuf][l32 * C::VPITCH + hi * 8];
+    auto vfrag = [&](int f) FA_INLINE {
+      const int g = f / C::NDB, db = f % C::NDB;
+      return *reinterpret_cast<const bf16x8*>(vbase + db * 32 * C::VPITCH + g * 16);
+    };
+#endif
+    bf16x8 ring[kPre];
+#pragma unroll
+    for (int f = 0; f < kPre && f < NF; ++f) ring[f] = vfrag(f);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int g = f / C::NDB, db = f % C::NDB;
+      const bf16x8 vf = ring[f % kPre];
+      if (f + kPre < NF) ring[f % kPre] = vfrag(f + kPre);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma_bf16(vf, pf[g][qb], oacc[db][qb]);
+    }
+#if FA_FWD_SCHED >= 2
+    __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+    for (int f = 0; f < NF - kPre; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kPre * QB, 0);
+#endif
+  };
+
+  // mask (tiles crossing the key length or the wave's diagonal only), online
+  // softmax with lazy rescaling, P^T as bf16; rescales O when a maximum jumped
+  auto stage_softmax = [&](int kt) FA_INLINE {
+    const int key0 = kt * BC;
+    const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0);
+    if (need_mask) {
 #pragma unroll
       for (int c = 0; c < C::NCB; ++c)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[c][qb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-        for (int c = 0; c < C::NCB; ++c) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-              &Ks[buf][(c * 32 + l32) * C::KPITCH + ks * 16 + hi * 8]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) sacc[c][qb] = mfma_bf16(kf, qf[qb][ks], sacc[c][qb]);
-        }
-      }
-
-      // ---- mask (only tiles crossing the key length or this wave's diagonal)
-      const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0);
-      if (need_mask) {
-#pragma unroll
-        for (int c = 0; c < C::NCB; ++c)
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const int query = qw0 + qb * 32 + l32;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int key = key0 + c * 32 + c_row(v, lane);
-              const bool vis = key < kv_len && (!causal || key <= query);
-              if (!vis) sacc[c][qb][v] = kNegInf;
-            }
-          }
-      }
-
-      // ---- online softmax update (log2 domain)
-      bf16x8 pf[C::NG][QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int c = 0; c < C::NCB; ++c)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[c][qb][v]);
-        mx = halfwave_max(mx);
-        const float m_new = fmaxf(m[qb], mx * scale_log2);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m[qb] - m_use);
-        m[qb] = m_new;
-        float rs = 0.f;
-#pragma unroll
-        for (int c = 0; c < C::NCB; ++c)
+        for (int qb = 0; qb < QB; ++qb) {
+          const int query = qw0 + qb * 32 + l32;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const float p = fast_exp2(__builtin_fmaf(sacc[c][qb][v], scale_log2, -m_use));
-            rs += p;
-            pf[2 * c + (v >> 3)][qb][v & 7] = to_bf16(p);
+            const int key = key0 + c * 32 + c_row(v, lane);
+            const bool vis = key < kv_len && (!causal || key <= query);
+            if (!vis) sacc[c][qb][v] = kNegInf;
           }
-        l[qb] = l[qb] * alpha + rs;
+        }
+    }
+    bool scale_o = false;
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) oacc[db][qb] *= alpha;
-      }
-
-      // ---- O^T += V^T P^T
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int c = 0; c < C::NCB; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[c][qb][v]);
+      mx = halfwave_max(mx) * scale_log2;
+      const bool upd = mx > m[qb] + kRescaleThreshold;
+      const float m_new = upd ? mx : m[qb];
+      alpha[qb] = upd ? fast_exp2(m[qb] - m_new) : 1.f;
+      scale_o |= upd && (m[qb] != kNegInf);
+      m[qb] = m_new;
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      // the row sum accumulates the fp32 weights (the LSE the backward relies
+      // on stays exact to fp32 rounding); P^T is rounded to bf16 for the MFMA
+      float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
       for (int g = 0; g < C::NG; ++g) {
+        bf16x8 pk;
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-              &Vt[buf][(db * 32 + l32) * C::VPITCH + g * 16 + hi * 8]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma_bf16(vf, pf[g][qb], oacc[db][qb]);
+        for (int i = 0; i < 8; ++i) {
+          const float p =
+              fast_exp2(__builtin_fmaf(sacc[g >> 1][qb][8 * (g & 1) + i], scale_log2, -m_use));
+          if (i & 1) rs1 += p; else rs0 += p;
+          pk[i] = to_bf16(p);
         }
+        pf[g][qb] = pk;
       }
+      l[qb] = l[qb] * alpha[qb] + (rs0 + rs1);
     }
+    // the O accumulators move only when some lane's maximum jumped
+    if (__builtin_amdgcn_ballot_w64(scale_o) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) oacc[db][qb] *= alpha[qb];
+    }
+  };
 
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+#if FA_FWD_DIRECT
+  if (n_kt > 0) {
+    load_direct(0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
+#else
+  if (n_kt > 0) {
+    load_tile(0);
+    store_tile(0, 0);
+    __syncthreads();
+  }
+#endif
+
+  // one loop per group, so each is a plain straight-line schedule
+  auto run = [&](auto lag_tag) FA_INLINE {
+    constexpr bool kLag = decltype(lag_tag)::value;
+    for (int kt = 0; kt < n_kt; ++kt) {
+      const int kbuf = kt & 1;
+#if FA_FWD_DIRECT
+      // the slots tile kt+1 lands in were last read in iteration kt-1
+      if (kt + 1 < n_kt) load_direct(kt + 1, kbuf ^ 1, (kt + 1) % kVSlots);
+#else
+      if (kt + 1 < n_kt) load_tile(kt + 1);
+#endif
+      if (kLag) {
+        // second group: P(t-1) V(t-1), then S(t) and softmax(t)
+        if (kt >= 1 && kt - 1 < n_act) stage_PV((kt - 1) % kVSlots);
+        if (kt < n_act) {
+          stage_S(kbuf);
+          stage_softmax(kt);
+        }
+      } else if (kt < n_act) {
+        stage_S(kbuf);
+        stage_softmax(kt);
+        stage_PV(kt % kVSlots);
+      }
+#if FA_FWD_DIRECT
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#else
+      if (kt + 1 < n_kt) store_tile(kbuf ^ 1, (kt + 1) % kVSlots);
+#endif
+      __syncthreads();
+    }
+    // the second group's last P V
+    if (kLag && n_kt > 0 && n_kt - 1 < n_act) stage_PV((n_kt - 1) % kVSlots);
+  };
+  if (lagging)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // ---- epilogue: O = o / l (zeros for empty rows), LSE = (m + log2 l) ln 2
 #pragma unroll
@@ -354,7 +572,7 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   float m = kNegInf, l = 0.f;
 
   f32x4 kreg[C::KU], vreg[C::KU];
-  auto load_tile = [&](int kt) {
+  auto load_tile = [&](int kt) FA_INLINE {
     const int key0 = kt * BC;
 #pragma unroll
     for (int i = 0; i < C::KU; ++i) {
@@ -367,7 +585,7 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       vreg[i] = ok ? *reinterpret_cast<const f32x4*>(Vh + (size_t)key * D + c4 * 4) : f32x4{};
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf) FA_INLINE {
 #pragma unroll
     for (int i = 0; i < C::KU; ++i) {
       const int u = tid + i * C::NT;
@@ -470,17 +688,10 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   }
 }
 
-// Tile choices per head dimension.
-constexpr int kBf16QB = 2, kBf16NW = 4;
+constexpr int kBf16QB = FA_FWD_QB, kBf16NW = FA_FWD_NW;
 template <int D>
-struct Bf16Tile;
-template <>
-struct Bf16Tile<128> {
-  static constexpr int BC = 64;
-};
-template <>
-struct Bf16Tile<64> {
-  static constexpr int BC = 128;
+struct Bf16Tile {
+  static constexpr int BC = FA_FWD_BC;
 };
 constexpr int kF32NW = 2, kF32BC = 32;
 
