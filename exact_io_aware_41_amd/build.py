@@ -24,9 +24,8 @@ LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
-# per-source code-generation options: the backward kernels keep their MFMA
-# results in VGPRs rather than accumulation registers (fewer register copies)
-EXTRA_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# per-source code-generation options (none at present)
+EXTRA_FLAGS: dict[str, list[str]] = {}
 ARCH = "gfx950"
 
 

@@ -10,11 +10,11 @@
 //
 // Three launches on the caller's stream, no atomics (deterministic):
 //  1. row dot products D (memory-bound, one pass over O and dO);
-//  2. dK/dV: a work-group owns NW*32 keys of one (batch, head); each wave keeps
-//     its 32 keys' K and V rows in VGPRs (B operands) and its dK/dV
-//     accumulators resident, and loops over query tiles staged in LDS both
-//     row-major (A operands of S and dP) and transposed with a permuted query
-//     order (B operands of dV and dK).  S and dP come out with one key per
+//  2. dK/dV: a work-group owns 128 keys of one (batch, head); a pair of waves
+//     keeps 32 keys' K and V rows in VGPRs (B operands) and their dK/dV
+//     accumulators resident, and loops over 64-row query tiles staged in LDS
+//     both row-major (A operands of S and dP) and transposed with a permuted
+//     row order (B operands of dV and dK).  S and dP come out with one key per
 //     lane, so P and dS feed the next MFMA straight from registers;
 //  3. dQ: a work-group owns query rows (like the forward) and loops over key
 //     tiles; S^T and dP^T come out with one query per lane, so LSE_i and D_i
@@ -26,6 +26,14 @@
 
 #include "fa_common.hpp"
 #include "fa_internal.h"
+
+// Tile choices (compile-time).
+#ifndef FA_DQ_NW
+#define FA_DQ_NW 8
+#endif
+#ifndef FA_DQ_BC
+#define FA_DQ_BC 64
+#endif
 
 namespace fa {
 
@@ -39,6 +47,16 @@ constexpr int kPerm4[4] = {0, 2, 1, 3};
 // feeds into one 32x32x16 MFMA (rows 16u + 8*(i/4) + 4*hi + i%4 of a C tile)
 // are contiguous.
 __device__ __forceinline__ int perm_pos(int grp) { return 16 * (grp >> 2) + 4 * kPerm4[grp & 3]; }
+
+// Row-major tiles written by 4-row staging units are stored unpadded with
+// their 16-byte chunks XOR-swizzled by this function of the row: 16
+// consecutive lanes writing rows 4q + r (q = 0..15) and 16 lanes reading
+// rows r..r+15 both land on distinct chunks, so neither access has LDS bank
+// conflicts.
+template <int D>
+__device__ __forceinline__ int row_swizzle(int row) {
+  return (row ^ (row >> 2)) & (D / 8 - 1);
+}
 
 // Write 4 rows x 8 features (four 16-byte row chunks) transposed into a
 // [feature][row] LDS array at column `pos`.
@@ -82,247 +100,7 @@ void fa_bwd_rowdot_kernel(const __bf16* __restrict__ O, const __bf16* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK / dV
-// ---------------------------------------------------------------------------
-template <int D, int NW, int BQ>
-struct DkdvCfg {
-  static constexpr int BK = NW * 32;       // keys per work-group
-  static constexpr int NT = NW * 64;
-  static constexpr int KS = D / 16;
-  static constexpr int NQB = BQ / 32;      // 32-query blocks per tile
-  static constexpr int NG = BQ / 16;       // 16-query groups per tile
-  static constexpr int NDB = D / 32;
-  static constexpr int RPITCH = D + 8;     // row-major copies (bf16 per row)
-  static constexpr int TPITCH = BQ + 8;    // transposed copies (bf16 per feature row)
-  static constexpr int UNITS = (BQ / 4) * (D / 8);
-  static constexpr int UPT = (UNITS + NT - 1) / NT;
-};
-
-template <int D, int NW, int BQ>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1)))
-void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                        const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                        const float* __restrict__ LSE, const float* __restrict__ Dlt,
-                        const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
-                        int causal, __bf16* __restrict__ dK, __bf16* __restrict__ dV, int B,
-                        int H, int N, int n_ktiles) {
-  using C = DkdvCfg<D, NW, BQ>;
-  __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * C::RPITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 dOs[2][BQ * C::RPITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 Qt[2][D * C::TPITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 dOt[2][D * C::TPITCH];
-  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-
-  // key tiles in increasing order: under a causal mask the first key tiles see
-  // the most query rows, so the longest work-groups are issued first
-  const int bh_count = B * H;
-  const int kt = blockIdx.x / bh_count;
-  const int bh = blockIdx.x - kt * bh_count;
-  const int b = bh / H;
-  const int h = bh - b * H;
-  const size_t head = (size_t)b * H + h;
-  const __bf16* Qh = Q + head * (size_t)N * D;
-  const __bf16* Kh = K + head * (size_t)N * D;
-  const __bf16* Vh = V + head * (size_t)N * D;
-  const __bf16* dOh = dO + head * (size_t)N * D;
-  const float* Lh = LSE + head * (size_t)N;
-  const float* Dh = Dlt + head * (size_t)N;
-  __bf16* dKh = dK + head * (size_t)N * D;
-  __bf16* dVh = dV + head * (size_t)N * D;
-
-  const int kv_len = key_length(seqlens_k, b, N);
-  const int k0 = kt * C::BK;
-  const int kw0 = k0 + wave * 32;
-  const int my_key = kw0 + l32;
-
-  // query tiles: all rows, or (causal) rows from the first key of this group
-  const int q_begin = (causal ? (k0 / BQ) * BQ : 0);
-  const int n_qt = (k0 < kv_len) ? (N - q_begin + BQ - 1) / BQ : 0;
-
-  // this wave's K and V rows (B operands of S = Q K^T and dP = dO V^T)
-  bf16x8 kf[C::KS], vf[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    if (my_key < N) {
-      kf[ks] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)my_key * D + ks * 16 + hi * 8);
-      vf[ks] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)my_key * D + ks * 16 + hi * 8);
-    } else {
-      kf[ks] = bf16x8{};
-      vf[ks] = bf16x8{};
-    }
-  }
-
-  f32x16 dkacc[C::NDB], dvacc[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-    dkacc[db] = f32x16{};
-    dvacc[db] = f32x16{};
-  }
-
-  // staging: with at least two threads per unit, half the threads stage Q and
-  // half stage dO; otherwise every thread stages both
-  constexpr bool kSplit = C::NT >= 2 * C::UNITS;
-  constexpr int kRegsets = kSplit ? 1 : 2;
-  constexpr int kUpt = kSplit ? 1 : C::UPT;
-  u32x4 sreg[kRegsets][kUpt][4];
-  float lreg = 0.f, dreg = 0.f;
-
-  auto load_tile = [&](int qi) FA_INLINE {
-    const int qt0 = q_begin + qi * BQ;
-#pragma unroll
-    for (int set = 0; set < kRegsets; ++set)
-#pragma unroll
-      for (int i = 0; i < kUpt; ++i) {
-        const int u = kSplit ? tid % C::UNITS : tid + i * C::NT;
-        const bool is_q = kSplit ? (tid < C::UNITS) : (set == 0);
-        const __bf16* src = is_q ? Qh : dOh;
-        const int qg = u % (BQ / 4);
-        const int dc = u / (BQ / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = qt0 + 4 * qg + r;
-          const bool ok = (kSplit ? tid < 2 * C::UNITS : u < C::UNITS) && row < N;
-          sreg[set][i][r] = ok ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + dc * 8)
-                               : u32x4{};
-        }
-      }
-    if (tid < BQ) {
-      const int row = qt0 + tid;
-      // rows past N, and rows that see no key, get +inf so that P = 0
-      float lse = row < N ? Lh[row] : __builtin_huge_valf();
-      lreg = (lse == kNegInf) ? __builtin_huge_valf() : lse * kLog2e;
-      dreg = row < N ? Dh[row] : 0.f;
-    }
-  };
-  auto store_tile = [&](int buf) FA_INLINE {
-#pragma unroll
-    for (int set = 0; set < kRegsets; ++set)
-#pragma unroll
-      for (int i = 0; i < kUpt; ++i) {
-        const int u = kSplit ? tid % C::UNITS : tid + i * C::NT;
-        const bool active = kSplit ? tid < 2 * C::UNITS : u < C::UNITS;
-        if (!active) continue;
-        const bool is_q = kSplit ? (tid < C::UNITS) : (set == 0);
-        __bf16* rm = is_q ? Qs[buf] : dOs[buf];
-        __bf16* tr = is_q ? Qt[buf] : dOt[buf];
-        const int qg = u % (BQ / 4);
-        const int dc = u / (BQ / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          *reinterpret_cast<u32x4*>(&rm[(4 * qg + r) * C::RPITCH + dc * 8]) = sreg[set][i][r];
-        store_transposed(tr, C::TPITCH, dc * 8, perm_pos(qg), sreg[set][i]);
-      }
-    if (tid < BQ) {
-      Ls[buf][tid] = lreg;
-      Ds[buf][tid] = dreg;
-    }
-  };
-
-  if (n_qt > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-  }
-
-  const bool wave_keys_valid = kw0 < kv_len;
-  for (int qi = 0; qi < n_qt; ++qi) {
-    const int buf = qi & 1;
-    if (qi + 1 < n_qt) load_tile(qi + 1);
-    const int qt0 = q_begin + qi * BQ;
-    const bool wave_active = wave_keys_valid && (!causal || qt0 + BQ - 1 >= kw0);
-    if (wave_active) {
-      // ---- S = Q K^T and dP = dO V^T (C: one key per lane, rows = queries)
-      f32x16 sacc[C::NQB], pacc[C::NQB];
-#pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) {
-        sacc[qb] = f32x16{};
-        pacc[qb] = f32x16{};
-      }
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(
-              &Qs[buf][(qb * 32 + l32) * C::RPITCH + ks * 16 + hi * 8]);
-          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(
-              &dOs[buf][(qb * 32 + l32) * C::RPITCH + ks * 16 + hi * 8]);
-          sacc[qb] = mfma_bf16(qa, kf[ks], sacc[qb]);
-          pacc[qb] = mfma_bf16(oa, vf[ks], pacc[qb]);
-        }
-
-      // ---- P = exp2(s*scale*log2e - LSE*log2e); dS = P (dP - D); the mask is
-      // applied only on tiles that cross the diagonal or the key length
-      bf16x8 pa[C::NG], dsa[C::NG];
-      auto p_and_ds = [&](auto masked_tag) FA_INLINE {
-        constexpr bool kMasked = decltype(masked_tag)::value;
-#pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) {
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const int r0 = qb * 32 + 8 * a4 + 4 * hi;
-            const f32x4 lq = *reinterpret_cast<const f32x4*>(&Ls[buf][r0]);
-            const f32x4 dq = *reinterpret_cast<const f32x4*>(&Ds[buf][r0]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int v = 4 * a4 + e;
-              float p = fast_exp2(__builtin_fmaf(sacc[qb][v], scale_log2, -lq[e]));
-              if (kMasked) {
-                const int query = qt0 + r0 + e;
-                const bool vis = my_key < kv_len && (!causal || my_key <= query);
-                p = vis ? p : 0.f;
-              }
-              const float ds = p * (pacc[qb][v] - dq[e]);
-              pa[2 * qb + (v >> 3)][v & 7] = to_bf16(p);
-              dsa[2 * qb + (v >> 3)][v & 7] = to_bf16(ds);
-            }
-          }
-        }
-      };
-      if ((kw0 + 31 >= kv_len) || (causal && qt0 < kw0 + 31))
-        p_and_ds(std::true_type{});
-      else
-        p_and_ds(std::false_type{});
-
-      // ---- dV += P^T dO ; dK += dS^T Q   (B operands from the transposed copies)
-#pragma unroll
-      for (int g = 0; g < C::NG; ++g)
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          const bf16x8 ob = *reinterpret_cast<const bf16x8*>(
-              &dOt[buf][(db * 32 + l32) * C::TPITCH + g * 16 + hi * 8]);
-          const bf16x8 qbv = *reinterpret_cast<const bf16x8*>(
-              &Qt[buf][(db * 32 + l32) * C::TPITCH + g * 16 + hi * 8]);
-          dvacc[db] = mfma_bf16(pa[g], ob, dvacc[db]);
-          dkacc[db] = mfma_bf16(dsa[g], qbv, dkacc[db]);
-        }
-    }
-    if (qi + 1 < n_qt) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- write dK = scale * acc, dV = acc  (C: lane = feature, rows = keys)
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = kw0 + c_row(v, lane);
-      if (key < N) {
-        dKh[(size_t)key * D + db * 32 + l32] = to_bf16(dkacc[db][v] * scale);
-        dVh[(size_t)key * D + db * 32 + l32] = to_bf16(dvacc[db][v]);
-      }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// 2b. dK / dV with paired waves (two waves per SIMD)
+// 2. dK / dV with paired waves (two waves per SIMD)
 //
 // Eight waves; waves w and w+4 (a pair, same SIMD) share 32 keys of the
 // work-group's 128.  For each 64-query tile, wave w computes S and dP for
@@ -342,7 +120,6 @@ struct DkdvPairCfg {
   static constexpr int NG = BQ / 16;       // 16-query groups per tile
   static constexpr int NDB = D / 32;
   static constexpr int HDB = NDB / 2;      // 32-feature blocks per wave (its half)
-  static constexpr int RPITCH = D + 8;
   static constexpr int TPITCH = BQ + 8;
   static constexpr int UNITS = (BQ / 4) * (D / 8);  // 4-row x 8-feature units per tensor
   static_assert(BQ == 64, "two 32-row halves per tile");
@@ -360,8 +137,8 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
                              float scale_log2, int causal, __bf16* __restrict__ dK,
                              __bf16* __restrict__ dV, int B, int H, int N, int n_ktiles) {
   using C = DkdvPairCfg<D, BQ>;
-  __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * C::RPITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 dOs[2][BQ * C::RPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 dOs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) __bf16 Qt[D * C::TPITCH];
   __shared__ __attribute__((aligned(16))) __bf16 dOt[D * C::TPITCH];
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
@@ -449,8 +226,10 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
     if (stager) {
       __bf16* rm = stage_q ? Qs[buf] : dOs[buf];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<u32x4*>(&rm[(4 * sqg + r) * C::RPITCH + sdc * 8]) = sreg[r];
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * sqg + r;
+        *reinterpret_cast<u32x4*>(&rm[row * D + (sdc ^ row_swizzle<D>(row)) * 8]) = sreg[r];
+      }
     }
     if (tid < BQ) {
       Ls[buf][tid] = lreg;
@@ -480,9 +259,11 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
     if (pair_active) {
       // ---- phase 1: S and dP for this wave's 32 query rows (one key per lane)
       f32x16 sacc = f32x16{}, pacc = f32x16{};
+      const int arow = 32 * half + l32;
+      const int asw = row_swizzle<D>(arow);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const int ro = (32 * half + l32) * C::RPITCH + ks * 16 + hi * 8;
+        const int ro = arow * D + ((2 * ks + hi) ^ asw) * 8;
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[buf][ro]);
         const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&dOs[buf][ro]);
         sacc = mfma_bf16(qa, kf[ks], sacc);
@@ -576,7 +357,6 @@ struct DqCfg {
   static constexpr int NCB = BC / 32;
   static constexpr int NG = BC / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int RPITCH = D + 8;
   static constexpr int TPITCH = BC + 8;
   static constexpr int UNITS = (BC / 4) * (D / 8);
   static constexpr int UPT = (UNITS + NT - 1) / NT;
@@ -591,8 +371,8 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                       const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
                       int causal, __bf16* __restrict__ dQ, int B, int H, int N, int n_qtiles) {
   using C = DqCfg<D, NW, BC>;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * C::RPITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BC * C::RPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BC * D];
   __shared__ __attribute__((aligned(16))) __bf16 Kt[2][D * C::TPITCH];
 
   const int tid = threadIdx.x;
@@ -678,8 +458,11 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         const int kg = u % (BC / 4);
         const int dc = u / (BC / 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          *reinterpret_cast<u32x4*>(&rm[(4 * kg + r) * C::RPITCH + dc * 8]) = sreg[set][i][r];
+        for (int r = 0; r < 4; ++r) {
+          const int row = 4 * kg + r;
+          *reinterpret_cast<u32x4*>(&rm[row * D + (dc ^ row_swizzle<D>(row)) * 8]) =
+              sreg[set][i][r];
+        }
         if (is_k) store_transposed(Kt[buf], C::TPITCH, dc * 8, perm_pos(kg), sreg[set][i]);
       }
   };
@@ -707,10 +490,10 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
         for (int c = 0; c < C::NCB; ++c) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-              &Ks[buf][(c * 32 + l32) * C::RPITCH + ks * 16 + hi * 8]);
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-              &Vs[buf][(c * 32 + l32) * C::RPITCH + ks * 16 + hi * 8]);
+          const int arow = c * 32 + l32;
+          const int ro = arow * D + ((2 * ks + hi) ^ row_swizzle<D>(arow)) * 8;
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][ro]);
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[buf][ro]);
           sacc[c] = mfma_bf16(ka, qf[ks], sacc[c]);
           pacc[c] = mfma_bf16(va, of[ks], pacc[c]);
         }
@@ -756,23 +539,6 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   }
 }
 
-// Tile choices (compile-time).
-#ifndef FA_DKDV_NW
-#define FA_DKDV_NW 4
-#endif
-#ifndef FA_DKDV_BQ
-#define FA_DKDV_BQ 64
-#endif
-#ifndef FA_DQ_NW
-#define FA_DQ_NW 8
-#endif
-#ifndef FA_DKDV_PAIR
-#define FA_DKDV_PAIR 0
-#endif
-#ifndef FA_DQ_BC
-#define FA_DQ_BC 64
-#endif
-constexpr int kDkdvNW = FA_DKDV_NW, kDkdvBQ = FA_DKDV_BQ;
 constexpr int kDqNW = FA_DQ_NW, kDqBC = FA_DQ_BC;
 
 template <int D>
@@ -787,7 +553,6 @@ hipError_t launch_preprocess_d(const BwdArgs& a) {
 
 template <int D>
 hipError_t launch_dkdv_d(const BwdArgs& a) {
-#if FA_DKDV_PAIR
   using CK = DkdvPairCfg<D, 64>;
   const int n_ktiles = (a.N + CK::BK - 1) / CK::BK;
   hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<D, 64>),
@@ -797,17 +562,6 @@ hipError_t launch_dkdv_d(const BwdArgs& a) {
                      a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
                      static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.B, a.H, a.N,
                      n_ktiles);
-#else
-  using CK = DkdvCfg<D, kDkdvNW, kDkdvBQ>;
-  const int n_ktiles = (a.N + CK::BK - 1) / CK::BK;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, kDkdvNW, kDkdvBQ>),
-                     dim3((unsigned)((long long)n_ktiles * a.B * a.H)), dim3(CK::NT), 0, a.stream,
-                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dout), a.lse,
-                     a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
-                     static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.B, a.H, a.N,
-                     n_ktiles);
-#endif
   return hipGetLastError();
 }
 
@@ -828,7 +582,7 @@ hipError_t launch_dq_d(const BwdArgs& a) {
 
 long long bwd_bf16_grid(int B, int H, int N, int d) {
   (void)d;
-  const long long kt = (N + kDkdvNW * 32 - 1) / (kDkdvNW * 32);
+  const long long kt = (N + 127) / 128;
   const long long qt = (N + kDqNW * 32 - 1) / (kDqNW * 32);
   const long long rows_wg = ((long long)B * H * N * 16 + 255) / 256;
   long long m = kt * B * H;

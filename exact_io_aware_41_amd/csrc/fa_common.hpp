@@ -33,10 +33,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
-// s_waitcnt immediate that waits for every outstanding vector-memory access
-// (vmcnt = 0) and leaves the other counters unconstrained.
-constexpr int kWaitVmcnt0 = 0x0F70;
-
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();

@@ -11,17 +11,23 @@
 // chip and writes O and one LSE per row once.
 //
 // gfx950 mapping (bf16 kernel):
-//  * a work-group of NW waves owns BR = NW*QB*32 consecutive query rows of one
-//    (batch, head); each wave owns QB blocks of 32 queries, one query per lane
-//    (lanes l and l^32 share a query).
+//  * a work-group of 8 waves owns 256 consecutive query rows of one (batch,
+//    head); each wave owns 32 queries, one query per lane (lanes l and l^32
+//    share a query).  A wave fits in 256 VGPRs, so two waves share a SIMD.
 //  * Q stays in VGPRs as the B operand of S^T = K Q^T (32x32x16 bf16 MFMA).
-//  * K and V tiles of BC keys are loaded from HBM with 16-byte coalesced loads
-//    into registers one tile ahead, then written to a double-buffered LDS
-//    ring: K row-major (padded rows), V transposed to [d][key] with the key
-//    order permuted inside each 16-key group so that every MFMA A fragment is
-//    one 16-byte LDS read.
+//  * K and V tiles of 64 keys are loaded from HBM with 16-byte coalesced loads
+//    into registers one tile ahead and written to LDS: K row-major (padded
+//    rows) in a two-slot ring, V transposed to [d][key] in a three-slot ring,
+//    with the key order permuted inside each 16-key group so that every MFMA
+//    A fragment is one 16-byte LDS read.  Fragments are read several MFMAs
+//    ahead of use.
+//  * the waves of a SIMD run out of phase: waves 4..7 multiply P(t-1) V(t-1)
+//    before computing S(t), while waves 0..3 compute S(t) first, so one
+//    wave's MFMAs overlap the other's softmax.
 //  * scores are handled in the log2 domain: x = s * scale * log2(e), so the
-//    exponentials are single v_exp_f32 instructions.
+//    exponentials are single v_exp_f32 instructions.  The reference maximum
+//    only moves when a tile's maximum exceeds it by more than 2^8, so the O
+//    accumulators are rescaled rarely (the result is the same function).
 //  * P^T leaves the S^T accumulators as bf16 (round to nearest even) and is
 //    the B operand of O^T = V^T P^T, whose accumulators hold one query per
 //    lane, so the rescale by alpha is lane-local.
@@ -54,9 +60,6 @@
 #endif
 #ifndef FA_FWD_SCHED
 #define FA_FWD_SCHED 2
-#endif
-#ifndef FA_FWD_DIRECT
-#define FA_FWD_DIRECT 0
 #endif
 
 
@@ -105,16 +108,8 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   // three-slot ring (group 2 still reads V(t-1) while V(t+1) is written).
   constexpr bool kPingPong = (NW >= 8);
   constexpr int kVSlots = kPingPong ? 3 : 2;
-#if FA_FWD_DIRECT
-  // K and V tiles arrive straight from HBM (one 16-byte chunk per lane per
-  // load) as unpadded rows whose 16-byte chunks are XOR-swizzled by row, so
-  // both the row reads of K and the transposed reads of V are conflict-free.
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[kVSlots][BC * D];
-#else
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * C::KPITCH];
   __shared__ __attribute__((aligned(16))) __bf16 Vt[kVSlots][D * C::VPITCH];
-#endif
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -239,47 +234,6 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     }
   };
 
-#if FA_FWD_DIRECT
-  constexpr int kChunks = D / 8;                       // 16-byte chunks per row
-  constexpr int kRowsPerLoad = 64 / kChunks;           // rows one wave load covers
-  constexpr int kLoads = BC / kRowsPerLoad;            // wave loads per tile per tensor
-  static_assert(kLoads % NW == 0, "direct tile loads must split evenly over waves");
-  // issue this wave's share of tile kt into K buffer kbuf and V slot vbuf
-  auto load_direct = [&](int kt, int kbuf, int vbuf) FA_INLINE {
-    const int key0 = kt * BC;
-#pragma unroll
-    for (int i = 0; i < kLoads / NW; ++i) {
-      const int blk = wave + i * NW;
-      const int row = blk * kRowsPerLoad + lane / kChunks;
-      const int chunk = (lane % kChunks) ^ (row % kChunks);
-      // rows past the key length are masked out of S and carry P = 0; they are
-      // loaded from the last valid row so that V holds finite values
-      const int key = min(key0 + row, kv_len - 1);
-      const size_t goff = (size_t)key * D + chunk * 8;
-      __builtin_amdgcn_global_load_lds(Kh + goff, (__attribute__((address_space(3))) void*)&Ks[kbuf][blk * 512], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Vh + goff, (__attribute__((address_space(3))) void*)&Vt[vbuf][blk * 512], 16, 0, 0);
-    }
-  };
-  // byte offsets of this lane's reads inside a tile (the tile base is added later)
-  // K fragment (row c*32 + l32, chunk 2ks + hi); rows of different c share the swizzle
-  int koff[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = l32 * D * 2 + 16 * ((2 * ks + hi) ^ (l32 % kChunks));
-  // V^T fragment (g, db) = two transposed 8-byte reads r = 0, 1: lane l of group
-  // G = l/16 reads row 16g + 8r + 4(G/2) + (l%16)/4 at feature 32db + 16(G%2) + 4(l%4)
-  int voff[C::NDB][2];
-  {
-    const int G = lane >> 4, sl = lane & 15;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int row = 8 * r + 4 * (G >> 1) + (sl >> 2);
-        const int d = 32 * db + 16 * (G & 1) + 4 * (sl & 3);
-        voff[db][r] = row * D * 2 + 16 * ((d >> 3) ^ (row % kChunks)) + 2 * (d & 7);
-      }
-  }
-#endif
 
   f32x16 sacc[C::NCB][QB];
   bf16x8 pf[C::NG][QB];
@@ -289,19 +243,11 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   constexpr int kPre = FA_FWD_PREFETCH;
   auto stage_S = [&](int kbuf) FA_INLINE {
     constexpr int NF = C::KS * C::NCB;   // fragments per tile, ordered (ks, c)
-#if FA_FWD_DIRECT
-    const char* kbase = reinterpret_cast<const char*>(&Ks[kbuf][0]);
-    auto kfrag = [&](int f) FA_INLINE {
-      const int ks = f / C::NCB, c = f % C::NCB;
-      return *reinterpret_cast<const bf16x8*>(kbase + koff[ks] + c * 32 * D * 2);
-    };
-#else
     const __bf16* kbase = &Ks[kbuf][l32 * C::KPITCH + hi * 8];
     auto kfrag = [&](int f) FA_INLINE {
       const int ks = f / C::NCB, c = f % C::NCB;
       return *reinterpret_cast<const bf16x8*>(kbase + c * 32 * C::KPITCH + ks * 16);
     };
-#endif
     bf16x8 ring[kPre];
 #pragma unroll
     for (int f = 0; f < kPre && f < NF; ++f) ring[f] = kfrag(f);
@@ -332,27 +278,11 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   // O^T += V^T(t) P^T(t), V^T fragments prefetched the same way
   auto stage_PV = [&](int vbuf) FA_INLINE {
     constexpr int NF = C::NG * C::NDB;   // fragments per tile, ordered (g, db)
-#if FA_FWD_DIRECT
-    const char* vbase = reinterpret_cast<const char*>(&Vt[vbuf][0]);
-    auto vfrag = [&](int f) FA_INLINE {
-      const int g = f / C::NDB, db = f % C::NDB;
-      typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-      const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(vbase + voff[db][0] + g * 16 * D * 2));
-      const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(vbase + voff[db][1] + g * 16 * D * 2));
-      typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
-      const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-      return __builtin_bit_cast(bf16x8, ab);
-    };
-#else
     const __bf16* vbase = &Vt[vbuf][l32 * C::VPITCH + hi * 8];
     auto vfrag = [&](int f) FA_INLINE {
       const int g = f / C::NDB, db = f % C::NDB;
       return *reinterpret_cast<const bf16x8*>(vbase + db * 32 * C::VPITCH + g * 16);
     };
-#endif
     bf16x8 ring[kPre];
 #pragma unroll
     for (int f = 0; f < kPre && f < NF; ++f) ring[f] = vfrag(f);
@@ -435,31 +365,18 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     }
   };
 
-#if FA_FWD_DIRECT
-  if (n_kt > 0) {
-    load_direct(0, 0, 0);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-  }
-#else
   if (n_kt > 0) {
     load_tile(0);
     store_tile(0, 0);
     __syncthreads();
   }
-#endif
 
   // one loop per group, so each is a plain straight-line schedule
   auto run = [&](auto lag_tag) FA_INLINE {
     constexpr bool kLag = decltype(lag_tag)::value;
     for (int kt = 0; kt < n_kt; ++kt) {
       const int kbuf = kt & 1;
-#if FA_FWD_DIRECT
-      // the slots tile kt+1 lands in were last read in iteration kt-1
-      if (kt + 1 < n_kt) load_direct(kt + 1, kbuf ^ 1, (kt + 1) % kVSlots);
-#else
       if (kt + 1 < n_kt) load_tile(kt + 1);
-#endif
       if (kLag) {
         // second group: P(t-1) V(t-1), then S(t) and softmax(t)
         if (kt >= 1 && kt - 1 < n_act) stage_PV((kt - 1) % kVSlots);
@@ -472,11 +389,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         stage_softmax(kt);
         stage_PV(kt % kVSlots);
       }
-#if FA_FWD_DIRECT
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-#else
       if (kt + 1 < n_kt) store_tile(kbuf ^ 1, (kt + 1) % kVSlots);
-#endif
       __syncthreads();
     }
     // the second group's last P V
