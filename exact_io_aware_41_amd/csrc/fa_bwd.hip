@@ -39,14 +39,15 @@ namespace fa {
 
 namespace {
 
-constexpr int kPerm4[4] = {0, 2, 1, 3};
-
 // Position of element (4*grp + r) of a 4-element group inside the permuted
 // order used for transposed LDS copies: within each 16-element group the
 // middle two 4-element chunks are swapped, so that the 8 elements a lane
 // feeds into one 32x32x16 MFMA (rows 16u + 8*(i/4) + 4*hi + i%4 of a C tile)
 // are contiguous.
-__device__ __forceinline__ int perm_pos(int grp) { return 16 * (grp >> 2) + 4 * kPerm4[grp & 3]; }
+// (The chunk swap exchanges the two low bits of the group index.)
+__device__ __forceinline__ int perm_pos(int grp) {
+  return 16 * (grp >> 2) + 4 * (((grp & 1) << 1) | ((grp >> 1) & 1));
+}
 
 // Row-major tiles written by 4-row staging units are stored unpadded with
 // their 16-byte chunks XOR-swizzled by this function of the row: 16
@@ -195,55 +196,79 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
     dvacc[j] = f32x16{};
   }
 
-  // staging: threads [0, UNITS) stage Q, [UNITS, 2 UNITS) stage dO
-  u32x4 sreg[4];
+  // Staging.  The row-major Q and dO tiles are copied straight from global
+  // memory into LDS (buffer loads with an LDS destination: lane l of a wave
+  // fills bytes [16 l, 16 l + 16) of a 1 KiB block), issued one tile ahead so
+  // that the copy has a whole iteration to land.  The buffer descriptors
+  // cover exactly one head, so rows at or past N read as zeros.  Each lane
+  // fetches the global 16-byte chunk that the XOR swizzle places at its LDS
+  // position.  The transposed copies are then built from the row-major ones.
+  constexpr int kRowsPerBlk = 1024 / (D * 2);
+  constexpr int kBlksPerTensor = BQ / kRowsPerBlk;
+  constexpr int kBlksPerWave = 2 * kBlksPerTensor / C::NW;
+  static_assert(2 * kBlksPerTensor % C::NW == 0, "whole 1 KiB blocks per wave");
+  const int head_bytes = N * D * 2;
+  const __amdgpu_buffer_rsrc_t q_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Qh), 0, head_bytes, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t o_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(dOh), 0, head_bytes, kBufferRsrcWord3);
+  const int blk_row = lane / (D / 8);
+  const int blk_cpos = lane % (D / 8);
   float lreg = 0.f, dreg = 0.f;
+  auto issue_tile = [&](int qi, int buf) FA_INLINE {
+    const int qt0 = q_begin + qi * BQ;
+    // statistics first: vector-memory counters retire in order, so waiting
+    // for them later does not wait for the tile copy issued after them
+    if (tid < BQ) {
+      const int row = qt0 + tid;
+      lreg = row < N ? Lh[row] : __builtin_huge_valf();
+      dreg = row < N ? Dh[row] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kBlksPerWave; ++j) {
+      const int blk = wave * kBlksPerWave + j;
+      const bool is_q = blk < kBlksPerTensor;
+      const int rb = is_q ? blk : blk - kBlksPerTensor;
+      const int row = rb * kRowsPerBlk + blk_row;
+      const int chunk = blk_cpos ^ row_swizzle<D>(row);
+      const int voff = (qt0 + row) * (D * 2) + chunk * 16;
+      __bf16* dst = (is_q ? Qs[buf] : dOs[buf]) + rb * kRowsPerBlk * D;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_q ? q_rsrc : o_rsrc, dst, 16, voff, 0, 0, 0);
+    }
+  };
+  auto store_stats = [&](int buf) FA_INLINE {
+    if (tid < BQ) {
+      // rows past N, and rows that see no key, get +inf so that P = 0
+      Ls[buf][tid] = (lreg == kNegInf) ? __builtin_huge_valf() : lreg * kLog2e;
+      Ds[buf][tid] = dreg;
+    }
+  };
+  // transposed copies of the row-major tile in `buf`: threads [0, UNITS)
+  // handle Q, [UNITS, 2 UNITS) dO, one 4-row x 8-feature unit each
   const bool stager = tid < 2 * C::UNITS;
   const bool stage_q = tid < C::UNITS;
   const int su = tid % C::UNITS;
   const int sqg = su % (BQ / 4);
   const int sdc = su / (BQ / 4);
-  auto load_tile = [&](int qi) FA_INLINE {
-    const int qt0 = q_begin + qi * BQ;
+  auto transpose_tile = [&](int buf) FA_INLINE {
     if (stager) {
-      const __bf16* src = stage_q ? Qh : dOh;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = qt0 + 4 * sqg + r;
-        sreg[r] = row < N ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + sdc * 8)
-                          : u32x4{};
-      }
-    }
-    if (tid < BQ) {
-      const int row = qt0 + tid;
-      // rows past N, and rows that see no key, get +inf so that P = 0
-      const float lse = row < N ? Lh[row] : __builtin_huge_valf();
-      lreg = (lse == kNegInf) ? __builtin_huge_valf() : lse * kLog2e;
-      dreg = row < N ? Dh[row] : 0.f;
-    }
-  };
-  auto store_rowmajor = [&](int buf) FA_INLINE {
-    if (stager) {
-      __bf16* rm = stage_q ? Qs[buf] : dOs[buf];
+      const __bf16* rm = stage_q ? Qs[buf] : dOs[buf];
+      u32x4 rows[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * sqg + r;
-        *reinterpret_cast<u32x4*>(&rm[row * D + (sdc ^ row_swizzle<D>(row)) * 8]) = sreg[r];
+        rows[r] = *reinterpret_cast<const u32x4*>(&rm[row * D + (sdc ^ row_swizzle<D>(row)) * 8]);
       }
+      store_transposed(stage_q ? Qt : dOt, C::TPITCH, sdc * 8, perm_pos(sqg), rows);
     }
-    if (tid < BQ) {
-      Ls[buf][tid] = lreg;
-      Ds[buf][tid] = dreg;
-    }
-  };
-  auto store_transposed_copy = [&]() FA_INLINE {
-    if (stager) store_transposed(stage_q ? Qt : dOt, C::TPITCH, sdc * 8, perm_pos(sqg), sreg);
   };
 
   if (n_qt > 0) {
-    load_tile(0);
-    store_rowmajor(0);
-    store_transposed_copy();
+    issue_tile(0, 0);
+    store_stats(0);
+    wait_vmem();
+    __syncthreads();
+    transpose_tile(0);
     __syncthreads();
   }
 
@@ -252,7 +277,7 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
     const int buf = qi & 1;
     const int qt0 = q_begin + qi * BQ;
     const bool more = qi + 1 < n_qt;
-    if (more) load_tile(qi + 1);
+    if (more) issue_tile(qi + 1, buf ^ 1);
     const bool pair_active = pair_keys_valid && (!causal || qt0 + BQ - 1 >= kw0);
 
     bf16x8 pa[2], dsa[2];
@@ -299,9 +324,8 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
       Xs[wave][2][lane] = dsa[0];
       Xs[wave][3][lane] = dsa[1];
     }
-    __syncthreads();
-    // the next tile's row-major copies go to the other buffer while phase 2 runs
-    if (more) store_rowmajor(buf ^ 1);
+    lds_barrier();
+    if (more) store_stats(buf ^ 1);
     if (pair_active) {
       // ---- phase 2: dV += P^T dO, dK += dS^T Q over all 64 rows, own feature half
       const int partner = wave ^ 4;
@@ -327,8 +351,10 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
         }
       }
     }
-    __syncthreads();
-    if (more) store_transposed_copy();
+    // the next tile's row-major copy has landed once every wave passes here
+    wait_vmem();
+    lds_barrier();
+    if (more) transpose_tile(buf ^ 1);
   }
 
   // ---- write dK = scale * acc, dV = acc for this wave's feature half
@@ -371,8 +397,10 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                       const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
                       int causal, __bf16* __restrict__ dQ, int B, int H, int N, int n_qtiles) {
   using C = DqCfg<D, NW, BC>;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BC * D];
+  // row-major K and V tiles in three slots (read, being transposed, being
+  // loaded), transposed K in two
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[3][BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[3][BC * D];
   __shared__ __attribute__((aligned(16))) __bf16 Kt[2][D * C::TPITCH];
 
   const int tid = threadIdx.x;
@@ -419,63 +447,67 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) dqacc[db] = f32x16{};
 
-  // staging: with at least two threads per unit, half the threads stage K and
-  // half stage V; otherwise every thread stages both
-  constexpr bool kSplit = C::NT >= 2 * C::UNITS;
-  constexpr int kRegsets = kSplit ? 1 : 2;
-  constexpr int kUpt = kSplit ? 1 : C::UPT;
-  u32x4 sreg[kRegsets][kUpt][4];
-  auto load_tile = [&](int kt) FA_INLINE {
-    const int key0 = kt * BC;
+  // Staging.  Row-major K and V tiles are copied straight from global memory
+  // into LDS (lane l of a wave fills bytes [16 l, 16 l + 16) of a 1 KiB
+  // block; each lane fetches the global chunk that the XOR swizzle places
+  // there), two tiles ahead.  The buffer descriptors cover exactly one head,
+  // so keys at or past N read as zeros; keys in [L_b, N) are masked.  Tile
+  // t+1's transposed K copy is built from its row-major copy during
+  // iteration t, so one barrier per tile suffices.
+  constexpr int kRowsPerBlk = 1024 / (D * 2);
+  constexpr int kBlksPerTensor = BC / kRowsPerBlk;
+  constexpr int kBlksPerWave = 2 * kBlksPerTensor / NW;
+  static_assert(2 * kBlksPerTensor % NW == 0 && kBlksPerWave >= 1, "whole 1 KiB blocks per wave");
+  static_assert(C::UNITS <= C::NT, "one transposition unit per thread");
+  const int head_bytes = N * D * 2;
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Kh), 0, head_bytes, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Vh), 0, head_bytes, kBufferRsrcWord3);
+  const int blk_row = lane / (D / 8);
+  const int blk_cpos = lane % (D / 8);
+  auto issue_tile = [&](int kt, int slot) FA_INLINE {
 #pragma unroll
-    for (int set = 0; set < kRegsets; ++set)
-#pragma unroll
-      for (int i = 0; i < kUpt; ++i) {
-        const int u = kSplit ? tid % C::UNITS : tid + i * C::NT;
-        const bool is_k = kSplit ? (tid < C::UNITS) : (set == 0);
-        const __bf16* src = is_k ? Kh : Vh;
-        const int kg = u % (BC / 4);
-        const int dc = u / (BC / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + 4 * kg + r;
-          const bool ok = (kSplit ? tid < 2 * C::UNITS : u < C::UNITS) && key < kv_len;
-          sreg[set][i][r] = ok ? *reinterpret_cast<const u32x4*>(src + (size_t)key * D + dc * 8)
-                               : u32x4{};
-        }
-      }
+    for (int j = 0; j < kBlksPerWave; ++j) {
+      const int blk = wave * kBlksPerWave + j;
+      const bool is_k = blk < kBlksPerTensor;
+      const int rb = is_k ? blk : blk - kBlksPerTensor;
+      const int row = rb * kRowsPerBlk + blk_row;
+      const int chunk = blk_cpos ^ row_swizzle<D>(row);
+      const int voff = (kt * BC + row) * (D * 2) + chunk * 16;
+      __bf16* dst = (is_k ? Ks[slot] : Vs[slot]) + rb * kRowsPerBlk * D;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_k ? k_rsrc : v_rsrc, dst, 16, voff, 0, 0, 0);
+    }
   };
-  auto store_tile = [&](int buf) FA_INLINE {
+  const int tkg = tid % (BC / 4);
+  const int tdc = tid / (BC / 4);
+  auto transpose_tile = [&](int slot, int tbuf) FA_INLINE {
+    if (tid < C::UNITS) {
+      u32x4 rows[4];
 #pragma unroll
-    for (int set = 0; set < kRegsets; ++set)
-#pragma unroll
-      for (int i = 0; i < kUpt; ++i) {
-        const int u = kSplit ? tid % C::UNITS : tid + i * C::NT;
-        const bool active = kSplit ? tid < 2 * C::UNITS : u < C::UNITS;
-        if (!active) continue;
-        const bool is_k = kSplit ? (tid < C::UNITS) : (set == 0);
-        __bf16* rm = is_k ? Ks[buf] : Vs[buf];
-        const int kg = u % (BC / 4);
-        const int dc = u / (BC / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 4 * kg + r;
-          *reinterpret_cast<u32x4*>(&rm[row * D + (dc ^ row_swizzle<D>(row)) * 8]) =
-              sreg[set][i][r];
-        }
-        if (is_k) store_transposed(Kt[buf], C::TPITCH, dc * 8, perm_pos(kg), sreg[set][i]);
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * tkg + r;
+        rows[r] = *reinterpret_cast<const u32x4*>(
+            &Ks[slot][row * D + (tdc ^ row_swizzle<D>(row)) * 8]);
       }
+      store_transposed(Kt[tbuf], C::TPITCH, tdc * 8, perm_pos(tkg), rows);
+    }
   };
 
   if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
+    issue_tile(0, 0);
+    if (n_kt > 1) issue_tile(1, 1);
+    wait_vmem();
+    __syncthreads();
+    transpose_tile(0, 0);
     __syncthreads();
   }
 
   for (int kt = 0; kt < n_kt; ++kt) {
+    const int slot = kt % 3;
     const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (kt + 2 < n_kt) issue_tile(kt + 2, (kt + 2) % 3);
+    if (kt + 1 < n_kt) transpose_tile((kt + 1) % 3, buf ^ 1);
     const int key0 = kt * BC;
     const bool wave_active = (qw0 < N) && (!causal || key0 <= qw0 + 31);
     if (wave_active) {
@@ -492,8 +524,8 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         for (int c = 0; c < C::NCB; ++c) {
           const int arow = c * 32 + l32;
           const int ro = arow * D + ((2 * ks + hi) ^ row_swizzle<D>(arow)) * 8;
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][ro]);
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[buf][ro]);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[slot][ro]);
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[slot][ro]);
           sacc[c] = mfma_bf16(ka, qf[ks], sacc[c]);
           pacc[c] = mfma_bf16(va, of[ks], pacc[c]);
         }
@@ -521,8 +553,10 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           dqacc[db] = mfma_bf16(ka, dsb[g], dqacc[db]);
         }
     }
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
-    __syncthreads();
+    // tile t+2 has landed and tile t+1's transposed copy is complete once
+    // every wave passes here
+    wait_vmem();
+    lds_barrier();
   }
 
   if (qrow < N) {

@@ -69,6 +69,24 @@ __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 
 __device__ __forceinline__ float bf16_to_f32(__bf16 x) { return (float)x; }
 
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs (32-bit data format,
+// no swizzling); out-of-range offsets read as zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// Wait until every vector-memory load issued by this wave has completed,
+// including loads whose destination is LDS.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Work-group barrier for LDS traffic issued by ordinary LDS instructions:
+// waits for this wave's LDS reads and writes, then for every wave.  Global
+// loads still in flight, including loads whose destination is LDS, stay in
+// flight across it (a fence would wait for those as well); their LDS data
+// may be read only after wait_vmem() and a later barrier.  The memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Key length of sequence b clamped to [0, N] (N when no lengths are given).
 __device__ __forceinline__ int key_length(const int32_t* seqlens_k, int b, int N) {
   if (seqlens_k == nullptr) return N;

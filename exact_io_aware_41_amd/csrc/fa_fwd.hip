@@ -67,8 +67,6 @@ namespace fa {
 
 namespace {
 
-constexpr int kVPerm[4] = {0, 2, 1, 3};
-
 template <int D, int QB, int NW, int BC>
 struct FwdBf16Cfg {
   static constexpr int BR = NW * QB * 32;  // query rows per work-group
@@ -221,7 +219,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       const int kg = u % (BC / 4);
       const int dc = u / (BC / 4);
       // keys 4kg..4kg+3 sit at positions 16g + 4*perm(a) of each V^T row
-      const int pos = 16 * (kg >> 2) + 4 * kVPerm[kg & 3];
+      const int pos = 16 * (kg >> 2) + 4 * (((kg & 1) << 1) | ((kg >> 1) & 1));
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int w = j >> 1;
