@@ -24,6 +24,8 @@ from .attention import (
     attention_online,
     attention_backward,
     finite_difference_grads,
+    merge_states,
+    attention_decode,
 )
 
 __all__ = [
@@ -35,4 +37,6 @@ __all__ = [
     "attention_online",
     "attention_backward",
     "finite_difference_grads",
+    "merge_states",
+    "attention_decode",
 ]

@@ -37,6 +37,8 @@ __all__ = [
     "attention_online",
     "attention_backward",
     "finite_difference_grads",
+    "merge_states",
+    "attention_decode",
 ]
 
 
@@ -343,3 +345,76 @@ def finite_difference_grads(q, k, v, do, scale, causal=False, lengths=None, eps=
             g[idx] = (loss(*plus) - loss(*minus)) / (2.0 * eps)
         grads.append(g)
     return tuple(grads)
+
+
+# ---------------------------------------------------------------------------
+# Decoding against a key/value cache, split over the key dimension
+# ---------------------------------------------------------------------------
+
+def merge_states(o_parts, lse_parts):
+    """Combine partial results of one softmax row computed over disjoint key sets.
+
+    [deep] "What it does not do": at decode time the useful parallelism is
+    across the sequence dimension (flash-decoding).  Each part s covers its own
+    keys and yields the normalised partial output o_s and
+    lse_s = ln sum_{j in s} exp(s_j).  Writing lse_s = m_s + ln l_s, this is the
+    rescale-and-add step of the online recurrence ([clozo] "Step 2";
+    [infra] "Keep only the state needed for the final weighted average")
+    applied to whole parts:
+        LSE = ln sum_s exp(lse_s),   O = sum_s exp(lse_s - LSE) o_s.
+    The largest lse is subtracted before exponentiating.  Parts with
+    lse_s = -inf (no visible key) contribute nothing; when every part is empty
+    O = 0 and LSE = -inf (the empty-row policy of [infra] "Executable
+    recurrence, with an empty-state policy").
+
+    o_parts: [..., S, d]; lse_parts: [..., S].  Returns (O [..., d], LSE [...]).
+    """
+    o = np.asarray(o_parts, dtype=np.float64)
+    lse = np.asarray(lse_parts, dtype=np.float64)
+    m = lse.max(axis=-1, keepdims=True)
+    nonempty = np.isfinite(m)
+    m_safe = np.where(nonempty, m, 0.0)
+    w = np.where(np.isneginf(lse), 0.0, np.exp(lse - m_safe))
+    total = w.sum(axis=-1, keepdims=True)
+    total_safe = np.where(nonempty, total, 1.0)
+    out = (w[..., None] * o).sum(axis=-2) / total_safe
+    out = np.where(nonempty, out, 0.0)
+    lse_out = np.where(nonempty, m_safe + np.log(total_safe), -np.inf)
+    return out, lse_out[..., 0]
+
+
+def attention_decode(q, k, v, scale, lengths=None, chunk=None):
+    """One new query row per (batch, head) against a key/value cache.
+
+    q: [B, H, d]; k, v: [B, H, N, d] (cache of capacity N); the query attends
+    to every cached key j < L_b ([deep] "What it does not do": a decode step
+    has a single query row and reads the whole cache, one score per key).
+    chunk=None computes the plain definition (one materialised score row);
+    chunk=C splits the keys into parts [0, C), [C, 2C), ..., computes each
+    part's (o_s, lse_s) by the plain definition on its own keys, and combines
+    them with merge_states.  Returns (O [B, H, d], LSE [B, H]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, N, d = k.shape
+    o = np.zeros((B, H, v.shape[3]))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        L = _clamp_length(None if lengths is None else lengths[b], N)
+        bounds = [(0, L)] if chunk is None else [(c0, min(c0 + chunk, L))
+                                                 for c0 in range(0, max(L, 1), chunk)]
+        for h in range(H):
+            parts_o, parts_lse = [], []
+            for c0, c1 in bounds:
+                if c1 <= c0:
+                    parts_o.append(np.zeros(v.shape[3]))
+                    parts_lse.append(-np.inf)
+                    continue
+                s = scale * (k[b, h, c0:c1] @ q[b, h])
+                m = s.max()
+                e = np.exp(s - m)
+                parts_o.append(e @ v[b, h, c0:c1] / e.sum())
+                parts_lse.append(m + np.log(e.sum()))
+            o[b, h], lse[b, h] = merge_states(np.array(parts_o), np.array(parts_lse))
+    return o, lse

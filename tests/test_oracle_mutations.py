@@ -85,3 +85,37 @@ def test_swapped_backward_outputs_are_caught(monkeypatch):
     monkeypatch.setattr(oracle, "attention_backward", swapped)
     assert _fails(pins.test_backward_matches_finite_differences, False, None)
     assert _fails(pins.test_backward_invariants)
+
+
+def test_merge_without_max_subtraction_is_caught(monkeypatch):
+    def unsafe(o_parts, lse_parts):
+        o = np.asarray(o_parts, np.float64)
+        with np.errstate(over="ignore", invalid="ignore"):
+            w = np.exp(np.asarray(lse_parts, np.float64))
+            return (w[..., None] * o).sum(-2) / w.sum(-1, keepdims=True), np.log(w.sum(-1))
+
+    monkeypatch.setattr(oracle, "merge_states", unsafe)
+    assert _fails(pins.test_merge_is_finite_at_large_lse)
+
+
+def test_merge_ignoring_weights_is_caught(monkeypatch):
+    real = oa.merge_states
+
+    def plain_mean(o_parts, lse_parts):
+        _, lse = real(o_parts, lse_parts)
+        return np.asarray(o_parts, np.float64).mean(axis=-2), lse
+
+    monkeypatch.setattr(oracle, "merge_states", plain_mean)
+    assert _fails(pins.test_merge_reproduces_toy_two_tiles)
+
+
+def test_decode_key_range_off_by_one_is_caught(monkeypatch):
+    real = oa.attention_decode
+
+    def one_more(q, k, v, scale, lengths=None, chunk=None):
+        longer = None if lengths is None else np.minimum(np.asarray(lengths) + 1, k.shape[2])
+        return real(q, k, v, scale, longer, chunk)
+
+    monkeypatch.setattr(oracle, "attention_decode", one_more)
+    assert _fails(pins.test_decode_matches_torch_sdpa_with_lengths, 7)
+    assert _fails(pins.test_decode_closed_forms)

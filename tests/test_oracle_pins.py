@@ -449,3 +449,111 @@ def test_backward_invariants():
     assert np.all(dq[0] == 0.0) and np.all(dk[0] == 0.0) and np.all(dv[0] == 0.0)
     # keys beyond the length get no gradient
     assert np.all(dk[1, :, 29:] == 0.0) and np.all(dv[1, :, 29:] == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Decoding against a cache and merging partial results over key parts
+# ---------------------------------------------------------------------------
+
+def test_merge_reproduces_toy_two_tiles():
+    # each tile of the toy is one part: (o, lse) = (10, 0) and (20, ln 2)
+    g = golden("toy_two_tiles.json")
+    o, lse = oracle.merge_states(np.array([[10.0], [20.0]]), np.array([0.0, math.log(2.0)]))
+    assert o[0] == pytest.approx(g["output"]["numerator"] / g["output"]["denominator"], rel=1e-15)
+    # LSE = m + ln l after the last tile
+    assert lse == pytest.approx(math.log(2.0) + math.log(g["after_tile_2"]["l"]), rel=1e-15)
+
+
+def test_merge_reproduces_six_score_running_sum():
+    g = golden("six_scores.json")
+    s = np.array(g["scores"], dtype=np.float64)
+    t = g["tile"]
+    parts = [math.log(np.exp(s[i:i + t]).sum()) for i in range(0, len(s), t)]
+    _, lse = oracle.merge_states(np.zeros((len(parts), 1)), np.array(parts))
+    # the page's rescaled sum is l relative to the final maximum 4.0
+    assert round(math.exp(lse - 4.0), g["printed_decimals"]) == g["after_block_2"]["l"]
+
+
+def _sdpa_decode(q, k, v, scale, lengths):
+    import torch
+    B, H, N, d = k.shape
+    o = np.zeros((B, H, v.shape[3]))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        L = N if lengths is None else int(min(max(lengths[b], 0), N))
+        if L == 0:
+            continue
+        qt = torch.from_numpy(q[b][:, None, :])            # [H, 1, d]
+        kt = torch.from_numpy(np.ascontiguousarray(k[b, :, :L]))
+        vt = torch.from_numpy(np.ascontiguousarray(v[b, :, :L]))
+        o[b] = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[:, 0].numpy()
+        lse[b] = torch.logsumexp(scale * (kt @ qt.transpose(1, 2))[..., 0], dim=-1).numpy()
+    return o, lse
+
+
+@pytest.mark.parametrize("chunk", [None, 1, 3, 7, 16, 64])
+def test_decode_matches_torch_sdpa_with_lengths(chunk):
+    rng = np.random.default_rng(11)
+    B, H, N, d = 3, 2, 41, 8
+    q = rng.standard_normal((B, H, d)) * 3.0
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    lengths = np.array([41, 17, 1])
+    o, lse = oracle.attention_decode(q, k, v, 0.4, lengths, chunk=chunk)
+    ro, rl = _sdpa_decode(q, k, v, 0.4, lengths)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
+
+
+def test_decode_closed_forms():
+    rng = np.random.default_rng(12)
+    B, H, N, d = 3, 2, 9, 4
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    # zero query: every visible key weighs the same
+    lengths = np.array([9, 4, 0])
+    o, lse = oracle.attention_decode(np.zeros((B, H, d)), k, v, 1.0, lengths, chunk=2)
+    np.testing.assert_allclose(o[0], v[0].mean(axis=1), atol=1e-14)
+    np.testing.assert_allclose(o[1], v[1, :, :4].mean(axis=1), atol=1e-14)
+    np.testing.assert_allclose(lse[:2], np.log([[9.0, 9.0], [4.0, 4.0]]), atol=1e-14)
+    # an empty cache gives the empty-row policy
+    assert np.all(o[2] == 0.0) and np.all(np.isneginf(lse[2]))
+    # one visible key: the output is that value row, LSE its scaled score
+    q = rng.standard_normal((B, H, d))
+    o, lse = oracle.attention_decode(q, k, v, 0.7, np.array([1, 1, 1]), chunk=3)
+    np.testing.assert_allclose(o, v[:, :, 0], atol=1e-14)
+    np.testing.assert_allclose(lse, 0.7 * np.einsum("bhd,bhd->bh", q, k[:, :, 0]), atol=1e-14)
+
+
+def test_merge_associativity_and_order():
+    rng = np.random.default_rng(13)
+    o = rng.standard_normal((6, 5))
+    lse = rng.standard_normal(6) * 4.0
+    lse[2] = -np.inf
+    whole_o, whole_l = oracle.merge_states(o, lse)
+    a_o, a_l = oracle.merge_states(o[:4], lse[:4])
+    b_o, b_l = oracle.merge_states(o[4:], lse[4:])
+    two_o, two_l = oracle.merge_states(np.stack([a_o, b_o]), np.array([a_l, b_l]))
+    np.testing.assert_allclose(two_o, whole_o, atol=1e-14)
+    assert two_l == pytest.approx(whole_l, abs=1e-14)
+    perm = rng.permutation(6)
+    p_o, p_l = oracle.merge_states(o[perm], lse[perm])
+    np.testing.assert_allclose(p_o, whole_o, atol=1e-14)
+    assert p_l == pytest.approx(whole_l, abs=1e-14)
+
+
+def test_merge_is_finite_at_large_lse():
+    # parts with weights 1 : 3 at lse near 1000 (exp overflows without the max)
+    o = np.array([[1.0, 0.0], [0.0, 1.0]])
+    lse = np.array([1000.0, 1000.0 + math.log(3.0)])
+    out, l = oracle.merge_states(o, lse)
+    np.testing.assert_allclose(out, [0.25, 0.75], atol=1e-15)
+    assert l == pytest.approx(1000.0 + math.log(4.0), abs=1e-12)
+
+
+def test_merge_empty_parts():
+    o = np.array([[5.0], [7.0], [9.0]])
+    out, l = oracle.merge_states(o, np.array([-np.inf, 0.5, -np.inf]))
+    assert out[0] == 7.0 and l == 0.5
+    out, l = oracle.merge_states(o, np.array([-np.inf, -np.inf, -np.inf]))
+    assert out[0] == 0.0 and np.isneginf(l)
