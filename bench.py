@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd/bwd TFLOP/s at N=8192,d=128 bf16; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3          # MI355X fp32 MFMA, published
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("fa_common.hpp", "fa_fwd.hip", "fa_bwd.hip")
 
@@ -72,6 +73,11 @@ def parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--workload", default="attention", choices=["attention", "decode"],
+                   help="attention: the --config workload (default, the headline metric); "
+                        "decode: one query row per head against an 8192-position cache")
+    p.add_argument("--decode-lengths", default=None, choices=[None, "zero_then_uniform"],
+                   help="cached lengths of the decode workload (default: all full)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time for the oracle baseline sample (0 disables it)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -156,6 +162,9 @@ def main():
     if not torch.cuda.is_available():
         log("bench.py needs a GPU")
         sys.exit(1)
+    if args.workload == "decode":
+        decode_main(args)
+        return
     cfg = fi.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -246,14 +255,7 @@ def main():
         extra["bwd_tflops"] = round((flops - fwd_f) / (bwd_ms * 1e-3) / 1e12, 1)
 
     if args.calibrate_copy > 0:
-        nbytes = args.calibrate_copy << 20
-        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy: {nbytes} bytes read and {nbytes} bytes written")
-        del src, dst
+        calibration_copy(torch, dev, args.calibrate_copy)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -283,6 +285,133 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def calibration_copy(torch, dev, mib):
+    """One device copy of known size, so that counter readings of the kernels
+    can be scaled by what the same counters read for it."""
+    nbytes = mib << 20
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {nbytes} bytes read and {nbytes} bytes written")
+
+
+def decode_main(args):
+    """One decode step per timed step: fa_decode (split kernel + merge) over
+    the decode workload, reported as HBM GB/s of the minimum traffic."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_41_amd as fa
+    import fa_inputs as fi
+
+    cfg = fi.DECODE
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    inputs = fi.make_decode_inputs(cfg, lengths=args.decode_lengths)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s: {cfg.name}")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v = up(inputs["q"]), up(inputs["k"]), up(inputs["v"])
+    lengths = inputs["lengths"]
+    lens = None if lengths is None else torch.from_numpy(lengths).to(dev)
+    B, H, N, d = cfg.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    ws_bytes = fa.fa_decode_workspace_size(fa.FA_DTYPE_BF16, B, H, N, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    parts = ws_bytes // (B * H * (d + 1) * 4)
+    o_parts = ws[:B * H * parts * d * 4].view(torch.float32).view(B * H, parts, d)
+    lse_parts = ws[B * H * parts * d * 4:].view(torch.float32).view(B * H, parts)
+
+    def step():
+        fa.decode(q, k, v, scale=cfg.scale, seqlens_k=lens, out=o, lse=lse, workspace=ws)
+
+    def merge_only():
+        fa.merge_states(o_parts, lse_parts, dtype=torch.bfloat16, out=o.view(B * H, d),
+                        lse=lse.view(B * H))
+
+    def timed(fn, steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    for _ in range(args.warmup):
+        step()
+    ms_per_step = timed(step, args.steps)
+    merge_ms = timed(merge_only, args.steps)
+    step()
+    torch.cuda.synchronize()
+    split_ms = ms_per_step - merge_ms
+    if args.calibrate_copy > 0:
+        calibration_copy(torch, dev, args.calibrate_copy)
+    nbytes = fi.decode_bytes(B, H, N, d, 2, lengths)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (split_ms * 1e-3) / 1e9
+    log(f"per-launch ms: decode_split={split_ms:.4f} (by difference), merge={merge_ms:.4f}; "
+        f"{parts} parts per row")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                           if i.get("user_api") == "blas"), default=1)
+        except ImportError:
+            threads = 1
+        qw, kw, vw = (fi.widen(inputs[n], "bf16") for n in ("q", "k", "v"))
+        done_bytes, t_cpu, heads = 0, 0.0, 0
+        for b in range(B):
+            for h in range(H):
+                sub = None if lengths is None else lengths[b:b + 1]
+                t1 = time.perf_counter()
+                oracle.attention_decode(qw[b:b + 1, h:h + 1], kw[b:b + 1, h:h + 1],
+                                        vw[b:b + 1, h:h + 1], cfg.scale, sub)
+                t_cpu += time.perf_counter() - t1
+                done_bytes += fi.decode_bytes(1, 1, N, d, 2, sub)
+                heads += 1
+                if t_cpu >= args.cpu_seconds:
+                    break
+            if t_cpu >= args.cpu_seconds:
+                break
+        cpu = {"value": round(done_bytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{heads} of {B * H} heads (fp64 decode, one score row each), "
+                         f"{t_cpu:.1f} s", "seconds": round(t_cpu, 2)}
+
+    line = {
+        "metric": "decode HBM GB/s (one query row per head, 8192-position cache, d=128 bf16)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1) inputs)",
+        "config": {"workload": "decode against a key/value cache (split over keys + merge)",
+                   "B": B, "H": H, "N": N, "d": d, "parts_per_row": int(parts),
+                   "key_lengths": None if lengths is None else [int(x) for x in lengths],
+                   "bytes_per_step": int(nbytes)},
+        "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "per_launch_ms": {"decode_split": round(split_ms, 4), "merge": round(merge_ms, 4)},
     }
     print(json.dumps(line), flush=True)
 

@@ -26,7 +26,8 @@ __all__ = [
     "FAError", "FALibraryMissing", "LIB_PATH", "load_library",
     "fa_abi_version", "fa_status_string", "fa_forward", "fa_backward",
     "fa_backward_workspace_size", "fa_backward_preprocess", "fa_backward_dkdv",
-    "fa_backward_dq", "forward", "backward", "backward_phases",
+    "fa_backward_dq", "fa_decode_workspace_size", "fa_decode", "fa_merge_states",
+    "forward", "backward", "backward_phases", "decode", "merge_states",
 ]
 
 FA_SUCCESS = 0
@@ -38,7 +39,8 @@ FA_DTYPE_BF16 = 1
 
 EXPORTED_SYMBOLS = ("fa_abi_version", "fa_status_string", "fa_forward",
                     "fa_backward_workspace_size", "fa_backward", "fa_backward_preprocess",
-                    "fa_backward_dkdv", "fa_backward_dq")
+                    "fa_backward_dkdv", "fa_backward_dq", "fa_decode_workspace_size",
+                    "fa_decode", "fa_merge_states")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_mi355x.so")
 
@@ -86,6 +88,12 @@ def load_library():
     lib.fa_backward_dq.restype = i32
     lib.fa_backward_dq.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, i32,
                                    vp, vp]
+    lib.fa_decode_workspace_size.restype = sz
+    lib.fa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.fa_decode.restype = i32
+    lib.fa_decode.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
+    lib.fa_merge_states.restype = i32
+    lib.fa_merge_states.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -131,6 +139,21 @@ def fa_backward_dq(dtype, B, H, N, d, q, k, v, dout, lse, delta, seqlens_k, scal
                    stream=0) -> int:
     return load_library().fa_backward_dq(dtype, B, H, N, d, q, k, v, dout, lse, delta, seqlens_k,
                                          scale, causal, dq, stream)
+
+
+def fa_decode_workspace_size(dtype, B, H, N, d) -> int:
+    return load_library().fa_decode_workspace_size(dtype, B, H, N, d)
+
+
+def fa_decode(dtype, B, H, N, d, q, k, v, seqlens_k, scale, o, lse, workspace, workspace_bytes,
+              stream=0) -> int:
+    return load_library().fa_decode(dtype, B, H, N, d, q, k, v, seqlens_k, scale, o, lse,
+                                    workspace, workspace_bytes, stream)
+
+
+def fa_merge_states(dtype, rows, n_parts, d, o_parts, lse_parts, o, lse, stream=0) -> int:
+    return load_library().fa_merge_states(dtype, rows, n_parts, d, o_parts, lse_parts, o, lse,
+                                          stream)
 
 
 # ---------------------------------------------------------------------------
@@ -272,3 +295,66 @@ def backward_phases(q, k, v, o, do, lse, scale=None, causal=False, seqlens_k=Non
         raise FAError(st, "fa_backward_dq")
     rec(3)
     return dq, dk, dv
+
+
+def decode(q, k, v, scale=None, seqlens_k=None, out=None, lse=None, workspace=None):
+    """O, LSE of one query row per (batch, head) against a key/value cache.
+
+    q: [B, H, d]; k, v: [B, H, N, d] (cache of capacity N); ``seqlens_k`` an
+    optional int32 [B] tensor of cached lengths.  Returns (o [B, H, d] in q's
+    dtype, lse fp32 [B, H]).
+    """
+    import torch
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, H, d] and k, v [B, H, N, d]")
+    B, H, N, d = k.shape
+    if q.shape != (B, H, d) or q.dtype != k.dtype or q.device != k.device or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, H, d] tensor like k")
+    _check_like("v", v, k)
+    if not k.is_contiguous():
+        raise ValueError("k must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    seqlens_k = _lengths(seqlens_k, k)
+    out = torch.empty_like(q) if out is None else out
+    _check_like("out", out, q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if lse.shape != (B, H) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H] tensor")
+    code = _dtype_code(q)
+    ws_bytes = fa_decode_workspace_size(code, B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    st = fa_decode(code, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens_k), float(scale),
+                   _ptr(out), _ptr(lse), _ptr(workspace),
+                   workspace.numel() * workspace.element_size(), _stream(q.device))
+    if st != FA_SUCCESS:
+        raise FAError(st, "fa_decode")
+    return out, lse
+
+
+def merge_states(o_parts, lse_parts, dtype=None, out=None, lse=None):
+    """Merge partial results over disjoint key sets.
+
+    o_parts: fp32 [R, S, d]; lse_parts: fp32 [R, S].  Returns (o [R, d] in
+    ``dtype`` (default fp32), lse fp32 [R]).
+    """
+    import torch
+    if o_parts.dim() != 3 or o_parts.dtype != torch.float32 or not o_parts.is_contiguous():
+        raise ValueError("o_parts must be a contiguous fp32 [R, S, d] tensor")
+    R, S, d = o_parts.shape
+    if (lse_parts.shape != (R, S) or lse_parts.dtype != torch.float32
+            or not lse_parts.is_contiguous() or lse_parts.device != o_parts.device):
+        raise ValueError("lse_parts must be a contiguous fp32 [R, S] tensor on o_parts' device")
+    dtype = torch.float32 if dtype is None else dtype
+    out = torch.empty((R, d), dtype=dtype, device=o_parts.device) if out is None else out
+    if out.shape != (R, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [R, d] tensor")
+    if lse is None:
+        lse = torch.empty((R,), dtype=torch.float32, device=o_parts.device)
+    st = fa_merge_states(_dtype_code(out), R, S, d, _ptr(o_parts), _ptr(lse_parts), _ptr(out),
+                         _ptr(lse), _stream(o_parts.device))
+    if st != FA_SUCCESS:
+        raise FAError(st, "fa_merge_states")
+    return out, lse

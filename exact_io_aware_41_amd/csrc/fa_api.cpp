@@ -24,6 +24,14 @@ bool fwd_supported(fa_dtype dtype, int d) {
 
 bool bwd_supported(fa_dtype dtype, int d) { return dtype == FA_DTYPE_BF16 && (d == 64 || d == 128); }
 
+bool decode_supported(fa_dtype dtype, int d) {
+  return (dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_BF16) && (d == 64 || d == 128);
+}
+
+// Longest cache a decode call accepts (parts of at most 4096 keys, at most
+// 4096 parts per row).
+constexpr int kMaxDecodeN = 4096 * 4096;
+
 bool known_dtype(fa_dtype dtype) { return dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_BF16; }
 
 // Shared size/scale/flag checks.  Returns FA_SUCCESS when the problem is
@@ -170,6 +178,53 @@ fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int N, int d, const void*
                 lse,   seqlens_k, scale, causal, dq, nullptr, nullptr, const_cast<float*>(delta),
                 stream};
   return fa::launch_bwd_dq_bf16(a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+}
+
+size_t fa_decode_workspace_size(fa_dtype dtype, int B, int H, int N, int d) {
+  (void)dtype;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
+  const fa::DecodePlan p = fa::decode_plan(B, H, N);
+  return (size_t)B * (size_t)H * (size_t)p.parts * ((size_t)d + 1) * sizeof(float);
+}
+
+fa_status fa_decode(fa_dtype dtype, int B, int H, int N, int d, const void* q, const void* k,
+                    const void* v, const int32_t* seqlens_k, float scale, void* o, float* lse,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bool empty = false;
+  fa_status st = check_common(dtype, B, H, N, d, scale, 0, &empty);
+  if (st != FA_SUCCESS) return st;
+  if (!decode_supported(dtype, d)) return FA_ERROR_UNSUPPORTED;
+  if (empty) return FA_SUCCESS;
+  if (N > kMaxDecodeN) return FA_ERROR_INVALID_VALUE;
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(workspace))
+    return FA_ERROR_INVALID_VALUE;
+  if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < fa_decode_workspace_size(dtype, B, H, N, d)) return FA_ERROR_INVALID_VALUE;
+  const fa::DecodePlan p = fa::decode_plan(B, H, N);
+  if ((long long)B * H * p.parts > kMaxGrid || (long long)B * H > kMaxGrid)
+    return FA_ERROR_INVALID_VALUE;
+  fa::DecodeArgs a{B, H, N, d, q, k, v, seqlens_k, scale, o, lse,
+                   static_cast<float*>(workspace), stream};
+  return fa::launch_decode(a, dtype == FA_DTYPE_BF16) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+}
+
+fa_status fa_merge_states(fa_dtype dtype, int rows, int n_parts, int d, const float* o_parts,
+                          const float* lse_parts, void* o, float* lse, hipStream_t stream) {
+  if (!known_dtype(dtype)) return FA_ERROR_INVALID_VALUE;
+  if (rows < 0 || n_parts < 1 || d <= 0) return FA_ERROR_INVALID_VALUE;
+  if (!decode_supported(dtype, d)) return FA_ERROR_UNSUPPORTED;
+  if (n_parts > fa::kMaxMergeParts) return FA_ERROR_INVALID_VALUE;
+  if (rows == 0) return FA_SUCCESS;
+  if (!o_parts || !lse_parts || !o) return FA_ERROR_INVALID_VALUE;
+  if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || (lse && !aligned16(lse)))
+    return FA_ERROR_INVALID_VALUE;
+  if ((long long)rows > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  return fa::launch_merge(rows, n_parts, d, o_parts, lse_parts, o, lse, dtype == FA_DTYPE_BF16,
+                          stream) == hipSuccess
+             ? FA_SUCCESS
+             : FA_ERROR_LAUNCH;
 }
 
 }  // extern "C"

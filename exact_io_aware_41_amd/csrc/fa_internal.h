@@ -40,6 +40,28 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+struct DecodeArgs {
+  int B, H, N, d;
+  const void* q;  // [B][H][d]
+  const void* k;  // [B][H][N][d]
+  const void* v;
+  const int32_t* seqlens_k;
+  float scale;
+  void* o;     // [B][H][d]
+  float* lse;  // [B][H]
+  float* workspace;
+  hipStream_t stream;
+};
+
+// How decoding splits the keys of one (batch, head): `parts` parts of
+// `chunk` keys (the last one possibly shorter).
+struct DecodePlan {
+  int parts, chunk;
+};
+DecodePlan decode_plan(int B, int H, int N);
+// Largest number of parts a merge accepts (weights are kept in LDS).
+constexpr int kMaxMergeParts = 4096;
+
 // Each launcher returns hipSuccess or the error hipGetLastError reported
 // after enqueueing; it never synchronises.
 hipError_t launch_fwd_bf16(const FwdArgs& a);
@@ -48,6 +70,10 @@ hipError_t launch_bwd_bf16(const BwdArgs& a);
 hipError_t launch_bwd_preprocess_bf16(const BwdArgs& a);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a);
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a);
+hipError_t launch_decode(const DecodeArgs& a, bool bf16);
+hipError_t launch_merge(int rows, int n_parts, int d, const float* o_parts,
+                        const float* lse_parts, void* o, float* lse, bool bf16,
+                        hipStream_t stream);
 
 // Number of work-groups a launch of the given geometry needs; the ABI
 // rejects problems whose grid would not fit in a signed 32-bit count.

@@ -230,3 +230,36 @@ def min_bytes(B, H, N, d, es, backward=False):
     if not backward:
         return 4 * nd * es + 4 * rows
     return 8 * nd * es + 4 * rows + 8 * rows
+
+
+# ---------------------------------------------------------------------------
+# Decoding against a cache
+# ---------------------------------------------------------------------------
+
+# One new query row per (batch, head) against a cache shaped like the pages'
+# running example (8,192 positions, d = 128, 32 heads), batch 8.
+DECODE = Config(0, "decode: B=8 H=32 cache 8192 d=128 bf16", 8, 32, 8192, 128, "bf16", False,
+                None)
+
+
+def make_decode_inputs(cfg: Config, seed: int = 0, lengths: str | None = None):
+    """q [B, H, d] (row 0 of each head's q stream), k and v [B, H, N, d]
+    caches in device format, and int32 [B] cached lengths (None = all N;
+    "zero_then_uniform" as for the forward workloads)."""
+    q = make_tensor(cfg, "q", seed, N=1)[:, :, 0]
+    k = make_tensor(cfg, "k", seed)
+    v = make_tensor(cfg, "v", seed)
+    lens = None
+    if lengths is not None:
+        lens = make_lengths(dataclasses.replace(cfg, lengths=lengths), seed)
+    return {"q": np.ascontiguousarray(q), "k": k, "v": v, "lengths": lens}
+
+
+def decode_bytes(B, H, N, d, es, lengths=None):
+    """Minimum HBM bytes of a decode step: the visible cache rows of K and V
+    read once, q read and o written once, one fp32 LSE per row."""
+    if lengths is None:
+        cached = B * N
+    else:
+        cached = int(np.clip(np.asarray(lengths, np.int64), 0, N).sum())
+    return H * (2 * cached * d * es) + B * H * (2 * d * es + 4)

@@ -59,6 +59,7 @@
  * Compiled (dtype, d) set:
  *  forward : FA_DTYPE_F32 with d in {64, 128}; FA_DTYPE_BF16 with d in {64, 128}
  *  backward: FA_DTYPE_BF16 with d in {64, 128}
+ *  decode and merge: FA_DTYPE_F32 or FA_DTYPE_BF16 with d in {64, 128}
  */
 #ifndef FA_MI355X_FA_H
 #define FA_MI355X_FA_H
@@ -175,6 +176,58 @@ fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int N, int d,
                          const void* dout, const float* lse, const float* delta,
                          const int32_t* seqlens_k, float scale, int causal,
                          void* dq, hipStream_t stream);
+
+/*
+ * Decoding: one new query row per (batch, head) against a key/value cache,
+ * split over the key dimension ("FlashAttention" (deepconcepts.dev), "What
+ * it does not do": a decode step has a single query row and reads the whole
+ * cache; the parallelism that helps is across the sequence dimension when the
+ * batch is too small to fill the GPU, flash-decoding).  The query attends to
+ * every cached key j < L_b (no causal flag: it is the newest position).  The
+ * keys of each (batch, head) are cut into parts whose length the library
+ * chooses (a multiple of 64, at most 4096); one work-group per part writes
+ * the part's normalised output and LSE to the workspace, then
+ * fa_merge_states combines the parts.
+ *
+ *   q          [B][H][d] query rows (read only)
+ *   k, v       [B][H][N][d] cache of capacity N (read only); N <= 2^24
+ *   seqlens_k  [B] int32 cached lengths on the device, clamped to [0, N],
+ *              or NULL for N
+ *   scale      multiplier of q . k; finite and > 0
+ *   o          [B][H][d] output, same dtype as q (zeros for an empty cache)
+ *   lse        [B][H] fp32 output, natural log (-inf for an empty cache)
+ *   workspace  device buffer of at least fa_decode_workspace_size(...)
+ *              bytes, 16-byte aligned; contents on entry do not matter
+ * The result is deterministic.
+ */
+size_t fa_decode_workspace_size(fa_dtype dtype, int B, int H, int N, int d);
+fa_status fa_decode(fa_dtype dtype, int B, int H, int N, int d,
+                    const void* q, const void* k, const void* v,
+                    const int32_t* seqlens_k, float scale,
+                    void* o, float* lse,
+                    void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * Merge of partial results of the same softmax rows over disjoint key sets:
+ * the rescale-and-add step of the online recurrence applied to whole parts
+ * ("FlashAttention", "Why it is allowed to be exact"; "Explain
+ * FlashAttention and why it is IO-aware", "Keep only the state needed for
+ * the final weighted average").  For each row,
+ *   LSE = ln sum_s exp(lse_s),  O = sum_s exp(lse_s - LSE) o_s;
+ * parts with lse_s = -inf contribute nothing, and a row whose parts are all
+ * -inf gets O = 0 and LSE = -inf.
+ *
+ *   rows       number of rows (0 is an empty call)
+ *   n_parts    parts per row, 1 <= n_parts <= 4096
+ *   o_parts    [rows][n_parts][d] fp32 normalised partial outputs
+ *   lse_parts  [rows][n_parts] fp32 partial LSEs (natural log)
+ *   o          [rows][d] output in dtype
+ *   lse        [rows] fp32 output, or NULL
+ */
+fa_status fa_merge_states(fa_dtype dtype, int rows, int n_parts, int d,
+                          const float* o_parts, const float* lse_parts,
+                          void* o, float* lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

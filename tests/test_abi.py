@@ -150,3 +150,65 @@ def test_backward_phase_entry_points_validate():
     assert dkdv(dk=None) == fa.FA_ERROR_INVALID_VALUE
     assert dkdv(dv=MIS) == fa.FA_ERROR_INVALID_VALUE
     assert dq(out=None) == fa.FA_ERROR_INVALID_VALUE
+
+
+def dec(dtype=BF16, B=1, H=1, N=16, d=128, q=A, k=A, v=A, lens=None, scale=0.1, o=A, lse=A,
+        ws=A, ws_bytes=1 << 20):
+    return fa.fa_decode(dtype, B, H, N, d, q, k, v, lens, scale, o, lse, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None), dict(ws=None),
+    dict(q=MIS), dict(v=MIS), dict(o=MIS), dict(ws=MIS), dict(lens=A + 1),
+    dict(scale=0.0), dict(scale=float("nan")), dict(B=-1), dict(d=0),
+    dict(ws_bytes=16), dict(N=(1 << 24) + 1),
+])
+def test_decode_rejects_invalid_arguments(kw):
+    assert dec(**kw) == fa.FA_ERROR_INVALID_VALUE
+
+
+def test_decode_unsupported_and_empty():
+    assert dec(d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert dec(dtype=F32, d=256) == fa.FA_ERROR_UNSUPPORTED
+    assert dec(B=0, q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
+    assert dec(N=0, q=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
+
+
+def test_decode_workspace_follows_the_split_plan():
+    # B*H = 256 rows of 8192 keys: 32 parts of 256 keys, (d + 1) floats per part
+    assert fa.fa_decode_workspace_size(BF16, 8, 32, 8192, 128) == 8 * 32 * 32 * 129 * 4
+    # one short row: one part
+    assert fa.fa_decode_workspace_size(BF16, 1, 1, 100, 128) == 129 * 4
+    assert fa.fa_decode_workspace_size(BF16, 0, 1, 100, 128) == 0
+    for B, H, N in [(1, 1, 1), (1, 32, 8192), (3, 5, 777), (64, 64, 65536), (1, 1, 1 << 24),
+                    (2, 2, 4097), (1000, 8, 300)]:
+        parts = fa.fa_decode_workspace_size(BF16, B, H, N, 64) // (B * H * 65 * 4)
+        assert 1 <= parts <= 4096
+        assert parts * 4096 >= N                       # no part holds more than 4096 keys
+        assert parts <= max(1, -(-N // 64))            # parts hold at least 64 keys
+
+
+def test_merge_states_validates():
+    m = lambda dtype=F32, rows=4, parts=3, d=128, op=A, lp=A, o=A, lse=A: fa.fa_merge_states(
+        dtype, rows, parts, d, op, lp, o, lse, None)
+    assert m(op=None) == fa.FA_ERROR_INVALID_VALUE
+    assert m(lp=None) == fa.FA_ERROR_INVALID_VALUE
+    assert m(o=None) == fa.FA_ERROR_INVALID_VALUE
+    assert m(o=MIS) == fa.FA_ERROR_INVALID_VALUE
+    assert m(lse=MIS) == fa.FA_ERROR_INVALID_VALUE
+    assert m(parts=0) == fa.FA_ERROR_INVALID_VALUE
+    assert m(parts=4097) == fa.FA_ERROR_INVALID_VALUE
+    assert m(rows=-1) == fa.FA_ERROR_INVALID_VALUE
+    assert m(d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert m(rows=0, op=None, lp=None, o=None) == fa.FA_SUCCESS
+
+
+def test_decode_torch_wrapper_validates_before_calling():
+    torch = pytest.importorskip("torch")
+    k = torch.zeros(1, 2, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.decode(torch.zeros(1, 2, 64, dtype=torch.bfloat16), k, k)
+    with pytest.raises(ValueError):
+        fa.decode(torch.zeros(1, 2, 128, dtype=torch.float32), k, k)
+    with pytest.raises(ValueError):
+        fa.merge_states(torch.zeros(2, 3, 128), torch.zeros(2, 4))
