@@ -73,9 +73,41 @@ __device__ __forceinline__ float bf16_to_f32(__bf16 x) { return (float)x; }
 // no swizzling); out-of-range offsets read as zero.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// Raw buffer descriptor of `bytes` bytes at `base` (gfx9 layout: 48-bit base,
+// stride 0, num_records in bytes, word 3 as above), for inline assembly.
+__device__ __forceinline__ u32x4 buffer_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = (uint32_t)kBufferRsrcWord3;
+  return r;
+}
+
+// Direct load of 16 bytes per lane into LDS (buffer_load_dwordx4 ... lds):
+// lane l writes bytes [16 l, 16 l + 16) after the wave-uniform LDS address
+// `lds`, from byte voff + soff of the buffer; out-of-range reads give zeros.
+// Issued by inline assembly: the compiler neither counts it nor orders LDS
+// accesses against it, so the caller must wait_vmem() and pass a barrier
+// before anything reads the destination.  (Issued through the builtin, the
+// compiler makes the next LDS read wait for the whole copy.)
+__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, const void* lds, int voff, int soff) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)lds));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(base), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
 // Wait until every vector-memory load issued by this wave has completed,
 // including loads whose destination is LDS.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The builtin form is visible to the compiler's own counter tracking, which
+// then knows nothing is outstanding (s_waitcnt simm16 on gfx9: vmcnt bits 3:0
+// and 15:14 = 0, expcnt bits 6:4 = 7, lgkmcnt bits 11:8 = 15).
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
 
 // Work-group barrier for LDS traffic issued by ordinary LDS instructions:
 // waits for this wave's LDS reads and writes, then for every wave.  Global
@@ -85,6 +117,53 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Row-major tiles are stored unpadded with their 16-byte chunks XOR-swizzled
+// by a function of the row.  On gfx950 a ds_read_b128 serves lanes 0-31 and
+// 32-63 in different cycles, and within a half two groups of 16 lanes
+// (split by the parity of lane bits 2..4, e.g. lanes 0-3, 12-15, 20-23,
+// 24-27); LDS banks repeat every 256 bytes.  A read is conflict-free when
+// the 16 lanes of a group touch 16 distinct 16-byte bank slots.  For d = 128
+// (one 256-byte row per bank period) the swizzle below is a linear map of
+// the row bits that is one-to-one on every such group, both for fragment
+// reads (lane l reads row 32 b + l % 32) and for the transposition reads
+// (16 lanes read rows 4 q + r of consecutive 4-row groups q, two chunk
+// columns), so neither has conflicts.  For d = 64 the fragment reads are
+// conflict-free; the transposition reads conflict two ways (two rows share
+// a bank period, leaving 8 slots for 16 lanes).
+template <int D>
+__device__ __forceinline__ int row_swizzle(int row) {
+  if constexpr (D == 128)
+    return (row & 15) ^ (((row >> 4) & 1) * 12) ^ (((row >> 5) & 1) * 2);
+  else
+    return (row ^ (row >> 2)) & (D / 8 - 1);
+}
+
+// Row-major tiles read only by transposing reads (ds_read_b64_tr_b16) swizzle
+// their 64-byte segments instead: 16 lanes of such a read fetch 4 consecutive
+// rows x 32 bytes and a wave half 4 rows x 64 bytes; XOR-ing the segment
+// index with the row's position inside its group of four rows (d = 128,
+// 256-byte rows) or of two row pairs (d = 64, 128-byte rows) puts those
+// 4 x 64 bytes on 4 distinct 64-byte bank ranges (measured conflict-free).
+template <int D>
+__device__ __forceinline__ int seg_swizzle(int row) {
+  if constexpr (D == 128)
+    return row & 3;
+  else
+    return (row >> 1) & 1;
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4
+// of the 8-byte chunks addressed by lanes i / 4 + 4 j, j = 0..3.  With lane s
+// addressing row r0 + s / 4, columns c0 + 4 (s % 4) .. + 3, lane i receives
+// column c0 + i of rows r0 .. r0 + 3.
+__device__ __forceinline__ s16x4 read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<__bf16*>(p)));
 }
 
 // Key length of sequence b clamped to [0, N] (N when no lengths are given).

@@ -15,12 +15,15 @@
 //    head); each wave owns 32 queries, one query per lane (lanes l and l^32
 //    share a query).  A wave fits in 256 VGPRs, so two waves share a SIMD.
 //  * Q stays in VGPRs as the B operand of S^T = K Q^T (32x32x16 bf16 MFMA).
-//  * K and V tiles of 64 keys are loaded from HBM with 16-byte coalesced loads
-//    into registers one tile ahead and written to LDS: K row-major (padded
-//    rows) in a two-slot ring, V transposed to [d][key] in a three-slot ring,
-//    with the key order permuted inside each 16-key group so that every MFMA
-//    A fragment is one 16-byte LDS read.  Fragments are read several MFMAs
-//    ahead of use.
+//  * K and V tiles of 128 keys go from HBM straight into LDS (buffer loads
+//    with an LDS destination, 16 bytes per lane, one tile ahead, no
+//    registers): K row-major with XOR-swizzled 16-byte chunks in a two-slot
+//    ring, V row-major with swizzled 64-byte segments in a three-slot ring.
+//    The A fragments of V^T come from two transposing reads
+//    (ds_read_b64_tr_b16) each, which also put the keys in the order of the
+//    P^T fragment; no transposed copy of V is ever written.  Fragments are
+//    read several MFMAs ahead of use.  The loop's barriers wait only for LDS
+//    traffic, so the copy of the next tile stays in flight across them.
 //  * the waves of a SIMD run out of phase: waves 4..7 multiply P(t-1) V(t-1)
 //    before computing S(t), while waves 0..3 compute S(t) first, so one
 //    wave's MFMAs overlap the other's softmax.
@@ -53,10 +56,10 @@
 #define FA_FWD_NW 8
 #endif
 #ifndef FA_FWD_BC
-#define FA_FWD_BC 64
+#define FA_FWD_BC 128
 #endif
 #ifndef FA_FWD_PREFETCH
-#define FA_FWD_PREFETCH 6
+#define FA_FWD_PREFETCH 4
 #endif
 #ifndef FA_FWD_SCHED
 #define FA_FWD_SCHED 2
@@ -75,12 +78,6 @@ struct FwdBf16Cfg {
   static constexpr int NCB = BC / 32;      // 32-key blocks per tile
   static constexpr int NG = BC / 16;       // 16-key groups per tile
   static constexpr int NDB = D / 32;       // 32-row blocks of O^T
-  static constexpr int KPITCH = D + 8;     // bf16 per K row in LDS
-  static constexpr int VPITCH = BC + 8;    // bf16 per V^T row in LDS
-  static constexpr int KUNITS = BC * D / 8;          // 16-byte K chunks per tile
-  static constexpr int KU = (KUNITS + NT - 1) / NT;
-  static constexpr int VUNITS = (BC / 4) * (D / 8);  // 4-key x 8-feature V units per tile
-  static constexpr int VU = (VUNITS + NT - 1) / NT;
   static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
 };
 
@@ -106,8 +103,10 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   // three-slot ring (group 2 still reads V(t-1) while V(t+1) is written).
   constexpr bool kPingPong = (NW >= 8);
   constexpr int kVSlots = kPingPong ? 3 : 2;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * C::KPITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[kVSlots][D * C::VPITCH];
+  // K row-major with XOR-swizzled 16-byte chunks, V row-major with swizzled
+  // 64-byte segments (read transposed); both filled by direct loads
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[kVSlots][BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,6 +151,11 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     }
   }
 
+  // the Q fragments must have landed before the loop: its tile copies are
+  // issued outside the compiler's counter tracking, so a wait it placed for Q
+  // inside the loop would also wait for the copy in flight
+  wait_vmem();
+
   f32x16 oacc[C::NDB][QB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
@@ -165,73 +169,45 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     alpha[qb] = 1.f;
   }
 
-  // ---- staging of the next K/V tile through registers
-  u32x4 kreg[C::KU];
-  u32x4 vreg[C::VU][4];
-  auto load_tile = [&](int kt) FA_INLINE {
-    const int key0 = kt * BC;
-    const bool full = key0 + BC <= kv_len;  // uniform: no row of this tile is past the length
+  // ---- staging: K and V tiles go straight from global memory into LDS
+  // (buffer loads with an LDS destination: lane l of a wave fills bytes
+  // [16 l, 16 l + 16) of a 1 KiB block), one tile ahead, with no registers.
+  // The buffer descriptors cover exactly one head, so keys at or past N read
+  // as zeros; keys in [L_b, N) are masked.  Each lane fetches the global chunk
+  // that the tile's swizzle places at its LDS position.
+  constexpr int kRowsPerBlk = 1024 / (D * 2);
+  constexpr int kBlksPerTensor = BC / kRowsPerBlk;
+  constexpr int kBlksPerWave = 2 * kBlksPerTensor / NW;
+  static_assert(2 * kBlksPerTensor % NW == 0 && kBlksPerWave >= 1, "whole 1 KiB blocks per wave");
+  const int head_bytes = N * D * 2;
+  const u32x4 k_rsrc = buffer_rsrc_words(Kh, (uint32_t)head_bytes);
+  const u32x4 v_rsrc = buffer_rsrc_words(Vh, (uint32_t)head_bytes);
+  // per-lane byte offsets inside a tile, computed once: the loads' address
+  // registers then stay untouched for the whole loop (the compiler treats
+  // them as pending load results and would otherwise wait for the copy
+  // before reusing them); the tile's position goes in the scalar offset
+  int voff[kBlksPerWave];
 #pragma unroll
-    for (int i = 0; i < C::KU; ++i) {
-      const int u = tid + i * C::NT;
-      const int r = u / (D / 8);
-      const int c8 = u % (D / 8);
-      const int key = key0 + r;
-      const bool unit = (C::KUNITS % C::NT == 0) || (u < C::KUNITS);
-      const __bf16* src = Kh + (size_t)key * D + c8 * 8;
-      if (full && unit)
-        kreg[i] = *reinterpret_cast<const u32x4*>(src);
-      else
-        kreg[i] = (unit && key < kv_len) ? *reinterpret_cast<const u32x4*>(src) : u32x4{};
-    }
+  for (int j = 0; j < kBlksPerWave; ++j) {
+    const int blk = wave * kBlksPerWave + j;
+    const bool is_k = blk < kBlksPerTensor;
+    const int rb = is_k ? blk : blk - kBlksPerTensor;
+    const int row = rb * kRowsPerBlk + lane / (D / 8);
+    const int cpos = lane % (D / 8);
+    const int chunk = is_k ? (cpos ^ row_swizzle<D>(row))
+                           : ((((cpos >> 2) ^ seg_swizzle<D>(row)) << 2) | (cpos & 3));
+    voff[j] = row * (D * 2) + chunk * 16;
+  }
+  auto issue_tile = [&](int kt, int kbuf, int vslot) FA_INLINE {
 #pragma unroll
-    for (int i = 0; i < C::VU; ++i) {
-      // whole waves own V units, so this test is uniform
-      if ((C::VUNITS % C::NT != 0) && (wave * 64 + i * C::NT >= C::VUNITS)) continue;
-      const int u = tid + i * C::NT;
-      const int kg = u % (BC / 4);
-      const int dc = u / (BC / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + 4 * kg + r;
-        const __bf16* src = Vh + (size_t)key * D + dc * 8;
-        if (full)
-          vreg[i][r] = *reinterpret_cast<const u32x4*>(src);
-        else
-          vreg[i][r] = key < kv_len ? *reinterpret_cast<const u32x4*>(src) : u32x4{};
-      }
-    }
-  };
-
-  auto store_tile = [&](int kbuf, int vbuf) FA_INLINE {
-#pragma unroll
-    for (int i = 0; i < C::KU; ++i) {
-      const int u = tid + i * C::NT;
-      if ((C::KUNITS % C::NT != 0) && u >= C::KUNITS) continue;
-      const int r = u / (D / 8);
-      const int c8 = u % (D / 8);
-      *reinterpret_cast<u32x4*>(&Ks[kbuf][r * C::KPITCH + c8 * 8]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::VU; ++i) {
-      if ((C::VUNITS % C::NT != 0) && (wave * 64 + i * C::NT >= C::VUNITS)) continue;
-      const int u = tid + i * C::NT;
-      const int kg = u % (BC / 4);
-      const int dc = u / (BC / 4);
-      // keys 4kg..4kg+3 sit at positions 16g + 4*perm(a) of each V^T row
-      const int pos = 16 * (kg >> 2) + 4 * (((kg & 1) << 1) | ((kg >> 1) & 1));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int w = j >> 1;
-        const int sh = (j & 1) * 16;
-        u32x2 pk;
-        pk[0] = ((vreg[i][0][w] >> sh) & 0xffffu) | (((vreg[i][1][w] >> sh) & 0xffffu) << 16);
-        pk[1] = ((vreg[i][2][w] >> sh) & 0xffffu) | (((vreg[i][3][w] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2*>(&Vt[vbuf][(dc * 8 + j) * C::VPITCH + pos]) = pk;
-      }
+    for (int j = 0; j < kBlksPerWave; ++j) {
+      const int blk = wave * kBlksPerWave + j;
+      const bool is_k = blk < kBlksPerTensor;
+      const int rb = is_k ? blk : blk - kBlksPerTensor;
+      __bf16* dst = (is_k ? Ks[kbuf] : Vs[vslot]) + rb * kRowsPerBlk * D;
+      lds_dma16(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D * 2);
     }
   };
-
 
   f32x16 sacc[C::NCB][QB];
   bf16x8 pf[C::NG][QB];
@@ -241,10 +217,11 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   constexpr int kPre = FA_FWD_PREFETCH;
   auto stage_S = [&](int kbuf) FA_INLINE {
     constexpr int NF = C::KS * C::NCB;   // fragments per tile, ordered (ks, c)
-    const __bf16* kbase = &Ks[kbuf][l32 * C::KPITCH + hi * 8];
     auto kfrag = [&](int f) FA_INLINE {
       const int ks = f / C::NCB, c = f % C::NCB;
-      return *reinterpret_cast<const bf16x8*>(kbase + c * 32 * C::KPITCH + ks * 16);
+      const int row = c * 32 + l32;
+      return *reinterpret_cast<const bf16x8*>(
+          &Ks[kbuf][row * D + ((2 * ks + hi) ^ row_swizzle<D>(row)) * 8]);
     };
     bf16x8 ring[kPre];
 #pragma unroll
@@ -276,11 +253,22 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   // O^T += V^T(t) P^T(t), V^T fragments prefetched the same way
   auto stage_PV = [&](int vbuf) FA_INLINE {
     constexpr int NF = C::NG * C::NDB;   // fragments per tile, ordered (g, db)
-    const __bf16* vbase = &Vt[vbuf][l32 * C::VPITCH + hi * 8];
+    // A fragment of V^T for keys {16g + 4hi + 0..3, 16g + 8 + 4hi + 0..3}
+    // (the order of the P^T fragment) and features 32 db + l32: two
+    // transposing reads of the row-major V tile
+    const int ts = lane & 15;
+    const int tcol = ((lane >> 4) & 1) * 16 + 4 * (ts & 3);
     auto vfrag = [&](int f) FA_INLINE {
       const int g = f / C::NDB, db = f % C::NDB;
-      return *reinterpret_cast<const bf16x8*>(vbase + db * 32 * C::VPITCH + g * 16);
+      const int r0 = 16 * g + 4 * hi + (ts >> 2);
+      const int r1 = r0 + 8;
+      const int col = db * 32 + tcol;
+      const __bf16* vb = Vs[vbuf];
+      const s16x4 lo = read_tr16(vb + r0 * D + (((col >> 5) ^ seg_swizzle<D>(r0)) << 5) + (col & 31));
+      const s16x4 up = read_tr16(vb + r1 * D + (((col >> 5) ^ seg_swizzle<D>(r1)) << 5) + (col & 31));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
     };
+    constexpr int kReadsPerFrag = 2;
     bf16x8 ring[kPre];
 #pragma unroll
     for (int f = 0; f < kPre && f < NF; ++f) ring[f] = vfrag(f);
@@ -293,11 +281,11 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma_bf16(vf, pf[g][qb], oacc[db][qb]);
     }
 #if FA_FWD_SCHED >= 2
-    __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kPre * kReadsPerFrag, 0);
 #pragma unroll
     for (int f = 0; f < NF - kPre; ++f) {
       __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerFrag, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kPre * QB, 0);
 #endif
@@ -364,8 +352,8 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   };
 
   if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0, 0);
+    issue_tile(0, 0, 0);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -374,7 +362,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     constexpr bool kLag = decltype(lag_tag)::value;
     for (int kt = 0; kt < n_kt; ++kt) {
       const int kbuf = kt & 1;
-      if (kt + 1 < n_kt) load_tile(kt + 1);
+      if (kt + 1 < n_kt) issue_tile(kt + 1, kbuf ^ 1, (kt + 1) % kVSlots);
       if (kLag) {
         // second group: P(t-1) V(t-1), then S(t) and softmax(t)
         if (kt >= 1 && kt - 1 < n_act) stage_PV((kt - 1) % kVSlots);
@@ -387,8 +375,9 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         stage_softmax(kt);
         stage_PV(kt % kVSlots);
       }
-      if (kt + 1 < n_kt) store_tile(kbuf ^ 1, (kt + 1) % kVSlots);
-      __syncthreads();
+      // the next tile has landed once every wave passes here
+      wait_vmem();
+      lds_barrier();
     }
     // the second group's last P V
     if (kLag && n_kt > 0 && n_kt - 1 < n_act) stage_PV((n_kt - 1) % kVSlots);
