@@ -12,13 +12,19 @@
 //  1. row dot products D (memory-bound, one pass over O and dO);
 //  2. dK/dV: a work-group owns 128 keys of one (batch, head); a pair of waves
 //     keeps 32 keys' K and V rows in VGPRs (B operands) and their dK/dV
-//     accumulators resident, and loops over 64-row query tiles staged in LDS
-//     both row-major (A operands of S and dP) and transposed with a permuted
-//     row order (B operands of dV and dK).  S and dP come out with one key per
-//     lane, so P and dS feed the next MFMA straight from registers;
+//     accumulators resident, and loops over 64-row query tiles held row-major
+//     in LDS: 16-row fragments are the A operands of S and dP, and
+//     transposing reads (ds_read_b64_tr_b16) of the same tile give the B
+//     operands of dV and dK with the rows in the order of the P fragment.  S
+//     and dP come out with one key per lane, so P and dS feed the next MFMA
+//     straight from registers;
 //  3. dQ: a work-group owns query rows (like the forward) and loops over key
 //     tiles; S^T and dP^T come out with one query per lane, so LSE_i and D_i
-//     are one register each, and dS^T feeds dQ^T = K^T dS^T from registers.
+//     are one register each, and dS^T feeds dQ^T = K^T dS^T from registers,
+//     with K^T read transposed from the row-major K tile.
+// Tiles go from global memory straight into LDS (buffer loads with an LDS
+// destination) one tile ahead, so no staging registers and no transposed
+// copies exist; barriers inside the loops wait only for LDS traffic.
 // Kernels 2 and 3 recompute S and P each, so the backward executes 14 N^2 d
 // flops per head (7 contractions) for the 10 N^2 d it is credited with.
 
@@ -38,31 +44,6 @@
 namespace fa {
 
 namespace {
-
-// Position of element (4*grp + r) of a 4-element group inside the permuted
-// order used for transposed LDS copies: within each 16-element group the
-// middle two 4-element chunks are swapped, so that the 8 elements a lane
-// feeds into one 32x32x16 MFMA (rows 16u + 8*(i/4) + 4*hi + i%4 of a C tile)
-// are contiguous.
-// (The chunk swap exchanges the two low bits of the group index.)
-__device__ __forceinline__ int perm_pos(int grp) {
-  return 16 * (grp >> 2) + 4 * (((grp & 1) << 1) | ((grp >> 1) & 1));
-}
-
-// Write 4 rows x 8 features (four 16-byte row chunks) transposed into a
-// [feature][row] LDS array at column `pos`.
-__device__ __forceinline__ void store_transposed(__bf16* dst, int pitch, int feat0, int pos,
-                                                 const u32x4 (&rows)[4]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int w = j >> 1;
-    const int sh = (j & 1) * 16;
-    u32x2 pk;
-    pk[0] = ((rows[0][w] >> sh) & 0xffffu) | (((rows[1][w] >> sh) & 0xffffu) << 16);
-    pk[1] = ((rows[2][w] >> sh) & 0xffffu) | (((rows[3][w] >> sh) & 0xffffu) << 16);
-    *reinterpret_cast<u32x2*>(dst + (feat0 + j) * pitch + pos) = pk;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // 1. D_i = sum_t dO_it O_it (fp32), one row per D/8 threads
@@ -100,7 +81,10 @@ void fa_bwd_rowdot_kernel(const __bf16* __restrict__ O, const __bf16* __restrict
 // area.  Then each wave accumulates dV = P^T dO and dK = dS^T Q for all 64
 // rows but only its half of the head dimension.  Per wave this halves the
 // dK/dV accumulators, so a wave fits in 256 VGPRs and two waves share each
-// SIMD, without any duplicated MFMA work.
+// SIMD, without any duplicated MFMA work.  (Running the pairs' two halves of
+// the work half a tile apart, so that one wave's exponentials overlap the
+// other's MFMAs, measured slower: the accumulators held across the extra
+// barrier did not fit without spills.)
 // ---------------------------------------------------------------------------
 template <int D, int BQ>
 struct DkdvPairCfg {
@@ -111,11 +95,8 @@ struct DkdvPairCfg {
   static constexpr int NG = BQ / 16;       // 16-query groups per tile
   static constexpr int NDB = D / 32;
   static constexpr int HDB = NDB / 2;      // 32-feature blocks per wave (its half)
-  static constexpr int TPITCH = BQ + 8;
-  static constexpr int UNITS = (BQ / 4) * (D / 8);  // 4-row x 8-feature units per tensor
   static_assert(BQ == 64, "two 32-row halves per tile");
   static_assert(NDB % 2 == 0, "head dimension splits in two halves of 32-feature blocks");
-  static_assert(2 * UNITS <= NT, "one staging unit per thread");
 };
 
 template <int D, int BQ>
@@ -130,8 +111,6 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
   using C = DkdvPairCfg<D, BQ>;
   __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) __bf16 dOs[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Qt[D * C::TPITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 dOt[D * C::TPITCH];
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
   // P and dS fragments handed to the partner wave: [wave][slot][lane]
@@ -192,7 +171,21 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
   // that the copy has a whole iteration to land.  The buffer descriptors
   // cover exactly one head, so rows at or past N read as zeros.  Each lane
   // fetches the global 16-byte chunk that the XOR swizzle places at its LDS
-  // position.  The transposed copies are then built from the row-major ones.
+  // position; the tile is read both as 16-row fragments and by transposing
+  // reads, so it takes the swizzle that serves both.
+  auto kSwz = [](int row) FA_INLINE { return tile_swizzle<D>(row); };
+  // B fragment of dO (or Q) for query rows {16g + 4hi + 0..3, 16g + 8 + 4hi
+  // + 0..3} (the order of the P^T fragment) and features 32 db + l32
+  const int ts = lane & 15;
+  const int tcol = ((lane >> 4) & 1) * 16 + 4 * (ts & 3);
+  auto colfrag = [&](const __bf16* tile, int g, int db) FA_INLINE {
+    const int r0 = 16 * g + 4 * hi + (ts >> 2);
+    const int r1 = r0 + 8;
+    const int col = db * 32 + tcol;
+    const s16x4 lo = read_tr16(tile + r0 * D + ((col >> 3) ^ tile_swizzle<D>(r0)) * 8 + (col & 7));
+    const s16x4 up = read_tr16(tile + r1 * D + ((col >> 3) ^ tile_swizzle<D>(r1)) * 8 + (col & 7));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   constexpr int kRowsPerBlk = 1024 / (D * 2);
   constexpr int kBlksPerTensor = BQ / kRowsPerBlk;
   constexpr int kBlksPerWave = 2 * kBlksPerTensor / C::NW;
@@ -220,7 +213,7 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
       const bool is_q = blk < kBlksPerTensor;
       const int rb = is_q ? blk : blk - kBlksPerTensor;
       const int row = rb * kRowsPerBlk + blk_row;
-      const int chunk = blk_cpos ^ row_swizzle<D>(row);
+      const int chunk = blk_cpos ^ kSwz(row);
       const int voff = (qt0 + row) * (D * 2) + chunk * 16;
       __bf16* dst = (is_q ? Qs[buf] : dOs[buf]) + rb * kRowsPerBlk * D;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_q ? q_rsrc : o_rsrc, dst, 16, voff, 0, 0, 0);
@@ -233,32 +226,13 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
       Ds[buf][tid] = dreg;
     }
   };
-  // transposed copies of the row-major tile in `buf`: threads [0, UNITS)
-  // handle Q, [UNITS, 2 UNITS) dO, one 4-row x 8-feature unit each
-  const bool stager = tid < 2 * C::UNITS;
-  const bool stage_q = tid < C::UNITS;
-  const int su = tid % C::UNITS;
-  const int sqg = su % (BQ / 4);
-  const int sdc = su / (BQ / 4);
-  auto transpose_tile = [&](int buf) FA_INLINE {
-    if (stager) {
-      const __bf16* rm = stage_q ? Qs[buf] : dOs[buf];
-      u32x4 rows[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * sqg + r;
-        rows[r] = *reinterpret_cast<const u32x4*>(&rm[row * D + (sdc ^ row_swizzle<D>(row)) * 8]);
-      }
-      store_transposed(stage_q ? Qt : dOt, C::TPITCH, sdc * 8, perm_pos(sqg), rows);
-    }
-  };
+
 
   if (n_qt > 0) {
     issue_tile(0, 0);
     store_stats(0);
     wait_vmem();
     __syncthreads();
-    transpose_tile(0);
     __syncthreads();
   }
 
@@ -275,7 +249,7 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
       // ---- phase 1: S and dP for this wave's 32 query rows (one key per lane)
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       const int arow = 32 * half + l32;
-      const int asw = row_swizzle<D>(arow);
+      const int asw = kSwz(arow);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const int ro = arow * D + ((2 * ks + hi) ^ asw) * 8;
@@ -333,9 +307,8 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
 #pragma unroll
         for (int j = 0; j < C::HDB; ++j) {
           const int db = half * C::HDB + j;
-          const int to = (db * 32 + l32) * C::TPITCH + g * 16 + hi * 8;
-          const bf16x8 ob = *reinterpret_cast<const bf16x8*>(&dOt[to]);
-          const bf16x8 qbv = *reinterpret_cast<const bf16x8*>(&Qt[to]);
+          const bf16x8 ob = colfrag(dOs[buf], g, db);
+          const bf16x8 qbv = colfrag(Qs[buf], g, db);
           dvacc[j] = mfma_bf16(pfrag, ob, dvacc[j]);
           dkacc[j] = mfma_bf16(dsfrag, qbv, dkacc[j]);
         }
@@ -344,7 +317,6 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
     // the next tile's row-major copy has landed once every wave passes here
     wait_vmem();
     lds_barrier();
-    if (more) transpose_tile(buf ^ 1);
   }
 
   // ---- write dK = scale * acc, dV = acc for this wave's feature half
@@ -373,9 +345,6 @@ struct DqCfg {
   static constexpr int NCB = BC / 32;
   static constexpr int NG = BC / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int TPITCH = BC + 8;
-  static constexpr int UNITS = (BC / 4) * (D / 8);
-  static constexpr int UPT = (UNITS + NT - 1) / NT;
 };
 
 template <int D, int NW, int BC>
@@ -387,11 +356,9 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                       const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
                       int causal, __bf16* __restrict__ dQ, int B, int H, int N, int n_qtiles) {
   using C = DqCfg<D, NW, BC>;
-  // row-major K and V tiles in three slots (read, being transposed, being
-  // loaded), transposed K in two
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[3][BC * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[3][BC * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Kt[2][D * C::TPITCH];
+  // row-major K and V tiles in two slots (one read, one being loaded)
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -439,65 +406,62 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 
   // Staging.  Row-major K and V tiles are copied straight from global memory
   // into LDS (lane l of a wave fills bytes [16 l, 16 l + 16) of a 1 KiB
-  // block; each lane fetches the global chunk that the XOR swizzle places
-  // there), two tiles ahead.  The buffer descriptors cover exactly one head,
-  // so keys at or past N read as zeros; keys in [L_b, N) are masked.  Tile
-  // t+1's transposed K copy is built from its row-major copy during
-  // iteration t, so one barrier per tile suffices.
+  // block; each lane fetches the global chunk that the tile's XOR swizzle
+  // places there), one tile ahead.  The buffer descriptors cover exactly one
+  // head, so keys at or past N read as zeros; keys in [L_b, N) are masked.
+  // K is read both as 16-row fragments (S^T = K Q^T) and by transposing
+  // reads (the A operand of dQ^T = K^T dS^T), so no transposed copy exists.
   constexpr int kRowsPerBlk = 1024 / (D * 2);
   constexpr int kBlksPerTensor = BC / kRowsPerBlk;
   constexpr int kBlksPerWave = 2 * kBlksPerTensor / NW;
   static_assert(2 * kBlksPerTensor % NW == 0 && kBlksPerWave >= 1, "whole 1 KiB blocks per wave");
-  static_assert(C::UNITS <= C::NT, "one transposition unit per thread");
   const int head_bytes = N * D * 2;
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Kh), 0, head_bytes, kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Vh), 0, head_bytes, kBufferRsrcWord3);
-  const int blk_row = lane / (D / 8);
-  const int blk_cpos = lane % (D / 8);
+  const u32x4 k_rsrc = buffer_rsrc_words(Kh, (uint32_t)head_bytes);
+  const u32x4 v_rsrc = buffer_rsrc_words(Vh, (uint32_t)head_bytes);
+  // per-lane byte offsets inside a tile, computed once; the tile's position
+  // goes in the scalar offset (see fa_fwd.hip: copies issued through the
+  // builtin made the next transposing read wait for the whole copy)
+  int voff[kBlksPerWave];
+#pragma unroll
+  for (int j = 0; j < kBlksPerWave; ++j) {
+    const int blk = wave * kBlksPerWave + j;
+    const int rb = blk < kBlksPerTensor ? blk : blk - kBlksPerTensor;
+    const int row = rb * kRowsPerBlk + lane / (D / 8);
+    voff[j] = row * (D * 2) + ((lane % (D / 8)) ^ tile_swizzle<D>(row)) * 16;
+  }
   auto issue_tile = [&](int kt, int slot) FA_INLINE {
 #pragma unroll
     for (int j = 0; j < kBlksPerWave; ++j) {
       const int blk = wave * kBlksPerWave + j;
       const bool is_k = blk < kBlksPerTensor;
       const int rb = is_k ? blk : blk - kBlksPerTensor;
-      const int row = rb * kRowsPerBlk + blk_row;
-      const int chunk = blk_cpos ^ row_swizzle<D>(row);
-      const int voff = (kt * BC + row) * (D * 2) + chunk * 16;
       __bf16* dst = (is_k ? Ks[slot] : Vs[slot]) + rb * kRowsPerBlk * D;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_k ? k_rsrc : v_rsrc, dst, 16, voff, 0, 0, 0);
+      lds_dma16(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D * 2);
     }
   };
-  const int tkg = tid % (BC / 4);
-  const int tdc = tid / (BC / 4);
-  auto transpose_tile = [&](int slot, int tbuf) FA_INLINE {
-    if (tid < C::UNITS) {
-      u32x4 rows[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * tkg + r;
-        rows[r] = *reinterpret_cast<const u32x4*>(
-            &Ks[slot][row * D + (tdc ^ row_swizzle<D>(row)) * 8]);
-      }
-      store_transposed(Kt[tbuf], C::TPITCH, tdc * 8, perm_pos(tkg), rows);
-    }
+  // A fragment of K^T for keys {16g + 4hi + 0..3, 16g + 8 + 4hi + 0..3} (the
+  // order of the dS^T fragment) and features 32 db + l32
+  const int ts = lane & 15;
+  const int tcol = ((lane >> 4) & 1) * 16 + 4 * (ts & 3);
+  auto colfrag = [&](const __bf16* tile, int g, int db) FA_INLINE {
+    const int r0 = 16 * g + 4 * hi + (ts >> 2);
+    const int r1 = r0 + 8;
+    const int col = db * 32 + tcol;
+    const s16x4 lo = read_tr16(tile + r0 * D + ((col >> 3) ^ tile_swizzle<D>(r0)) * 8 + (col & 7));
+    const s16x4 up = read_tr16(tile + r1 * D + ((col >> 3) ^ tile_swizzle<D>(r1)) * 8 + (col & 7));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
+  wait_vmem();   // the query rows and their statistics
   if (n_kt > 0) {
     issue_tile(0, 0);
-    if (n_kt > 1) issue_tile(1, 1);
     wait_vmem();
-    __syncthreads();
-    transpose_tile(0, 0);
     __syncthreads();
   }
 
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int slot = kt % 3;
-    const int buf = kt & 1;
-    if (kt + 2 < n_kt) issue_tile(kt + 2, (kt + 2) % 3);
-    if (kt + 1 < n_kt) transpose_tile((kt + 1) % 3, buf ^ 1);
+    const int slot = kt & 1;
+    if (kt + 1 < n_kt) issue_tile(kt + 1, slot ^ 1);
     const int key0 = kt * BC;
     const bool wave_active = (qw0 < N) && (!causal || key0 <= qw0 + 31);
     if (wave_active) {
@@ -513,7 +477,7 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 #pragma unroll
         for (int c = 0; c < C::NCB; ++c) {
           const int arow = c * 32 + l32;
-          const int ro = arow * D + ((2 * ks + hi) ^ row_swizzle<D>(arow)) * 8;
+          const int ro = arow * D + ((2 * ks + hi) ^ tile_swizzle<D>(arow)) * 8;
           const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[slot][ro]);
           const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[slot][ro]);
           sacc[c] = mfma_bf16(ka, qf[ks], sacc[c]);
@@ -538,13 +502,10 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       for (int g = 0; g < C::NG; ++g)
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-              &Kt[buf][(db * 32 + l32) * C::TPITCH + g * 16 + hi * 8]);
-          dqacc[db] = mfma_bf16(ka, dsb[g], dqacc[db]);
+          dqacc[db] = mfma_bf16(colfrag(Ks[slot], g, db), dsb[g], dqacc[db]);
         }
     }
-    // tile t+2 has landed and tile t+1's transposed copy is complete once
-    // every wave passes here
+    // the next tile has landed once every wave passes here
     wait_vmem();
     lds_barrier();
   }

@@ -140,6 +140,20 @@ __device__ __forceinline__ int row_swizzle(int row) {
     return (row ^ (row >> 2)) & (D / 8 - 1);
 }
 
+// Row-major tiles read both ways - 16-row fragments by ds_read_b128 and
+// column fragments by transposing reads (16 lanes: 4 consecutive rows x 32
+// bytes; a wave half: 4 rows x 64 bytes, served as 32 lanes per cycle) -
+// XOR their 16-byte chunk index with a linear map of the row bits that is
+// one-to-one on every lane group of both access kinds (searched exhaustively
+// under the measured grouping rules).
+template <int D>
+__device__ __forceinline__ int tile_swizzle(int row) {
+  if constexpr (D == 128)
+    return ((row & 3) << 2) ^ ((row >> 2) & 3) ^ (((row >> 4) & 1) * 3);
+  else
+    return (((row >> 1) & 1) << 2) ^ ((row >> 3) & 1) ^ (((row >> 4) & 1) << 1);
+}
+
 // Row-major tiles read only by transposing reads (ds_read_b64_tr_b16) swizzle
 // their 64-byte segments instead: 16 lanes of such a read fetch 4 consecutive
 // rows x 32 bytes and a wave half 4 rows x 64 bytes; XOR-ing the segment
