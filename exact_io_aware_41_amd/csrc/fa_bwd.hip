@@ -258,6 +258,9 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
         sacc = mfma_bf16(qa, kf[ks], sacc);
         pacc = mfma_bf16(oa, vf[ks], pacc);
       }
+      // this lane's key is visible from tile row 32 half + 8 a4 + 4 hi + e iff
+      // 32 half + 8 a4 + e >= first_vis
+      const int first_vis = my_key >= kv_len ? BQ : (causal ? my_key - qt0 - 4 * hi : -BQ);
       auto p_and_ds = [&](auto masked_tag) FA_INLINE {
         constexpr bool kMasked = decltype(masked_tag)::value;
 #pragma unroll
@@ -269,11 +272,7 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * a4 + e;
             float p = fast_exp2(__builtin_fmaf(sacc[v], scale_log2, -lq[e]));
-            if (kMasked) {
-              const int query = qt0 + r0 + e;
-              const bool vis = my_key < kv_len && (!causal || my_key <= query);
-              p = vis ? p : 0.f;
-            }
+            if (kMasked) p = (32 * half + 8 * a4 + e >= first_vis) ? p : 0.f;
             pa[v >> 3][v & 7] = to_bf16(p);
             dsa[v >> 3][v & 7] = to_bf16(p * (pacc[v] - dq[e]));
           }
@@ -483,18 +482,26 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           sacc[c] = mfma_bf16(ka, qf[ks], sacc[c]);
           pacc[c] = mfma_bf16(va, of[ks], pacc[c]);
         }
-      const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0);
+      // only tiles crossing the key length or the wave's diagonal are masked:
+      // key key0 + 32c + 4hi + p, p = 8(v/4) + v%4, is visible iff it is at
+      // most min(L - 1, this lane's query); S = -inf gives P = 0
+      if ((key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0)) {
+        const int lim = (causal ? min(kv_len - 1, qrow) : kv_len - 1) - key0 - 4 * hi;
+#pragma unroll
+        for (int c = 0; c < C::NCB; ++c) {
+          const uint32_t vis = prefix_bits(lim - 32 * c);
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            sacc[c][v] = keep_if_bit(sacc[c][v], vis, 8 * (v >> 2) + (v & 3), kNegInf);
+        }
+      }
+      // dS^T = P^T o (dP^T - rowdot)
       bf16x8 dsb[C::NG];
 #pragma unroll
       for (int c = 0; c < C::NCB; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float p = fast_exp2(__builtin_fmaf(sacc[c][v], scale_log2, -lse2));
-          if (need_mask) {
-            const int key = key0 + c * 32 + c_row(v, lane);
-            const bool vis = key < kv_len && (!causal || key <= qrow);
-            if (!vis) p = 0.f;
-          }
+          const float p = fast_exp2(__builtin_fmaf(sacc[c][v], scale_log2, -lse2));
           dsb[2 * c + (v >> 3)][v & 7] = to_bf16(p * (pacc[c][v] - drow));
         }
       // ---- dQ^T += K^T dS^T

@@ -50,6 +50,21 @@ __device__ __forceinline__ int c_row(int v, int lane) {
   return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
 
+// Bits p of a 32-bit word set iff p <= rel (none for rel < 0, all for
+// rel >= 31): the visible positions of a run of 32 keys.
+__device__ __forceinline__ uint32_t prefix_bits(int rel) {
+  const int r = min(max(rel + 1, 0), 32);
+  return (uint32_t)((1ull << r) - 1ull);
+}
+
+// x where bit `pos` (a constant) of `bits` is set, `other` elsewhere, by bit
+// operations only (v_bfe_i32 gives 0 or -1, then a bitwise select): unlike a
+// compare per element, this holds no lane masks in scalar registers.
+__device__ __forceinline__ float keep_if_bit(float x, uint32_t bits, int pos, float other) {
+  const int m = __builtin_amdgcn_sbfe((int)bits, pos, 1);
+  return __int_as_float((__float_as_int(x) & m) | (__float_as_int(other) & ~m));
+}
+
 // max / sum of a value with the same value in the other half of the wave
 // (lane l and lane l^32).  v_permlane32_swap(x, x) leaves (own, other) in the
 // lower half and (other, own) in the upper half, so one max/add finishes it.

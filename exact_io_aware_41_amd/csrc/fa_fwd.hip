@@ -301,13 +301,14 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       for (int c = 0; c < C::NCB; ++c)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
+          // key key0 + 32c + 4hi + p, p = 8(v/4) + v%4, is visible iff it is
+          // at most min(L - 1, query): bit p of a per-lane prefix mask
           const int query = qw0 + qb * 32 + l32;
+          const int lim = (causal ? min(kv_len - 1, query) : kv_len - 1) - key0 - 4 * hi;
+          const uint32_t vis = prefix_bits(lim - 32 * c);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = key0 + c * 32 + c_row(v, lane);
-            const bool vis = key < kv_len && (!causal || key <= query);
-            if (!vis) sacc[c][qb][v] = kNegInf;
-          }
+          for (int v = 0; v < 16; ++v)
+            sacc[c][qb][v] = keep_if_bit(sacc[c][qb][v], vis, 8 * (v >> 2) + (v & 3), kNegInf);
         }
     }
     bool scale_o = false;
