@@ -24,9 +24,12 @@
 //    P^T fragment; no transposed copy of V is ever written.  Fragments are
 //    read several MFMAs ahead of use.  The loop's barriers wait only for LDS
 //    traffic, so the copy of the next tile stays in flight across them.
-//  * the waves of a SIMD run out of phase: waves 4..7 multiply P(t-1) V(t-1)
-//    before computing S(t), while waves 0..3 compute S(t) first, so one
-//    wave's MFMAs overlap the other's softmax.
+//  * the waves of a SIMD run out of phase: waves 4..7 take the softmax of
+//    tile t-1 and multiply P(t-1) V(t-1) before computing S(t), while waves
+//    0..3 compute S(t) first, so one wave's MFMAs overlap the other's softmax.
+//    Waves 0..3 issue their copies of the next tile between their S(t)
+//    MFMAs, so the copies of all eight waves do not queue up at once after
+//    the barrier.
 //  * scores are handled in the log2 domain: x = s * scale * log2(e), so the
 //    exponentials are single v_exp_f32 instructions.  The reference maximum
 //    only moves when a tile's maximum exceeds it by more than 2^8, so the O
@@ -97,10 +100,11 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
                         float* __restrict__ LSE, int B, int H, int N, int n_qtiles) {
   using C = FwdBf16Cfg<D, QB, NW, BC>;
   // Two groups of NW/2 waves; the waves of a SIMD (w and w + NW/2) sit in
-  // different groups.  The second group runs one stage behind: it multiplies
-  // P(t-1) V(t-1) before computing S(t), so while one wave of a SIMD is in its
-  // MFMA phase the other is in its softmax phase.  V therefore lives in a
-  // three-slot ring (group 2 still reads V(t-1) while V(t+1) is written).
+  // different groups.  The second group runs one stage behind: it takes the
+  // softmax of tile t-1 and multiplies P(t-1) V(t-1) before computing S(t),
+  // so while one wave of a SIMD is in its MFMA phase the other is in its
+  // softmax phase.  V therefore lives in a three-slot ring (group 2 still
+  // reads V(t-1) while V(t+1) is written).
   constexpr bool kPingPong = (NW >= 8);
   constexpr int kVSlots = kPingPong ? 3 : 2;
   // K row-major with XOR-swizzled 16-byte chunks, V row-major with swizzled
@@ -209,13 +213,27 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     }
   };
 
+  // one of this wave's copies of tile kt (block j of its share)
+  auto issue_block = [&](int kt, int kbuf, int vslot, int j) FA_INLINE {
+    const int blk = wave * kBlksPerWave + j;
+    const bool is_k = blk < kBlksPerTensor;
+    const int rb = is_k ? blk : blk - kBlksPerTensor;
+    __bf16* dst = (is_k ? Ks[kbuf] : Vs[vslot]) + rb * kRowsPerBlk * D;
+    lds_dma16(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D * 2);
+  };
+  auto no_dma = [](int) FA_INLINE {};
+
   f32x16 sacc[C::NCB][QB];
   bf16x8 pf[C::NG][QB];
 
   // S^T(t) = K(t) Q^T.  The K fragments are read from LDS kPre reads ahead of
   // the MFMA that consumes them, so LDS latency overlaps the MFMA pipeline.
   constexpr int kPre = FA_FWD_PREFETCH;
-  auto stage_S = [&](int kbuf) FA_INLINE {
+  // `dma(j)` issues this wave's copy j of the next tile; the stage spreads the
+  // copies over its MFMAs, one every NF / kBlksPerWave
+  constexpr int kDmaEvery = (C::KS * C::NCB) / kBlksPerWave;
+  static_assert(kDmaEvery >= 1 && kDmaEvery * kBlksPerWave == C::KS * C::NCB, "copies per stage");
+  auto stage_S = [&](int kbuf, auto&& dma) FA_INLINE {
     constexpr int NF = C::KS * C::NCB;   // fragments per tile, ordered (ks, c)
     auto kfrag = [&](int f) FA_INLINE {
       const int ks = f / C::NCB, c = f % C::NCB;
@@ -237,6 +255,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       if (f + kPre < NF) ring[f % kPre] = kfrag(f + kPre);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sacc[c][qb] = mfma_bf16(kf, qf[qb][ks], sacc[c][qb]);
+      if (f % kDmaEvery == 0) dma(f / kDmaEvery);
     }
 #if FA_FWD_SCHED
     // keep the fragment reads kPre ahead of the MFMAs that consume them
@@ -251,7 +270,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   };
 
   // O^T += V^T(t) P^T(t), V^T fragments prefetched the same way
-  auto stage_PV = [&](int vbuf) FA_INLINE {
+  auto stage_PV = [&](int vbuf, auto&& dma) FA_INLINE {
     constexpr int NF = C::NG * C::NDB;   // fragments per tile, ordered (g, db)
     // A fragment of V^T for keys {16g + 4hi + 0..3, 16g + 8 + 4hi + 0..3}
     // (the order of the P^T fragment) and features 32 db + l32: two
@@ -279,6 +298,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       if (f + kPre < NF) ring[f % kPre] = vfrag(f + kPre);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma_bf16(vf, pf[g][qb], oacc[db][qb]);
+      if (f % kDmaEvery == 0) dma(f / kDmaEvery);
     }
 #if FA_FWD_SCHED >= 2
     __builtin_amdgcn_sched_group_barrier(0x100, kPre * kReadsPerFrag, 0);
@@ -363,25 +383,42 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     constexpr bool kLag = decltype(lag_tag)::value;
     for (int kt = 0; kt < n_kt; ++kt) {
       const int kbuf = kt & 1;
-      if (kt + 1 < n_kt) issue_tile(kt + 1, kbuf ^ 1, (kt + 1) % kVSlots);
+      // the copies of tile kt+1 ride inside this iteration's first MFMA stage
+      // (S for the first group, P V for the second) instead of all leaving at
+      // once after the barrier, where they queue behind each other.  They are
+      // issued unconditionally (a branch between the MFMAs costs more): in the
+      // last iteration they fill slots nobody reads again, from rows past the
+      // head (zeros) or past the work-group's last key.
+      auto dma = [&](int j) FA_INLINE { issue_block(kt + 1, kbuf ^ 1, (kt + 1) % kVSlots, j); };
+      auto dma_all = [&]() FA_INLINE {
+#pragma unroll
+        for (int j = 0; j < kBlksPerWave; ++j) dma(j);
+      };
       if (kLag) {
-        // second group: P(t-1) V(t-1), then S(t) and softmax(t)
-        if (kt >= 1 && kt - 1 < n_act) stage_PV((kt - 1) % kVSlots);
-        if (kt < n_act) {
-          stage_S(kbuf);
-          stage_softmax(kt);
+        // second group: softmax(t-1) and P(t-1) V(t-1), then S(t); its
+        // softmax runs while the first group computes S(t)
+        dma_all();
+        if (kt >= 1 && kt - 1 < n_act) {
+          stage_softmax(kt - 1);
+          stage_PV((kt - 1) % kVSlots, no_dma);
         }
+        if (kt < n_act) stage_S(kbuf, no_dma);
       } else if (kt < n_act) {
-        stage_S(kbuf);
+        stage_S(kbuf, dma);
         stage_softmax(kt);
-        stage_PV(kt % kVSlots);
+        stage_PV(kt % kVSlots, no_dma);
+      } else {
+        dma_all();
       }
       // the next tile has landed once every wave passes here
       wait_vmem();
       lds_barrier();
     }
-    // the second group's last P V
-    if (kLag && n_kt > 0 && n_kt - 1 < n_act) stage_PV((n_kt - 1) % kVSlots);
+    // the second group's last softmax and P V
+    if (kLag && n_kt > 0 && n_kt - 1 < n_act) {
+      stage_softmax(n_kt - 1);
+      stage_PV((n_kt - 1) % kVSlots, no_dma);
+    }
   };
   if (lagging)
     run(std::true_type{});
