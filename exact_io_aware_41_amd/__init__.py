@@ -22,7 +22,7 @@ import os
 
 __all__ = [
     "FA_SUCCESS", "FA_ERROR_INVALID_VALUE", "FA_ERROR_UNSUPPORTED", "FA_ERROR_LAUNCH",
-    "FA_DTYPE_F32", "FA_DTYPE_BF16", "EXPORTED_SYMBOLS",
+    "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "EXPORTED_SYMBOLS",
     "FAError", "FALibraryMissing", "LIB_PATH", "load_library",
     "fa_abi_version", "fa_status_string", "fa_forward", "fa_backward",
     "fa_backward_workspace_size", "fa_backward_preprocess", "fa_backward_dkdv",
@@ -36,6 +36,7 @@ FA_ERROR_UNSUPPORTED = 2
 FA_ERROR_LAUNCH = 3
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
+FA_DTYPE_F16 = 2
 
 EXPORTED_SYMBOLS = ("fa_abi_version", "fa_status_string", "fa_forward",
                     "fa_backward_workspace_size", "fa_backward", "fa_backward_preprocess",
@@ -164,6 +165,8 @@ def _dtype_code(t):
     import torch
     if t.dtype == torch.bfloat16:
         return FA_DTYPE_BF16
+    if t.dtype == torch.float16:
+        return FA_DTYPE_F16
     if t.dtype == torch.float32:
         return FA_DTYPE_F32
     raise FAError(FA_ERROR_UNSUPPORTED, f"dtype {t.dtype}")

@@ -16,23 +16,28 @@ constexpr long long kMaxGrid = 0x7fffffffLL;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool is_half(fa_dtype dtype) { return dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16; }
+
 bool fwd_supported(fa_dtype dtype, int d) {
-  if (dtype == FA_DTYPE_F32) return d == 64 || d == 128;
-  if (dtype == FA_DTYPE_BF16) return d == 64 || d == 128;
-  return false;
+  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128);
 }
 
-bool bwd_supported(fa_dtype dtype, int d) { return dtype == FA_DTYPE_BF16 && (d == 64 || d == 128); }
+bool bwd_supported(fa_dtype dtype, int d) { return is_half(dtype) && (d == 64 || d == 128); }
 
 bool decode_supported(fa_dtype dtype, int d) {
-  return (dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_BF16) && (d == 64 || d == 128);
+  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128);
+}
+
+fa::Elt elt_of(fa_dtype dtype) {
+  return dtype == FA_DTYPE_BF16 ? fa::Elt::kBf16
+                                : dtype == FA_DTYPE_F16 ? fa::Elt::kF16 : fa::Elt::kF32;
 }
 
 // Longest cache a decode call accepts (parts of at most 4096 keys, at most
 // 4096 parts per row).
 constexpr int kMaxDecodeN = 4096 * 4096;
 
-bool known_dtype(fa_dtype dtype) { return dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_BF16; }
+bool known_dtype(fa_dtype dtype) { return dtype == FA_DTYPE_F32 || is_half(dtype); }
 
 // Shared size/scale/flag checks.  Returns FA_SUCCESS when the problem is
 // well formed; *empty is set when there is nothing to compute.
@@ -75,12 +80,12 @@ fa_status fa_forward(fa_dtype dtype, int B, int H, int N, int d, const void* q, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERROR_INVALID_VALUE;
   if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
-  const long long grid = dtype == FA_DTYPE_BF16 ? fa::fwd_bf16_grid(B, H, N, d)
-                                                : fa::fwd_f32_grid(B, H, N, d);
+  const long long grid = is_half(dtype) ? fa::fwd_half_grid(B, H, N, d)
+                                        : fa::fwd_f32_grid(B, H, N, d);
   if (grid > kMaxGrid) return FA_ERROR_INVALID_VALUE;
 
   fa::FwdArgs a{B, H, N, d, q, k, v, seqlens_k, scale, causal, o, lse, stream};
-  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a) : fa::launch_fwd_f32(a);
+  const hipError_t e = is_half(dtype) ? fa::launch_fwd_half(a, elt_of(dtype)) : fa::launch_fwd_f32(a);
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
@@ -108,12 +113,12 @@ fa_status fa_backward(fa_dtype dtype, int B, int H, int N, int d, const void* q,
     return FA_ERROR_INVALID_VALUE;
   if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
   if (workspace_bytes < fa_backward_workspace_size(dtype, B, H, N, d)) return FA_ERROR_INVALID_VALUE;
-  if (fa::bwd_bf16_grid(B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  if (fa::bwd_half_grid(B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
 
   fa::BwdArgs a{B,     H,       N,          d,      q,  k,  v,  o,  dout,
                 lse,   seqlens_k, scale,    causal, dq, dk, dv, static_cast<float*>(workspace),
                 stream};
-  const hipError_t e = fa::launch_bwd_bf16(a);
+  const hipError_t e = fa::launch_bwd_half(a, elt_of(dtype));
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
@@ -127,10 +132,10 @@ fa_status fa_backward_preprocess(fa_dtype dtype, int B, int H, int N, int d, con
   if (empty) return FA_SUCCESS;
   if (!o || !dout || !delta) return FA_ERROR_INVALID_VALUE;
   if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return FA_ERROR_INVALID_VALUE;
-  if (fa::bwd_bf16_grid(B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  if (fa::bwd_half_grid(B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
   fa::BwdArgs a{B, H, N, d, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, 1.f, 0,
                 nullptr, nullptr, nullptr, delta, stream};
-  return fa::launch_bwd_preprocess_bf16(a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+  return fa::launch_bwd_preprocess_half(a, elt_of(dtype)) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
 namespace {
@@ -147,7 +152,7 @@ fa_status check_bwd_phase(fa_dtype dtype, int B, int H, int N, int d, const void
       !aligned16(delta) || !aligned16(out0) || !aligned16(out1))
     return FA_ERROR_INVALID_VALUE;
   if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
-  if (fa::bwd_bf16_grid(B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  if (fa::bwd_half_grid(B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
   return FA_SUCCESS;
 }
 }  // namespace
@@ -163,7 +168,7 @@ fa_status fa_backward_dkdv(fa_dtype dtype, int B, int H, int N, int d, const voi
   fa::BwdArgs a{B,     H,         N,     d,      q,       k,  v,  nullptr, dout,
                 lse,   seqlens_k, scale, causal, nullptr, dk, dv, const_cast<float*>(delta),
                 stream};
-  return fa::launch_bwd_dkdv_bf16(a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+  return fa::launch_bwd_dkdv_half(a, elt_of(dtype)) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
 fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int N, int d, const void* q, const void* k,
@@ -177,7 +182,7 @@ fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int N, int d, const void*
   fa::BwdArgs a{B,     H,         N,     d,      q,  k,       v,       nullptr, dout,
                 lse,   seqlens_k, scale, causal, dq, nullptr, nullptr, const_cast<float*>(delta),
                 stream};
-  return fa::launch_bwd_dq_bf16(a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+  return fa::launch_bwd_dq_half(a, elt_of(dtype)) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
 size_t fa_decode_workspace_size(fa_dtype dtype, int B, int H, int N, int d) {
@@ -207,7 +212,7 @@ fa_status fa_decode(fa_dtype dtype, int B, int H, int N, int d, const void* q, c
     return FA_ERROR_INVALID_VALUE;
   fa::DecodeArgs a{B, H, N, d, q, k, v, seqlens_k, scale, o, lse,
                    static_cast<float*>(workspace), stream};
-  return fa::launch_decode(a, dtype == FA_DTYPE_BF16) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+  return fa::launch_decode(a, elt_of(dtype)) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
 fa_status fa_merge_states(fa_dtype dtype, int rows, int n_parts, int d, const float* o_parts,
@@ -221,7 +226,7 @@ fa_status fa_merge_states(fa_dtype dtype, int rows, int n_parts, int d, const fl
   if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || (lse && !aligned16(lse)))
     return FA_ERROR_INVALID_VALUE;
   if ((long long)rows > kMaxGrid) return FA_ERROR_INVALID_VALUE;
-  return fa::launch_merge(rows, n_parts, d, o_parts, lse_parts, o, lse, dtype == FA_DTYPE_BF16,
+  return fa::launch_merge(rows, n_parts, d, o_parts, lse_parts, o, lse, elt_of(dtype),
                           stream) == hipSuccess
              ? FA_SUCCESS
              : FA_ERROR_LAUNCH;

@@ -48,10 +48,13 @@ namespace {
 // ---------------------------------------------------------------------------
 // 1. D_i = sum_t dO_it O_it (fp32), one row per D/8 threads
 // ---------------------------------------------------------------------------
-template <int D>
+template <class E, int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
-void fa_bwd_rowdot_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO,
+void fa_bwd_rowdot_kernel(const typename E::T* __restrict__ O, const typename E::T* __restrict__ dO,
                           float* __restrict__ Dout, long long rows) {
+  using elt = typename E::T;
+  using elt8 = typename E::V8;
+  using elt4 = typename E::V4;
   constexpr int TPR = D / 8;  // threads per row
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = gid / TPR;
@@ -62,8 +65,11 @@ void fa_bwd_rowdot_kernel(const __bf16* __restrict__ O, const __bf16* __restrict
     const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * D + part * 8);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      acc += __uint_as_float(a[w] << 16) * __uint_as_float(b[w] << 16);
-      acc += __uint_as_float(a[w] & 0xffff0000u) * __uint_as_float(b[w] & 0xffff0000u);
+      float a0, a1, b0, b1;
+      E::unpack2(a[w], a0, a1);
+      E::unpack2(b[w], b0, b1);
+      acc += a0 * b0;
+      acc += a1 * b1;
     }
   }
 #pragma unroll
@@ -99,22 +105,25 @@ struct DkdvPairCfg {
   static_assert(NDB % 2 == 0, "head dimension splits in two halves of 32-feature blocks");
 };
 
-template <int D, int BQ>
+template <class E, int D, int BQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                             const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
+                             const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
                              const float* __restrict__ LSE, const float* __restrict__ Dlt,
                              const int32_t* __restrict__ seqlens_k, float scale,
-                             float scale_log2, int causal, __bf16* __restrict__ dK,
-                             __bf16* __restrict__ dV, int B, int H, int N, int n_ktiles) {
+                             float scale_log2, int causal, typename E::T* __restrict__ dK,
+                             typename E::T* __restrict__ dV, int B, int H, int N, int n_ktiles) {
+  using elt = typename E::T;
+  using elt8 = typename E::V8;
+  using elt4 = typename E::V4;
   using C = DkdvPairCfg<D, BQ>;
-  __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) __bf16 dOs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) elt Qs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) elt dOs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
   // P and dS fragments handed to the partner wave: [wave][slot][lane]
-  __shared__ __attribute__((aligned(16))) bf16x8 Xs[C::NW][4][64];
+  __shared__ __attribute__((aligned(16))) elt8 Xs[C::NW][4][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -130,14 +139,14 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
   const int b = bh / H;
   const int h = bh - b * H;
   const size_t head = (size_t)b * H + h;
-  const __bf16* Qh = Q + head * (size_t)N * D;
-  const __bf16* Kh = K + head * (size_t)N * D;
-  const __bf16* Vh = V + head * (size_t)N * D;
-  const __bf16* dOh = dO + head * (size_t)N * D;
+  const elt* Qh = Q + head * (size_t)N * D;
+  const elt* Kh = K + head * (size_t)N * D;
+  const elt* Vh = V + head * (size_t)N * D;
+  const elt* dOh = dO + head * (size_t)N * D;
   const float* Lh = LSE + head * (size_t)N;
   const float* Dh = Dlt + head * (size_t)N;
-  __bf16* dKh = dK + head * (size_t)N * D;
-  __bf16* dVh = dV + head * (size_t)N * D;
+  elt* dKh = dK + head * (size_t)N * D;
+  elt* dVh = dV + head * (size_t)N * D;
 
   const int kv_len = key_length(seqlens_k, b, N);
   const int k0 = kt * C::BK;
@@ -147,15 +156,15 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
   const int n_qt = (k0 < kv_len) ? (N - q_begin + BQ - 1) / BQ : 0;
 
   // the pair's K and V rows (B operands of S = Q K^T and dP = dO V^T)
-  bf16x8 kf[C::KS], vf[C::KS];
+  elt8 kf[C::KS], vf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
     if (my_key < N) {
-      kf[ks] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)my_key * D + ks * 16 + hi * 8);
-      vf[ks] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)my_key * D + ks * 16 + hi * 8);
+      kf[ks] = *reinterpret_cast<const elt8*>(Kh + (size_t)my_key * D + ks * 16 + hi * 8);
+      vf[ks] = *reinterpret_cast<const elt8*>(Vh + (size_t)my_key * D + ks * 16 + hi * 8);
     } else {
-      kf[ks] = bf16x8{};
-      vf[ks] = bf16x8{};
+      kf[ks] = elt8{};
+      vf[ks] = elt8{};
     }
   }
   f32x16 dkacc[C::HDB], dvacc[C::HDB];
@@ -178,23 +187,21 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
   // + 0..3} (the order of the P^T fragment) and features 32 db + l32
   const int ts = lane & 15;
   const int tcol = ((lane >> 4) & 1) * 16 + 4 * (ts & 3);
-  auto colfrag = [&](const __bf16* tile, int g, int db) FA_INLINE {
+  auto colfrag = [&](const elt* tile, int g, int db) FA_INLINE {
     const int r0 = 16 * g + 4 * hi + (ts >> 2);
     const int r1 = r0 + 8;
     const int col = db * 32 + tcol;
     const s16x4 lo = read_tr16(tile + r0 * D + ((col >> 3) ^ tile_swizzle<D>(r0)) * 8 + (col & 7));
     const s16x4 up = read_tr16(tile + r1 * D + ((col >> 3) ^ tile_swizzle<D>(r1)) * 8 + (col & 7));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(elt8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   constexpr int kRowsPerBlk = 1024 / (D * 2);
   constexpr int kBlksPerTensor = BQ / kRowsPerBlk;
   constexpr int kBlksPerWave = 2 * kBlksPerTensor / C::NW;
   static_assert(2 * kBlksPerTensor % C::NW == 0, "whole 1 KiB blocks per wave");
   const int head_bytes = N * D * 2;
-  const __amdgpu_buffer_rsrc_t q_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Qh), 0, head_bytes, kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t o_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(dOh), 0, head_bytes, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(Qh, head_bytes);
+  const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(dOh, head_bytes);
   const int blk_row = lane / (D / 8);
   const int blk_cpos = lane % (D / 8);
   float lreg = 0.f, dreg = 0.f;
@@ -215,8 +222,8 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
       const int row = rb * kRowsPerBlk + blk_row;
       const int chunk = blk_cpos ^ kSwz(row);
       const int voff = (qt0 + row) * (D * 2) + chunk * 16;
-      __bf16* dst = (is_q ? Qs[buf] : dOs[buf]) + rb * kRowsPerBlk * D;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_q ? q_rsrc : o_rsrc, dst, 16, voff, 0, 0, 0);
+      elt* dst = (is_q ? Qs[buf] : dOs[buf]) + rb * kRowsPerBlk * D;
+      lds_dma16_tracked(is_q ? q_rsrc : o_rsrc, dst, voff);
     }
   };
   auto store_stats = [&](int buf) FA_INLINE {
@@ -244,7 +251,7 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
     if (more) issue_tile(qi + 1, buf ^ 1);
     const bool pair_active = pair_keys_valid && (!causal || qt0 + BQ - 1 >= kw0);
 
-    bf16x8 pa[2], dsa[2];
+    elt8 pa[2], dsa[2];
     if (pair_active) {
       // ---- phase 1: S and dP for this wave's 32 query rows (one key per lane)
       f32x16 sacc = f32x16{}, pacc = f32x16{};
@@ -253,10 +260,10 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const int ro = arow * D + ((2 * ks + hi) ^ asw) * 8;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[buf][ro]);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&dOs[buf][ro]);
-        sacc = mfma_bf16(qa, kf[ks], sacc);
-        pacc = mfma_bf16(oa, vf[ks], pacc);
+        const elt8 qa = *reinterpret_cast<const elt8*>(&Qs[buf][ro]);
+        const elt8 oa = *reinterpret_cast<const elt8*>(&dOs[buf][ro]);
+        sacc = E::mfma(qa, kf[ks], sacc);
+        pacc = E::mfma(oa, vf[ks], pacc);
       }
       // this lane's key is visible from tile row 32 half + 8 a4 + 4 hi + e iff
       // 32 half + 8 a4 + e >= first_vis
@@ -273,8 +280,8 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
             const int v = 4 * a4 + e;
             float p = fast_exp2(__builtin_fmaf(sacc[v], scale_log2, -lq[e]));
             if (kMasked) p = (32 * half + 8 * a4 + e >= first_vis) ? p : 0.f;
-            pa[v >> 3][v & 7] = to_bf16(p);
-            dsa[v >> 3][v & 7] = to_bf16(p * (pacc[v] - dq[e]));
+            pa[v >> 3][v & 7] = E::cvt(p);
+            dsa[v >> 3][v & 7] = E::cvt(p * (pacc[v] - dq[e]));
           }
         }
       };
@@ -292,7 +299,7 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
     if (pair_active) {
       // ---- phase 2: dV += P^T dO, dK += dS^T Q over all 64 rows, own feature half
       const int partner = wave ^ 4;
-      bf16x8 po[2], dso[2];
+      elt8 po[2], dso[2];
       po[0] = Xs[partner][0][lane];
       po[1] = Xs[partner][1][lane];
       dso[0] = Xs[partner][2][lane];
@@ -301,15 +308,15 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
       for (int g = 0; g < C::NG; ++g) {
         // groups 2*half, 2*half+1 are this wave's rows; the others the partner's
         const bool own = (g >> 1) == half;
-        const bf16x8 pfrag = own ? pa[g & 1] : po[g & 1];
-        const bf16x8 dsfrag = own ? dsa[g & 1] : dso[g & 1];
+        const elt8 pfrag = own ? pa[g & 1] : po[g & 1];
+        const elt8 dsfrag = own ? dsa[g & 1] : dso[g & 1];
 #pragma unroll
         for (int j = 0; j < C::HDB; ++j) {
           const int db = half * C::HDB + j;
-          const bf16x8 ob = colfrag(dOs[buf], g, db);
-          const bf16x8 qbv = colfrag(Qs[buf], g, db);
-          dvacc[j] = mfma_bf16(pfrag, ob, dvacc[j]);
-          dkacc[j] = mfma_bf16(dsfrag, qbv, dkacc[j]);
+          const elt8 ob = colfrag(dOs[buf], g, db);
+          const elt8 qbv = colfrag(Qs[buf], g, db);
+          dvacc[j] = E::mfma(pfrag, ob, dvacc[j]);
+          dkacc[j] = E::mfma(dsfrag, qbv, dkacc[j]);
         }
       }
     }
@@ -326,8 +333,8 @@ void fa_bwd_dkdv_pair_kernel(const __bf16* __restrict__ Q, const __bf16* __restr
     for (int v = 0; v < 16; ++v) {
       const int key = kw0 + c_row(v, lane);
       if (key < N) {
-        dKh[(size_t)key * D + db * 32 + l32] = to_bf16(dkacc[j][v] * scale);
-        dVh[(size_t)key * D + db * 32 + l32] = to_bf16(dvacc[j][v]);
+        dKh[(size_t)key * D + db * 32 + l32] = E::cvt(dkacc[j][v] * scale);
+        dVh[(size_t)key * D + db * 32 + l32] = E::cvt(dvacc[j][v]);
       }
     }
   }
@@ -346,18 +353,21 @@ struct DqCfg {
   static constexpr int NDB = D / 32;
 };
 
-template <int D, int NW, int BC>
+template <class E, int D, int NW, int BC>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1)))
-void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
+                      const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
                       const float* __restrict__ LSE, const float* __restrict__ Dlt,
                       const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
-                      int causal, __bf16* __restrict__ dQ, int B, int H, int N, int n_qtiles) {
+                      int causal, typename E::T* __restrict__ dQ, int B, int H, int N, int n_qtiles) {
+  using elt = typename E::T;
+  using elt8 = typename E::V8;
+  using elt4 = typename E::V4;
   using C = DqCfg<D, NW, BC>;
   // row-major K and V tiles in two slots (one read, one being loaded)
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BC * D];
+  __shared__ __attribute__((aligned(16))) elt Ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) elt Vs[2][BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -367,11 +377,11 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 
   const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
   const size_t head = (size_t)tc.b * H + tc.h;
-  const __bf16* Qh = Q + head * (size_t)N * D;
-  const __bf16* Kh = K + head * (size_t)N * D;
-  const __bf16* Vh = V + head * (size_t)N * D;
-  const __bf16* dOh = dO + head * (size_t)N * D;
-  __bf16* dQh = dQ + head * (size_t)N * D;
+  const elt* Qh = Q + head * (size_t)N * D;
+  const elt* Kh = K + head * (size_t)N * D;
+  const elt* Vh = V + head * (size_t)N * D;
+  const elt* dOh = dO + head * (size_t)N * D;
+  elt* dQh = dQ + head * (size_t)N * D;
 
   const int kv_len = key_length(seqlens_k, tc.b, N);
   const int q0 = tc.qt * C::BR;
@@ -381,15 +391,15 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   if (causal) kv_end = min(kv_end, min(q0 + C::BR, N));
   const int n_kt = (kv_end + BC - 1) / BC;
 
-  bf16x8 qf[C::KS], of[C::KS];
+  elt8 qf[C::KS], of[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
     if (qrow < N) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + ks * 16 + hi * 8);
-      of[ks] = *reinterpret_cast<const bf16x8*>(dOh + (size_t)qrow * D + ks * 16 + hi * 8);
+      qf[ks] = *reinterpret_cast<const elt8*>(Qh + (size_t)qrow * D + ks * 16 + hi * 8);
+      of[ks] = *reinterpret_cast<const elt8*>(dOh + (size_t)qrow * D + ks * 16 + hi * 8);
     } else {
-      qf[ks] = bf16x8{};
-      of[ks] = bf16x8{};
+      qf[ks] = elt8{};
+      of[ks] = elt8{};
     }
   }
   float lse2 = __builtin_huge_valf(), drow = 0.f;
@@ -434,7 +444,7 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       const int blk = wave * kBlksPerWave + j;
       const bool is_k = blk < kBlksPerTensor;
       const int rb = is_k ? blk : blk - kBlksPerTensor;
-      __bf16* dst = (is_k ? Ks[slot] : Vs[slot]) + rb * kRowsPerBlk * D;
+      elt* dst = (is_k ? Ks[slot] : Vs[slot]) + rb * kRowsPerBlk * D;
       lds_dma16(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D * 2);
     }
   };
@@ -442,13 +452,13 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   // order of the dS^T fragment) and features 32 db + l32
   const int ts = lane & 15;
   const int tcol = ((lane >> 4) & 1) * 16 + 4 * (ts & 3);
-  auto colfrag = [&](const __bf16* tile, int g, int db) FA_INLINE {
+  auto colfrag = [&](const elt* tile, int g, int db) FA_INLINE {
     const int r0 = 16 * g + 4 * hi + (ts >> 2);
     const int r1 = r0 + 8;
     const int col = db * 32 + tcol;
     const s16x4 lo = read_tr16(tile + r0 * D + ((col >> 3) ^ tile_swizzle<D>(r0)) * 8 + (col & 7));
     const s16x4 up = read_tr16(tile + r1 * D + ((col >> 3) ^ tile_swizzle<D>(r1)) * 8 + (col & 7));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(elt8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
   wait_vmem();   // the query rows and their statistics
@@ -477,10 +487,10 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         for (int c = 0; c < C::NCB; ++c) {
           const int arow = c * 32 + l32;
           const int ro = arow * D + ((2 * ks + hi) ^ tile_swizzle<D>(arow)) * 8;
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[slot][ro]);
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[slot][ro]);
-          sacc[c] = mfma_bf16(ka, qf[ks], sacc[c]);
-          pacc[c] = mfma_bf16(va, of[ks], pacc[c]);
+          const elt8 ka = *reinterpret_cast<const elt8*>(&Ks[slot][ro]);
+          const elt8 va = *reinterpret_cast<const elt8*>(&Vs[slot][ro]);
+          sacc[c] = E::mfma(ka, qf[ks], sacc[c]);
+          pacc[c] = E::mfma(va, of[ks], pacc[c]);
         }
       // only tiles crossing the key length or the wave's diagonal are masked:
       // key key0 + 32c + 4hi + p, p = 8(v/4) + v%4, is visible iff it is at
@@ -496,20 +506,20 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         }
       }
       // dS^T = P^T o (dP^T - rowdot)
-      bf16x8 dsb[C::NG];
+      elt8 dsb[C::NG];
 #pragma unroll
       for (int c = 0; c < C::NCB; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = fast_exp2(__builtin_fmaf(sacc[c][v], scale_log2, -lse2));
-          dsb[2 * c + (v >> 3)][v & 7] = to_bf16(p * (pacc[c][v] - drow));
+          dsb[2 * c + (v >> 3)][v & 7] = E::cvt(p * (pacc[c][v] - drow));
         }
       // ---- dQ^T += K^T dS^T
 #pragma unroll
       for (int g = 0; g < C::NG; ++g)
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          dqacc[db] = mfma_bf16(colfrag(Ks[slot], g, db), dsb[g], dqacc[db]);
+          dqacc[db] = E::mfma(colfrag(Ks[slot], g, db), dsb[g], dqacc[db]);
         }
     }
     // the next tile has landed once every wave passes here
@@ -523,56 +533,58 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         const int d0 = db * 32 + 8 * v4 + 4 * hi;
-        bf16x4 w;
+        elt4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = to_bf16(dqacc[db][4 * v4 + e] * scale);
-        *reinterpret_cast<bf16x4*>(dQh + (size_t)qrow * D + d0) = w;
+        for (int e = 0; e < 4; ++e) w[e] = E::cvt(dqacc[db][4 * v4 + e] * scale);
+        *reinterpret_cast<elt4*>(dQh + (size_t)qrow * D + d0) = w;
       }
   }
 }
 
 constexpr int kDqNW = FA_DQ_NW, kDqBC = FA_DQ_BC;
 
-template <int D>
+template <class E, int D>
 hipError_t launch_preprocess_d(const BwdArgs& a) {
+  using T = typename E::T;
   const long long rows = (long long)a.B * a.H * a.N;
   const long long threads = rows * (D / 8);
-  hipLaunchKernelGGL((fa_bwd_rowdot_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                     0, a.stream, static_cast<const __bf16*>(a.o),
-                     static_cast<const __bf16*>(a.dout), a.delta, rows);
+  hipLaunchKernelGGL((fa_bwd_rowdot_kernel<E, D>), dim3((unsigned)((threads + 255) / 256)),
+                     dim3(256), 0, a.stream, static_cast<const T*>(a.o),
+                     static_cast<const T*>(a.dout), a.delta, rows);
   return hipGetLastError();
 }
 
-template <int D>
+template <class E, int D>
 hipError_t launch_dkdv_d(const BwdArgs& a) {
   using CK = DkdvPairCfg<D, 64>;
+  using T = typename E::T;
   const int n_ktiles = (a.N + CK::BK - 1) / CK::BK;
-  hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<D, 64>),
+  hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<E, D, 64>),
                      dim3((unsigned)((long long)n_ktiles * a.B * a.H)), dim3(CK::NT), 0, a.stream,
-                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dout), a.lse,
-                     a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
-                     static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.B, a.H, a.N,
-                     n_ktiles);
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
+                     a.seqlens_k, a.scale, a.scale * kLog2e, a.causal, static_cast<T*>(a.dk),
+                     static_cast<T*>(a.dv), a.B, a.H, a.N, n_ktiles);
   return hipGetLastError();
 }
 
-template <int D>
+template <class E, int D>
 hipError_t launch_dq_d(const BwdArgs& a) {
   using CQ = DqCfg<D, kDqNW, kDqBC>;
+  using T = typename E::T;
   const int n_qtiles = (a.N + CQ::BR - 1) / CQ::BR;
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, kDqNW, kDqBC>),
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, kDqNW, kDqBC>),
                      dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(CQ::NT), 0, a.stream,
-                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dout), a.lse,
-                     a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
-                     static_cast<__bf16*>(a.dq), a.B, a.H, a.N, n_qtiles);
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
+                     a.seqlens_k, a.scale, a.scale * kLog2e, a.causal, static_cast<T*>(a.dq),
+                     a.B, a.H, a.N, n_qtiles);
   return hipGetLastError();
 }
 
 }  // namespace
 
-long long bwd_bf16_grid(int B, int H, int N, int d) {
+long long bwd_half_grid(int B, int H, int N, int d) {
   (void)d;
   const long long kt = (N + 127) / 128;
   const long long qt = (N + kDqNW * 32 - 1) / (kDqNW * 32);
@@ -583,36 +595,39 @@ long long bwd_bf16_grid(int B, int H, int N, int d) {
   return m;
 }
 
-hipError_t launch_bwd_preprocess_bf16(const BwdArgs& a) {
-  switch (a.d) {
-    case 64: return launch_preprocess_d<64>(a);
-    case 128: return launch_preprocess_d<128>(a);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_bwd_preprocess_half(const BwdArgs& a, Elt e) {
+  if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
+  if (e == Elt::kBf16)
+    return a.d == 64 ? launch_preprocess_d<EltBf16, 64>(a) : launch_preprocess_d<EltBf16, 128>(a);
+  if (e == Elt::kF16)
+    return a.d == 64 ? launch_preprocess_d<EltF16, 64>(a) : launch_preprocess_d<EltF16, 128>(a);
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a) {
-  switch (a.d) {
-    case 64: return launch_dkdv_d<64>(a);
-    case 128: return launch_dkdv_d<128>(a);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_bwd_dkdv_half(const BwdArgs& a, Elt e) {
+  if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
+  if (e == Elt::kBf16)
+    return a.d == 64 ? launch_dkdv_d<EltBf16, 64>(a) : launch_dkdv_d<EltBf16, 128>(a);
+  if (e == Elt::kF16)
+    return a.d == 64 ? launch_dkdv_d<EltF16, 64>(a) : launch_dkdv_d<EltF16, 128>(a);
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
-  switch (a.d) {
-    case 64: return launch_dq_d<64>(a);
-    case 128: return launch_dq_d<128>(a);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_bwd_dq_half(const BwdArgs& a, Elt e) {
+  if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
+  if (e == Elt::kBf16)
+    return a.d == 64 ? launch_dq_d<EltBf16, 64>(a) : launch_dq_d<EltBf16, 128>(a);
+  if (e == Elt::kF16)
+    return a.d == 64 ? launch_dq_d<EltF16, 64>(a) : launch_dq_d<EltF16, 128>(a);
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_bf16(const BwdArgs& a) {
-  hipError_t e = launch_bwd_preprocess_bf16(a);
-  if (e != hipSuccess) return e;
-  e = launch_bwd_dkdv_bf16(a);
-  if (e != hipSuccess) return e;
-  return launch_bwd_dq_bf16(a);
+hipError_t launch_bwd_half(const BwdArgs& a, Elt e) {
+  hipError_t r = launch_bwd_preprocess_half(a, e);
+  if (r != hipSuccess) return r;
+  r = launch_bwd_dkdv_half(a, e);
+  if (r != hipSuccess) return r;
+  return launch_bwd_dq_half(a, e);
 }
 
 }  // namespace fa

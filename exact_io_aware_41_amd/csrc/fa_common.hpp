@@ -28,6 +28,8 @@ namespace fa {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
@@ -84,6 +86,38 @@ __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 
 __device__ __forceinline__ float bf16_to_f32(__bf16 x) { return (float)x; }
 
+// The two 16-bit element formats of the MFMA kernels: storage type, 8- and
+// 4-element vectors, the 32x32x16 MFMA with fp32 accumulation, and the
+// round-to-nearest-even conversion from fp32.  Both formats use the same
+// tiles, swizzles and transposing reads; only these operations differ.
+struct EltBf16 {
+  using T = __bf16;
+  using V8 = bf16x8;
+  using V4 = bf16x4;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ T cvt(float x) { return (T)x; }
+  // the two elements packed in a 32-bit word (low half first), widened
+  static __device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi) {
+    lo = __uint_as_float(w << 16);
+    hi = __uint_as_float(w & 0xffff0000u);
+  }
+};
+struct EltF16 {
+  using T = _Float16;
+  using V8 = f16x8;
+  using V4 = f16x4;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ T cvt(float x) { return (T)x; }
+  static __device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi) {
+    lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+};
+
 // Word 3 of a raw buffer descriptor on gfx9-family GPUs (32-bit data format,
 // no swizzling); out-of-range offsets read as zero.
 constexpr int kBufferRsrcWord3 = 0x00020000;
@@ -98,6 +132,19 @@ __device__ __forceinline__ u32x4 buffer_rsrc_words(const void* base, uint32_t by
   r[2] = __builtin_amdgcn_readfirstlane(bytes);
   r[3] = (uint32_t)kBufferRsrcWord3;
   return r;
+}
+
+// Buffer resource (pointer form) over `bytes` bytes at `base`, and the
+// compiler-issued direct load of 16 bytes per lane into LDS at `lds_dst`
+// (lane l writes bytes [16 l, 16 l + 16) of the wave's block).  Plain
+// functions: a kernel template calls them instead of the target builtins.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferRsrcWord3);
+}
+__device__ __forceinline__ void lds_dma16_tracked(__amdgpu_buffer_rsrc_t rsrc, void* lds_dst,
+                                                  int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, 0, 0, 0);
 }
 
 // Direct load of 16 bytes per lane into LDS (buffer_load_dwordx4 ... lds):
@@ -190,9 +237,11 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
 // of the 8-byte chunks addressed by lanes i / 4 + 4 j, j = 0..3.  With lane s
 // addressing row r0 + s / 4, columns c0 + 4 (s % 4) .. + 3, lane i receives
 // column c0 + i of rows r0 .. r0 + 3.
-__device__ __forceinline__ s16x4 read_tr16(const __bf16* p) {
+template <typename T>
+__device__ __forceinline__ s16x4 read_tr16(const T* p) {
+  static_assert(sizeof(T) == 2, "16-bit elements");
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(const_cast<__bf16*>(p)));
+      (__attribute__((address_space(3))) s16x4*)(const_cast<T*>(p)));
 }
 
 // Key length of sequence b clamped to [0, N] (N when no lengths are given).

@@ -53,6 +53,10 @@ struct ElemsPer16<__bf16> {
   static constexpr int value = 8;
 };
 template <>
+struct ElemsPer16<_Float16> {
+  static constexpr int value = 8;
+};
+template <>
 struct ElemsPer16<float> {
   static constexpr int value = 4;
 };
@@ -66,6 +70,11 @@ __device__ __forceinline__ void load16(const __bf16* p, float (&x)[8]) {
     x[2 * w + 1] = __uint_as_float(r[w] & 0xffff0000u);
   }
 }
+__device__ __forceinline__ void load16(const _Float16* p, float (&x)[8]) {
+  const f16x8 r = *reinterpret_cast<const f16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)r[e];
+}
 __device__ __forceinline__ void load16(const float* p, float (&x)[4]) {
   const f32x4 r = *reinterpret_cast<const f32x4*>(p);
 #pragma unroll
@@ -73,6 +82,7 @@ __device__ __forceinline__ void load16(const float* p, float (&x)[4]) {
 }
 
 __device__ __forceinline__ void store_out(__bf16* p, float x) { *p = to_bf16(x); }
+__device__ __forceinline__ void store_out(_Float16* p, float x) { *p = (_Float16)x; }
 __device__ __forceinline__ void store_out(float* p, float x) { *p = x; }
 
 // max / sum over a 256-thread block; `scratch` holds 4 floats
@@ -299,26 +309,35 @@ DecodePlan decode_plan(int B, int H, int N) {
   return p;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, bool bf16) {
+template <typename T>
+hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, float* o_parts,
+                           float* lse_parts) {
+  return a.d == 64 ? launch_decode_split<T, 64>(a, p, o_parts, lse_parts)
+                   : launch_decode_split<T, 128>(a, p, o_parts, lse_parts);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, Elt elt) {
   const DecodePlan p = decode_plan(a.B, a.H, a.N);
   float* o_parts = a.workspace;
   float* lse_parts = a.workspace + (size_t)a.B * a.H * p.parts * a.d;
   hipError_t e;
-  if (bf16)
-    e = a.d == 64 ? launch_decode_split<__bf16, 64>(a, p, o_parts, lse_parts)
-                  : launch_decode_split<__bf16, 128>(a, p, o_parts, lse_parts);
-  else
-    e = a.d == 64 ? launch_decode_split<float, 64>(a, p, o_parts, lse_parts)
-                  : launch_decode_split<float, 128>(a, p, o_parts, lse_parts);
+  switch (elt) {
+    case Elt::kBf16: e = launch_decode_t<__bf16>(a, p, o_parts, lse_parts); break;
+    case Elt::kF16: e = launch_decode_t<_Float16>(a, p, o_parts, lse_parts); break;
+    default: e = launch_decode_t<float>(a, p, o_parts, lse_parts); break;
+  }
   if (e != hipSuccess) return e;
-  return launch_merge(a.B * a.H, p.parts, a.d, o_parts, lse_parts, a.o, a.lse, bf16, a.stream);
+  return launch_merge(a.B * a.H, p.parts, a.d, o_parts, lse_parts, a.o, a.lse, elt, a.stream);
 }
 
 hipError_t launch_merge(int rows, int n_parts, int d, const float* o_parts,
-                        const float* lse_parts, void* o, float* lse, bool bf16,
+                        const float* lse_parts, void* o, float* lse, Elt elt,
                         hipStream_t stream) {
-  return bf16 ? launch_merge_t<__bf16>(rows, n_parts, d, o_parts, lse_parts, o, lse, stream)
-              : launch_merge_t<float>(rows, n_parts, d, o_parts, lse_parts, o, lse, stream);
+  switch (elt) {
+    case Elt::kBf16: return launch_merge_t<__bf16>(rows, n_parts, d, o_parts, lse_parts, o, lse, stream);
+    case Elt::kF16: return launch_merge_t<_Float16>(rows, n_parts, d, o_parts, lse_parts, o, lse, stream);
+    default: return launch_merge_t<float>(rows, n_parts, d, o_parts, lse_parts, o, lse, stream);
+  }
 }
 
 }  // namespace fa

@@ -91,13 +91,16 @@ struct FwdBf16Cfg {
 // accumulators are rescaled only when the maximum really jumps.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, int QB, int NW, int BC>
+template <class E, int D, int QB, int NW, int BC>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
-void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                        const __bf16* __restrict__ V, const int32_t* __restrict__ seqlens_k,
-                        float scale_log2, int causal, __bf16* __restrict__ O,
+void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
+                        const typename E::T* __restrict__ V, const int32_t* __restrict__ seqlens_k,
+                        float scale_log2, int causal, typename E::T* __restrict__ O,
                         float* __restrict__ LSE, int B, int H, int N, int n_qtiles) {
+  using elt = typename E::T;
+  using elt8 = typename E::V8;
+  using elt4 = typename E::V4;
   using C = FwdBf16Cfg<D, QB, NW, BC>;
   // Two groups of NW/2 waves; the waves of a SIMD (w and w + NW/2) sit in
   // different groups.  The second group runs one stage behind: it takes the
@@ -109,8 +112,8 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   constexpr int kVSlots = kPingPong ? 3 : 2;
   // K row-major with XOR-swizzled 16-byte chunks, V row-major with swizzled
   // 64-byte segments (read transposed); both filled by direct loads
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[kVSlots][BC * D];
+  __shared__ __attribute__((aligned(16))) elt Ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) elt Vs[kVSlots][BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -121,10 +124,10 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 
   const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
   const size_t head = (size_t)tc.b * H + tc.h;
-  const __bf16* Qh = Q + head * (size_t)N * D;
-  const __bf16* Kh = K + head * (size_t)N * D;
-  const __bf16* Vh = V + head * (size_t)N * D;
-  __bf16* Oh = O + head * (size_t)N * D;
+  const elt* Qh = Q + head * (size_t)N * D;
+  const elt* Kh = K + head * (size_t)N * D;
+  const elt* Vh = V + head * (size_t)N * D;
+  elt* Oh = O + head * (size_t)N * D;
   float* Lh = LSE + head * (size_t)N;
 
   const int kv_len = key_length(seqlens_k, tc.b, N);
@@ -142,16 +145,16 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   else if (causal) n_act = min(n_kt, qw_last / BC + 1);
 
   // ---- Q fragments (B operand of S^T = K Q^T): query l32, features 8*hi + [0..7]
-  bf16x8 qf[QB][C::KS];
+  elt8 qf[QB][C::KS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qrow = qw0 + qb * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       if (qrow < N)
-        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + ks * 16 + hi * 8);
+        qf[qb][ks] = *reinterpret_cast<const elt8*>(Qh + (size_t)qrow * D + ks * 16 + hi * 8);
       else
-        qf[qb][ks] = bf16x8{};
+        qf[qb][ks] = elt8{};
     }
   }
 
@@ -208,7 +211,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       const int blk = wave * kBlksPerWave + j;
       const bool is_k = blk < kBlksPerTensor;
       const int rb = is_k ? blk : blk - kBlksPerTensor;
-      __bf16* dst = (is_k ? Ks[kbuf] : Vs[vslot]) + rb * kRowsPerBlk * D;
+      elt* dst = (is_k ? Ks[kbuf] : Vs[vslot]) + rb * kRowsPerBlk * D;
       lds_dma16(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D * 2);
     }
   };
@@ -218,13 +221,13 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     const int blk = wave * kBlksPerWave + j;
     const bool is_k = blk < kBlksPerTensor;
     const int rb = is_k ? blk : blk - kBlksPerTensor;
-    __bf16* dst = (is_k ? Ks[kbuf] : Vs[vslot]) + rb * kRowsPerBlk * D;
+    elt* dst = (is_k ? Ks[kbuf] : Vs[vslot]) + rb * kRowsPerBlk * D;
     lds_dma16(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D * 2);
   };
   auto no_dma = [](int) FA_INLINE {};
 
   f32x16 sacc[C::NCB][QB];
-  bf16x8 pf[C::NG][QB];
+  elt8 pf[C::NG][QB];
 
   // S^T(t) = K(t) Q^T.  The K fragments are read from LDS kPre reads ahead of
   // the MFMA that consumes them, so LDS latency overlaps the MFMA pipeline.
@@ -238,10 +241,10 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     auto kfrag = [&](int f) FA_INLINE {
       const int ks = f / C::NCB, c = f % C::NCB;
       const int row = c * 32 + l32;
-      return *reinterpret_cast<const bf16x8*>(
+      return *reinterpret_cast<const elt8*>(
           &Ks[kbuf][row * D + ((2 * ks + hi) ^ row_swizzle<D>(row)) * 8]);
     };
-    bf16x8 ring[kPre];
+    elt8 ring[kPre];
 #pragma unroll
     for (int f = 0; f < kPre && f < NF; ++f) ring[f] = kfrag(f);
 #pragma unroll
@@ -251,10 +254,10 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int ks = f / C::NCB, c = f % C::NCB;
-      const bf16x8 kf = ring[f % kPre];
+      const elt8 kf = ring[f % kPre];
       if (f + kPre < NF) ring[f % kPre] = kfrag(f + kPre);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[c][qb] = mfma_bf16(kf, qf[qb][ks], sacc[c][qb]);
+      for (int qb = 0; qb < QB; ++qb) sacc[c][qb] = E::mfma(kf, qf[qb][ks], sacc[c][qb]);
       if (f % kDmaEvery == 0) dma(f / kDmaEvery);
     }
 #if FA_FWD_SCHED
@@ -282,22 +285,22 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       const int r0 = 16 * g + 4 * hi + (ts >> 2);
       const int r1 = r0 + 8;
       const int col = db * 32 + tcol;
-      const __bf16* vb = Vs[vbuf];
+      const elt* vb = Vs[vbuf];
       const s16x4 lo = read_tr16(vb + r0 * D + (((col >> 5) ^ seg_swizzle<D>(r0)) << 5) + (col & 31));
       const s16x4 up = read_tr16(vb + r1 * D + (((col >> 5) ^ seg_swizzle<D>(r1)) << 5) + (col & 31));
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+      return __builtin_bit_cast(elt8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     constexpr int kReadsPerFrag = 2;
-    bf16x8 ring[kPre];
+    elt8 ring[kPre];
 #pragma unroll
     for (int f = 0; f < kPre && f < NF; ++f) ring[f] = vfrag(f);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int g = f / C::NDB, db = f % C::NDB;
-      const bf16x8 vf = ring[f % kPre];
+      const elt8 vf = ring[f % kPre];
       if (f + kPre < NF) ring[f % kPre] = vfrag(f + kPre);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma_bf16(vf, pf[g][qb], oacc[db][qb]);
+      for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = E::mfma(vf, pf[g][qb], oacc[db][qb]);
       if (f % kDmaEvery == 0) dma(f / kDmaEvery);
     }
 #if FA_FWD_SCHED >= 2
@@ -351,13 +354,13 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
       for (int g = 0; g < C::NG; ++g) {
-        bf16x8 pk;
+        elt8 pk;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float p =
               fast_exp2(__builtin_fmaf(sacc[g >> 1][qb][8 * (g & 1) + i], scale_log2, -m_use));
           if (i & 1) rs1 += p; else rs0 += p;
-          pk[i] = to_bf16(p);
+          pk[i] = E::cvt(p);
         }
         pf[g][qb] = pk;
       }
@@ -437,10 +440,10 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
           const int d0 = db * 32 + 8 * v4 + 4 * hi;
-          bf16x4 w;
+          elt4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = to_bf16(oacc[db][qb][4 * v4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(Oh + (size_t)q * D + d0) = w;
+          for (int e = 0; e < 4; ++e) w[e] = E::cvt(oacc[db][qb][4 * v4 + e] * inv);
+          *reinterpret_cast<elt4*>(Oh + (size_t)q * D + d0) = w;
         }
       if (hi == 0)
         Lh[q] = lt > 0.f ? (m[qb] + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
@@ -633,17 +636,27 @@ struct Bf16Tile {
 };
 constexpr int kF32NW = 2, kF32BC = 32;
 
-template <int D>
-hipError_t launch_bf16_d(const FwdArgs& a) {
+template <class E, int D>
+hipError_t launch_half_d(const FwdArgs& a) {
   constexpr int BC = Bf16Tile<D>::BC;
   using C = FwdBf16Cfg<D, kBf16QB, kBf16NW, BC>;
+  using T = typename E::T;
   const int n_qtiles = (a.N + C::BR - 1) / C::BR;
   const dim3 grid((unsigned)((long long)n_qtiles * a.B * a.H));
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, kBf16QB, kBf16NW, BC>), grid, dim3(C::NT), 0,
-                     a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                     static_cast<const __bf16*>(a.v), a.seqlens_k, a.scale * kLog2e, a.causal,
-                     static_cast<__bf16*>(a.o), a.lse, a.B, a.H, a.N, n_qtiles);
+  hipLaunchKernelGGL((fa_fwd_half_kernel<E, D, kBf16QB, kBf16NW, BC>), grid, dim3(C::NT), 0,
+                     a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), a.seqlens_k, a.scale * kLog2e, a.causal,
+                     static_cast<T*>(a.o), a.lse, a.B, a.H, a.N, n_qtiles);
   return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_half_e(const FwdArgs& a) {
+  switch (a.d) {
+    case 64: return launch_half_d<E, 64>(a);
+    case 128: return launch_half_d<E, 128>(a);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int D>
@@ -660,7 +673,7 @@ hipError_t launch_f32_d(const FwdArgs& a) {
 
 }  // namespace
 
-long long fwd_bf16_grid(int B, int H, int N, int d) {
+long long fwd_half_grid(int B, int H, int N, int d) {
   const int BR = kBf16NW * kBf16QB * 32;
   (void)d;
   return (long long)((N + BR - 1) / BR) * B * H;
@@ -672,12 +685,10 @@ long long fwd_f32_grid(int B, int H, int N, int d) {
   return (long long)((N + BR - 1) / BR) * B * H;
 }
 
-hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  switch (a.d) {
-    case 64: return launch_bf16_d<64>(a);
-    case 128: return launch_bf16_d<128>(a);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_fwd_half(const FwdArgs& a, Elt e) {
+  if (e == Elt::kBf16) return launch_half_e<EltBf16>(a);
+  if (e == Elt::kF16) return launch_half_e<EltF16>(a);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a) {

@@ -9,6 +9,9 @@
 
 namespace fa {
 
+// Element format of a launch's inputs and outputs.
+enum class Elt { kF32, kBf16, kF16 };
+
 struct FwdArgs {
   int B, H, N, d;
   const void* q;
@@ -64,21 +67,22 @@ constexpr int kMaxMergeParts = 4096;
 
 // Each launcher returns hipSuccess or the error hipGetLastError reported
 // after enqueueing; it never synchronises.
-hipError_t launch_fwd_bf16(const FwdArgs& a);
+// The 16-bit launchers take Elt::kBf16 or Elt::kF16.
+hipError_t launch_fwd_half(const FwdArgs& a, Elt e);
 hipError_t launch_fwd_f32(const FwdArgs& a);
-hipError_t launch_bwd_bf16(const BwdArgs& a);
-hipError_t launch_bwd_preprocess_bf16(const BwdArgs& a);
-hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a);
-hipError_t launch_bwd_dq_bf16(const BwdArgs& a);
-hipError_t launch_decode(const DecodeArgs& a, bool bf16);
+hipError_t launch_bwd_half(const BwdArgs& a, Elt e);
+hipError_t launch_bwd_preprocess_half(const BwdArgs& a, Elt e);
+hipError_t launch_bwd_dkdv_half(const BwdArgs& a, Elt e);
+hipError_t launch_bwd_dq_half(const BwdArgs& a, Elt e);
+hipError_t launch_decode(const DecodeArgs& a, Elt e);
 hipError_t launch_merge(int rows, int n_parts, int d, const float* o_parts,
-                        const float* lse_parts, void* o, float* lse, bool bf16,
+                        const float* lse_parts, void* o, float* lse, Elt e,
                         hipStream_t stream);
 
 // Number of work-groups a launch of the given geometry needs; the ABI
 // rejects problems whose grid would not fit in a signed 32-bit count.
-long long fwd_bf16_grid(int B, int H, int N, int d);
+long long fwd_half_grid(int B, int H, int N, int d);
 long long fwd_f32_grid(int B, int H, int N, int d);
-long long bwd_bf16_grid(int B, int H, int N, int d);
+long long bwd_half_grid(int B, int H, int N, int d);
 
 }  // namespace fa

@@ -36,7 +36,7 @@ import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "TENSOR_IDS",
-    "f32_to_bf16_bits", "bf16_bits_to_f32", "widen",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "f32_to_f16_bits", "HALF_DTYPES", "widen",
     "make_lengths", "make_head", "make_tensor", "make_inputs",
     "credited_flops", "useful_pairs", "useful_flops", "min_bytes",
 ]
@@ -52,7 +52,7 @@ class Config:
     H: int
     N: int
     d: int
-    dtype: str            # "f32" or "bf16"
+    dtype: str            # "f32", "bf16" or "f16"
     causal: bool
     lengths: str | None   # None, or "zero_then_uniform"
     q_mult: float = 1.0
@@ -106,10 +106,20 @@ def bf16_bits_to_f32(bits):
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+HALF_DTYPES = ("bf16", "f16")
+
+
+def f32_to_f16_bits(x):
+    """Round float32 values to IEEE binary16 (nearest, ties to even); uint16 bits."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def widen(arr, dtype):
-    """Exact float64 values of a device-format array (fp32, or bf16 bits)."""
+    """Exact float64 values of a device-format array (fp32, or bf16 / f16 bits)."""
     if dtype == "bf16":
         return bf16_bits_to_f32(arr).astype(np.float64)
+    if dtype == "f16":
+        return np.ascontiguousarray(arr, dtype=np.uint16).view(np.float16).astype(np.float64)
     return np.asarray(arr, dtype=np.float32).astype(np.float64)
 
 
@@ -130,7 +140,7 @@ def make_lengths(cfg: Config, seed: int = 0):
 
 def make_head(cfg: Config, name: str, b: int, h: int, seed: int = 0, N: int | None = None,
               d: int | None = None):
-    """One head's [N, d] tensor in device format (float32, or bf16 bits)."""
+    """One head's [N, d] tensor in device format (float32, or bf16 / f16 bits)."""
     N = cfg.N if N is None else N
     d = cfg.d if d is None else d
     rng = np.random.default_rng([seed, TENSOR_IDS[name], b, h])
@@ -139,6 +149,8 @@ def make_head(cfg: Config, name: str, b: int, h: int, seed: int = 0, N: int | No
         x = x * np.float32(cfg.q_mult)
     if cfg.dtype == "bf16":
         return f32_to_bf16_bits(x)
+    if cfg.dtype == "f16":
+        return f32_to_f16_bits(x)
     return x
 
 
@@ -154,7 +166,7 @@ def make_tensor(cfg: Config, name: str, seed: int = 0, threads: int | None = Non
     H = cfg.H if H is None else H
     N = cfg.N if N is None else N
     d = cfg.d if d is None else d
-    out = np.empty((B, H, N, d), np.uint16 if cfg.dtype == "bf16" else np.float32)
+    out = np.empty((B, H, N, d), np.uint16 if cfg.dtype in HALF_DTYPES else np.float32)
 
     def fill(bh):
         b, h = divmod(bh, H)

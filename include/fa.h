@@ -57,9 +57,13 @@
  *                          kernel surface at the caller's next synchronise.
  *
  * Compiled (dtype, d) set:
- *  forward : FA_DTYPE_F32 with d in {64, 128}; FA_DTYPE_BF16 with d in {64, 128}
- *  backward: FA_DTYPE_BF16 with d in {64, 128}
- *  decode and merge: FA_DTYPE_F32 or FA_DTYPE_BF16 with d in {64, 128}
+ *  forward : FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128}
+ *  backward: FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128}
+ *  decode and merge: FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in
+ *  {64, 128}
+ * The 16-bit formats are those the pages list for fused kernels ("What is
+ * FlashAttention?", "Trade-offs and edge cases"); both run the same kernels,
+ * on the MFMA of their format, with fp32 accumulation and statistics.
  */
 #ifndef FA_MI355X_FA_H
 #define FA_MI355X_FA_H
@@ -81,7 +85,8 @@ typedef enum {
 
 typedef enum {
   FA_DTYPE_F32 = 0,  /* IEEE binary32 inputs and outputs                 */
-  FA_DTYPE_BF16 = 1  /* bfloat16 inputs and outputs, fp32 accumulation   */
+  FA_DTYPE_BF16 = 1, /* bfloat16 inputs and outputs, fp32 accumulation   */
+  FA_DTYPE_F16 = 2   /* IEEE binary16 inputs and outputs, fp32 accumulation */
 } fa_dtype;
 
 /* Version of this ABI; bumped on any incompatible change. */

@@ -37,18 +37,23 @@ def custom(cfg_id=2, **kw):
     return dataclasses.replace(fi.CONFIGS[cfg_id], **kw)
 
 
+def torch_dtype(torch, dtype):
+    return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+
+
 def to_device(torch, arr, dtype):
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda().view(torch.bfloat16)
+    if dtype in fi.HALF_DTYPES:
+        bits = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda()
+        return bits.view(torch_dtype(torch, dtype))
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
 
 
 def from_device(t, dtype):
-    """Exact float64 values of a device tensor (bf16 or fp32)."""
+    """Exact float64 values of a device tensor (bf16, f16 or fp32)."""
     import torch
-    if dtype == "bf16":
+    if dtype in fi.HALF_DTYPES:
         bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        return fi.widen(bits, "bf16")
+        return fi.widen(bits, dtype)
     return t.detach().cpu().numpy().astype(np.float64)
 
 

@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 pytestmark = pytest.mark.skipif(not os.path.exists(fa.LIB_PATH),
                                 reason="library not built (run __graft_entry__.build())")
 
-BF16, F32 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_F32
+BF16, F32, F16 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_F32, fa.FA_DTYPE_F16
 A = 0x10000          # aligned fake address: never dereferenced by these calls
 MIS = 0x10004        # 4-byte aligned, not 16-byte aligned
 
@@ -73,7 +73,8 @@ def test_forward_rejects_invalid_arguments(kw):
     assert fwd(**kw) == fa.FA_ERROR_INVALID_VALUE
 
 
-@pytest.mark.parametrize("dtype,d", [(BF16, 96), (BF16, 256), (BF16, 32), (F32, 96), (F32, 16)])
+@pytest.mark.parametrize("dtype,d", [(BF16, 96), (BF16, 256), (BF16, 32), (F32, 96), (F32, 16),
+                                     (F16, 96), (F16, 256)])
 def test_forward_unsupported_shapes_fail_loudly(dtype, d):
     assert fwd(dtype=dtype, d=d) == fa.FA_ERROR_UNSUPPORTED
 
@@ -83,6 +84,9 @@ def test_forward_empty_problems_succeed_without_pointers():
         assert fwd(B=B, H=H, N=N, q=None, k=None, v=None, o=None, lse=None) == fa.FA_SUCCESS
     # an empty problem with an unsupported head dim still reports it
     assert fwd(N=0, d=96) == fa.FA_ERROR_UNSUPPORTED
+    # f16 is a known format; an unknown code is an invalid value
+    assert fwd(dtype=F16, N=0, q=None, k=None, v=None, o=None, lse=None) == fa.FA_SUCCESS
+    assert fwd(dtype=3) == fa.FA_ERROR_INVALID_VALUE
 
 
 def test_forward_grid_too_large_is_rejected():
@@ -103,6 +107,9 @@ def test_backward_rejects_invalid_arguments(kw):
 def test_backward_unsupported_and_workspace_size():
     assert bwd(dtype=F32, d=64) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(dtype=F16, d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(dtype=F16, B=0, q=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
+    assert bwd(dtype=3) == fa.FA_ERROR_INVALID_VALUE
     assert fa.fa_backward_workspace_size(BF16, 2, 32, 8192, 128) == 2 * 32 * 8192 * 4
     assert fa.fa_backward_workspace_size(BF16, 0, 32, 8192, 128) == 0
     assert fa.fa_backward_workspace_size(BF16, -1, 32, 8192, 128) == 0
@@ -111,7 +118,7 @@ def test_backward_unsupported_and_workspace_size():
 
 def test_torch_wrappers_validate_before_calling():
     torch = pytest.importorskip("torch")
-    q = torch.zeros(1, 1, 4, 128, dtype=torch.float16)
+    q = torch.zeros(1, 1, 4, 128, dtype=torch.float64)
     with pytest.raises(fa.FAError) as e:
         fa.forward(q, q, q)
     assert e.value.status == fa.FA_ERROR_UNSUPPORTED
@@ -172,6 +179,9 @@ def test_decode_unsupported_and_empty():
     assert dec(dtype=F32, d=256) == fa.FA_ERROR_UNSUPPORTED
     assert dec(B=0, q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
     assert dec(N=0, q=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
+    assert dec(dtype=F16, d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert dec(dtype=F16, B=0, q=None, k=None, v=None, o=None, lse=None, ws=None,
+               ws_bytes=0) == fa.FA_SUCCESS
 
 
 def test_decode_workspace_follows_the_split_plan():

@@ -1,9 +1,9 @@
 """Decode and merge parity on the GPU: fa_decode and fa_merge_states through
 the C ABI against the fp64 oracle on the same seeded inputs.
 
-Tolerances are the forward's: O max-abs <= 2e-2 for bf16 inputs and
-<= 1e-5 for fp32; LSE <= 1e-3 + 1e-5 |LSE| for bf16 and <= 1e-5 for fp32; an
-empty cache must give O == 0 and LSE == -inf exactly.
+Tolerances are the forward's: O max-abs <= 2e-2 for bf16 inputs, <= 5e-3 for
+f16 and <= 1e-5 for fp32; LSE <= 1e-3 + 1e-5 |LSE| for the 16-bit formats and
+<= 1e-5 for fp32; an empty cache must give O == 0 and LSE == -inf exactly.
 """
 
 import dataclasses
@@ -17,8 +17,8 @@ from tests.gpu_helpers import check_lse, from_device, lib, log_case, max_abs, to
 
 pytestmark = pytest.mark.gpu
 
-O_TOL = {"f32": 1e-5, "bf16": 2e-2}
-LSE_TOL = {"f32": (1e-5, 0.0), "bf16": (1e-3, 1e-5)}
+O_TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 5e-3}
+LSE_TOL = {"f32": (1e-5, 0.0), "bf16": (1e-3, 1e-5), "f16": (1e-3, 1e-5)}
 
 
 def run_decode(torch, cfg, inputs, stream=None):
@@ -59,7 +59,7 @@ def oracle_decode(cfg, inputs, heads=None):
     return o, lse
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N,lengths", [
     (1, None), (63, None), (300, "zero_then_uniform"), (300, [300, 1, 0]), (5000, None),
@@ -107,7 +107,7 @@ def test_decode_one_long_row_many_parts():
     check_decode(cfg, o, lse, ref_o, ref_lse)
 
 
-@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("parts,d", [(1, 128), (7, 64), (300, 128), (4096, 64)])
 def test_merge_states_against_oracle(out_dtype, parts, d):
     torch = torch_cuda()
@@ -120,14 +120,14 @@ def test_merge_states_against_oracle(out_dtype, parts, d):
     lse_parts[rng.random((R, parts)) < 0.3] = -np.inf
     lse_parts[3] = -np.inf                       # a row with every part empty
     lse_parts[5, 1:] = -np.inf                   # a row with one live part
-    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out_dtype]
     o, lse = fa.merge_states(torch.from_numpy(o_parts).cuda(), torch.from_numpy(lse_parts).cuda(),
                              dtype=dt)
     torch.cuda.synchronize()
     ref_o, ref_lse = oracle.merge_states(o_parts.astype(np.float64), lse_parts.astype(np.float64))
     got = from_device(o, out_dtype)
     # fp32 arithmetic over `parts` terms, then the output rounding
-    tol = 2e-2 if out_dtype == "bf16" else 1e-5
+    tol = {"bf16": 2e-2, "f16": 5e-3, "f32": 1e-5}[out_dtype]
     assert max_abs(got, ref_o) <= tol
     check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, 1e-5, 1e-6)
     assert np.all(got[3] == 0.0)

@@ -150,3 +150,28 @@ def test_useful_pairs_brute_force():
                 assert fi.useful_pairs(N, causal, np.array([L])) == int(vis.sum())
     assert fi.useful_pairs(8, True) == 36
     assert fi.useful_flops(1, 2, 8, 4, True) == 4 * 4 * 2 * 36
+
+
+def test_f16_rounding_matches_binary16_facts():
+    """IEEE binary16: 1 = 0x3C00, 65504 = 0x7BFF (largest finite), 2^-24 =
+    0x0001 (smallest subnormal); 1 + 2^-11 is a tie between 1 and 1 + 2^-10
+    and rounds to the even 1; 1 + 3 * 2^-11 rounds up to 1 + 2^-9; 65520 rounds
+    to infinity (0x7C00)."""
+    x = np.array([1.0, 65504.0, 2.0 ** -24, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 65520.0, -2.0],
+                 np.float32)
+    bits = fi.f32_to_f16_bits(x)
+    assert bits.tolist() == [0x3C00, 0x7BFF, 0x0001, 0x3C00, 0x3C02, 0x7C00, 0xC000]
+    w = fi.widen(bits, "f16")
+    assert w.tolist()[:5] == [1.0, 65504.0, 2.0 ** -24, 1.0, 1 + 2.0 ** -9]
+
+
+def test_f16_tensors_are_the_rounded_float32_draws():
+    cfg = fi.CONFIGS[2]
+    import dataclasses
+    c16 = dataclasses.replace(cfg, dtype="f16", N=64)
+    c32 = dataclasses.replace(cfg, dtype="f32", N=64)
+    a = fi.widen(fi.make_head(c16, "k", 1, 3), "f16")
+    b = fi.make_head(c32, "k", 1, 3).astype(np.float64)
+    # the f16 value is the nearest binary16 value: within half an ulp
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(b), 2.0 ** -14))) - 10)
+    assert np.all(np.abs(a - b) <= ulp / 2)
