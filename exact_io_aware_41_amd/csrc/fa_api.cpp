@@ -18,20 +18,42 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool is_half(fa_dtype dtype) { return dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16; }
 
+fa::Elt elt_of(fa_dtype dtype) {
+  return dtype == FA_DTYPE_BF16 ? fa::Elt::kBf16
+                                : dtype == FA_DTYPE_F16 ? fa::Elt::kF16 : fa::Elt::kF32;
+}
+
 bool fwd_supported(fa_dtype dtype, int d) {
   return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128);
 }
 
-bool bwd_supported(fa_dtype dtype, int d) { return is_half(dtype) && (d == 64 || d == 128); }
+bool bwd_supported(fa_dtype dtype, int d) {
+  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128);
+}
+
+long long bwd_grid(fa_dtype dtype, int B, int H, int N, int d) {
+  return is_half(dtype) ? fa::bwd_half_grid(B, H, N, d) : fa::bwd_f32_grid(B, H, N, d);
+}
+
+// backward launches by element format (16-bit kernels or the fp32 ones)
+hipError_t bwd_all(fa_dtype t, const fa::BwdArgs& a) {
+  return is_half(t) ? fa::launch_bwd_half(a, elt_of(t)) : fa::launch_bwd_f32(a);
+}
+hipError_t bwd_pre(fa_dtype t, const fa::BwdArgs& a) {
+  return is_half(t) ? fa::launch_bwd_preprocess_half(a, elt_of(t))
+                    : fa::launch_bwd_preprocess_f32(a);
+}
+hipError_t bwd_dkdv(fa_dtype t, const fa::BwdArgs& a) {
+  return is_half(t) ? fa::launch_bwd_dkdv_half(a, elt_of(t)) : fa::launch_bwd_dkdv_f32(a);
+}
+hipError_t bwd_dq(fa_dtype t, const fa::BwdArgs& a) {
+  return is_half(t) ? fa::launch_bwd_dq_half(a, elt_of(t)) : fa::launch_bwd_dq_f32(a);
+}
 
 bool decode_supported(fa_dtype dtype, int d) {
   return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128);
 }
 
-fa::Elt elt_of(fa_dtype dtype) {
-  return dtype == FA_DTYPE_BF16 ? fa::Elt::kBf16
-                                : dtype == FA_DTYPE_F16 ? fa::Elt::kF16 : fa::Elt::kF32;
-}
 
 // Longest cache a decode call accepts (parts of at most 4096 keys, at most
 // 4096 parts per row).
@@ -85,7 +107,8 @@ fa_status fa_forward(fa_dtype dtype, int B, int H, int N, int d, const void* q, 
   if (grid > kMaxGrid) return FA_ERROR_INVALID_VALUE;
 
   fa::FwdArgs a{B, H, N, d, q, k, v, seqlens_k, scale, causal, o, lse, stream};
-  const hipError_t e = is_half(dtype) ? fa::launch_fwd_half(a, elt_of(dtype)) : fa::launch_fwd_f32(a);
+  const hipError_t e =
+      is_half(dtype) ? fa::launch_fwd_half(a, elt_of(dtype)) : fa::launch_fwd_f32(a);
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
@@ -112,13 +135,14 @@ fa_status fa_backward(fa_dtype dtype, int B, int H, int N, int d, const void* q,
       !aligned16(workspace))
     return FA_ERROR_INVALID_VALUE;
   if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
-  if (workspace_bytes < fa_backward_workspace_size(dtype, B, H, N, d)) return FA_ERROR_INVALID_VALUE;
-  if (fa::bwd_half_grid(B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < fa_backward_workspace_size(dtype, B, H, N, d))
+    return FA_ERROR_INVALID_VALUE;
+  if (bwd_grid(dtype, B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
 
   fa::BwdArgs a{B,     H,       N,          d,      q,  k,  v,  o,  dout,
                 lse,   seqlens_k, scale,    causal, dq, dk, dv, static_cast<float*>(workspace),
                 stream};
-  const hipError_t e = fa::launch_bwd_half(a, elt_of(dtype));
+  const hipError_t e = bwd_all(dtype, a);
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
@@ -132,10 +156,10 @@ fa_status fa_backward_preprocess(fa_dtype dtype, int B, int H, int N, int d, con
   if (empty) return FA_SUCCESS;
   if (!o || !dout || !delta) return FA_ERROR_INVALID_VALUE;
   if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return FA_ERROR_INVALID_VALUE;
-  if (fa::bwd_half_grid(B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  if (bwd_grid(dtype, B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
   fa::BwdArgs a{B, H, N, d, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, 1.f, 0,
                 nullptr, nullptr, nullptr, delta, stream};
-  return fa::launch_bwd_preprocess_half(a, elt_of(dtype)) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+  return bwd_pre(dtype, a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
 namespace {
@@ -152,7 +176,7 @@ fa_status check_bwd_phase(fa_dtype dtype, int B, int H, int N, int d, const void
       !aligned16(delta) || !aligned16(out0) || !aligned16(out1))
     return FA_ERROR_INVALID_VALUE;
   if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
-  if (fa::bwd_half_grid(B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  if (bwd_grid(dtype, B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
   return FA_SUCCESS;
 }
 }  // namespace
@@ -168,7 +192,7 @@ fa_status fa_backward_dkdv(fa_dtype dtype, int B, int H, int N, int d, const voi
   fa::BwdArgs a{B,     H,         N,     d,      q,       k,  v,  nullptr, dout,
                 lse,   seqlens_k, scale, causal, nullptr, dk, dv, const_cast<float*>(delta),
                 stream};
-  return fa::launch_bwd_dkdv_half(a, elt_of(dtype)) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+  return bwd_dkdv(dtype, a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
 fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int N, int d, const void* q, const void* k,
@@ -182,7 +206,7 @@ fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int N, int d, const void*
   fa::BwdArgs a{B,     H,         N,     d,      q,  k,       v,       nullptr, dout,
                 lse,   seqlens_k, scale, causal, dq, nullptr, nullptr, const_cast<float*>(delta),
                 stream};
-  return fa::launch_bwd_dq_half(a, elt_of(dtype)) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+  return bwd_dq(dtype, a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
 size_t fa_decode_workspace_size(fa_dtype dtype, int B, int H, int N, int d) {

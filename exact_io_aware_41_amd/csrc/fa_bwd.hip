@@ -108,8 +108,10 @@ struct DkdvPairCfg {
 template <class E, int D, int BQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
-                             const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
+void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
+                             const typename E::T* __restrict__ K,
+                             const typename E::T* __restrict__ V,
+                             const typename E::T* __restrict__ dO,
                              const float* __restrict__ LSE, const float* __restrict__ Dlt,
                              const int32_t* __restrict__ seqlens_k, float scale,
                              float scale_log2, int causal, typename E::T* __restrict__ dK,
@@ -360,7 +362,8 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
                       const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
                       const float* __restrict__ LSE, const float* __restrict__ Dlt,
                       const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
-                      int causal, typename E::T* __restrict__ dQ, int B, int H, int N, int n_qtiles) {
+                      int causal, typename E::T* __restrict__ dQ, int B, int H, int N,
+                      int n_qtiles) {
   using elt = typename E::T;
   using elt8 = typename E::V8;
   using elt4 = typename E::V4;

@@ -1,0 +1,396 @@
+// fa_bwd_f32.hip - backward kernels for fp32 inputs and outputs.
+//
+// Method ("What is FlashAttention?", Step 4; "FlashAttention", section "What
+// it does not do"; "Explain FlashAttention and why it is IO-aware", section
+// "Exact attention, finite precision and backward"): nothing N x N is read
+// back; S and P are recomputed tile by tile from Q, K and the saved
+// per-row LSE, P = exp(scale * q.k - LSE), and with D_i = sum_t dO_it O_it
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dK = scale dS^T Q,
+//   dQ = scale dS K.
+// The same algorithm as the 16-bit kernels, on the fp32 MFMA
+// (v_mfma_f32_32x32x2_f32: each lane supplies one fp32 of A and of B, A lane l
+// holds row l % 32 and k = l / 32, B lane l holds column l % 32 and the same
+// k, and the accumulator lane l holds column l % 32 and rows
+// 8 (v / 4) + 4 (l / 32) + v % 4).  The result keeps fp32 accuracy end to end.
+//
+//  * rowdot: one thread per 4 features of a row, D in fp32.
+//  * dK/dV: a work-group of two waves owns 64 keys (32 per wave, one key per
+//    lane) whose K and V rows stay in LDS; it walks the 32-row query tiles
+//    that see them.  S = Q K^T and dP = dO V^T come out with one key per
+//    lane and queries in the accumulator index, which is exactly the A
+//    operand of dV = P^T dO and dK = dS^T Q: the two rows a lane contributes
+//    to one MFMA are its own values for queries q and q + 4.
+//  * dQ: a work-group of two waves owns 64 query rows (one query per lane)
+//    and walks the 32-key tiles they see, as the forward does: S^T = K Q^T and
+//    dP^T = V dO^T with the query's Q and dO in registers, then
+//    dQ^T += K^T dS^T, the K^T fragments read across rows of the K tile.
+//  * masking on absolute positions (key j visible from row i iff j < L and,
+//    when causal, j <= i), only on tiles that cross the key length or the
+//    diagonal; masked entries of P are zero, so fully masked rows (LSE = -inf)
+//    contribute nothing.
+
+#include "fa_common.hpp"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kF32BwdNW = 2;   // waves per work-group in both kernels
+constexpr int kF32BwdRows = kF32BwdNW * 32;
+
+// Row pitches in floats: +2 makes the 32-row x 2-column fragment reads
+// (row l % 32, column 2 ks + l / 32) hit 64 distinct banks.
+template <int D>
+struct F32BwdCfg {
+  static constexpr int PITCH = D + 2;
+  static constexpr int KS = D / 2;     // k-steps of a D-long contraction
+  static constexpr int NDB = D / 32;   // 32-feature blocks
+  static_assert(D % 32 == 0, "head dimension");
+};
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void fa_bwd_rowdot_f32_kernel(const float* __restrict__ O, const float* __restrict__ dO,
+                              float* __restrict__ Dout, long long rows) {
+  constexpr int TPR = D / 4;   // threads per row
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = gid / TPR;
+  const int part = (int)(gid % TPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(O + row * D + part * 4);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(dO + row * D + part * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(a[e], b[e], acc);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) Dout[row] = acc;
+}
+
+// Copies rows [r0, r0 + n_rows) of a [N][D] head into an LDS tile of pitch
+// PITCH (rows past `valid` as zeros), all threads of the work-group.
+template <int D>
+__device__ __forceinline__ void load_rows(float* tile, const float* head, int r0, int n_rows,
+                                          int valid, int tid, int nthreads) {
+  using C = F32BwdCfg<D>;
+  for (int u = tid; u < n_rows * (D / 4); u += nthreads) {
+    const int r = u / (D / 4);
+    const int c4 = u % (D / 4);
+    const int row = r0 + r;
+    const f32x4 x = row < valid ? *reinterpret_cast<const f32x4*>(head + (size_t)row * D + c4 * 4)
+                                : f32x4{};
+    float* dst = tile + r * C::PITCH + c4 * 4;
+    dst[0] = x[0];
+    dst[1] = x[1];
+    dst[2] = x[2];
+    dst[3] = x[3];
+  }
+}
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kF32BwdNW * 64, kF32BwdNW * 64)))
+void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                            const float* __restrict__ V, const float* __restrict__ dO,
+                            const float* __restrict__ LSE, const float* __restrict__ Dlt,
+                            const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
+                            int causal, float* __restrict__ dK, float* __restrict__ dV, int B,
+                            int H, int N, int n_kblocks) {
+  using C = F32BwdCfg<D>;
+  constexpr int NT = kF32BwdNW * 64;
+  constexpr int BK = kF32BwdRows;   // keys per work-group
+  constexpr int QT = 32;            // query rows per tile
+  __shared__ __attribute__((aligned(16))) float Ks[BK * C::PITCH];
+  __shared__ __attribute__((aligned(16))) float Vs[BK * C::PITCH];
+  __shared__ __attribute__((aligned(16))) float Qs[QT * C::PITCH];
+  __shared__ __attribute__((aligned(16))) float dOs[QT * C::PITCH];
+  __shared__ float Ls[QT], Ds[QT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // key blocks in order: under a causal mask block 0 sees every query tile
+  const int bh_count = B * H;
+  const int kb = blockIdx.x / bh_count;
+  const int bh = blockIdx.x - kb * bh_count;
+  const int b = bh / H;
+  const size_t head = (size_t)bh;
+  const float* Qh = Q + head * (size_t)N * D;
+  const float* Kh = K + head * (size_t)N * D;
+  const float* Vh = V + head * (size_t)N * D;
+  const float* dOh = dO + head * (size_t)N * D;
+  const float* Lh = LSE + head * (size_t)N;
+  const float* Dh = Dlt + head * (size_t)N;
+  const int kv_len = key_length(seqlens_k, b, N);
+  const int k0 = kb * BK;
+  const int kw0 = k0 + wave * 32;           // this wave's first key
+  const int my_key = kw0 + l32;
+
+  load_rows<D>(Ks, Kh, k0, BK, kv_len, tid, NT);
+  load_rows<D>(Vs, Vh, k0, BK, kv_len, tid, NT);
+
+  f32x16 dvacc[C::NDB], dkacc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    dvacc[db] = f32x16{};
+    dkacc[db] = f32x16{};
+  }
+
+  // query tiles that see any key of the block: under the causal mask the
+  // first is the one holding row k0; keys past the length are never visible
+  const int q_begin = causal ? (k0 / QT) * QT : 0;
+  const bool block_live = k0 < kv_len;
+  const int n_qt = block_live ? (N - q_begin + QT - 1) / QT : 0;
+  const bool wave_keys_live = kw0 < kv_len;
+  const float* Kw = Ks + wave * 32 * C::PITCH;
+  const float* Vw = Vs + wave * 32 * C::PITCH;
+
+  for (int qi = 0; qi < n_qt; ++qi) {
+    const int qt0 = q_begin + qi * QT;
+    __syncthreads();   // the previous tile's readers are done
+    load_rows<D>(Qs, Qh, qt0, QT, N, tid, NT);
+    load_rows<D>(dOs, dOh, qt0, QT, N, tid, NT);
+    if (tid < QT) {
+      const int row = qt0 + tid;
+      Ls[tid] = row < N ? Lh[row] : 0.f;
+      Ds[tid] = row < N ? Dh[row] : 0.f;
+    }
+    __syncthreads();
+    // causal: the tile's last row precedes this wave's first key
+    const bool active = wave_keys_live && (!causal || qt0 + QT - 1 >= kw0);
+    if (!active) continue;
+
+    // S[q][key] = Q K^T and dP[q][key] = dO V^T: lane = key, v = query row
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll 8
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int col = 2 * ks + hi;
+      const float kb_op = Kw[l32 * C::PITCH + col];
+      const float vb_op = Vw[l32 * C::PITCH + col];
+      sacc = mfma_f32(Qs[l32 * C::PITCH + col], kb_op, sacc);
+      pacc = mfma_f32(dOs[l32 * C::PITCH + col], vb_op, pacc);
+    }
+    const bool need_mask = (kw0 + 31 >= kv_len) || (causal && qt0 < kw0 + 31) || qt0 + QT > N;
+    float p[16], ds[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = c_row(v, lane);
+      float x = fast_exp2(__builtin_fmaf(sacc[v], scale_log2, -Ls[r] * kLog2e));
+      if (need_mask) {
+        const int q = qt0 + r;
+        const bool vis = my_key < kv_len && (!causal || my_key <= q) && q < N;
+        x = vis ? x : 0.f;
+      }
+      p[v] = x;
+      ds[v] = x * (pacc[v] - Ds[r]);
+    }
+    // dV += P^T dO and dK += dS^T Q: step v contracts over rows c_row(v, .)
+    // (the pair q, q + 4 of the two lane halves)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = c_row(v, lane);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        dvacc[db] = mfma_f32(p[v], dOs[r * C::PITCH + db * 32 + l32], dvacc[db]);
+        dkacc[db] = mfma_f32(ds[v], Qs[r * C::PITCH + db * 32 + l32], dkacc[db]);
+      }
+    }
+  }
+
+  // dV[key][feature], dK = scale * acc: accumulator lane l holds feature
+  // 32 db + l % 32 of keys kw0 + c_row(v, l)
+  float* dKh = dK + head * (size_t)N * D;
+  float* dVh = dV + head * (size_t)N * D;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = kw0 + c_row(v, lane);
+      if (key < N) {
+        dVh[(size_t)key * D + db * 32 + l32] = dvacc[db][v];
+        dKh[(size_t)key * D + db * 32 + l32] = dkacc[db][v] * scale;
+      }
+    }
+}
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kF32BwdNW * 64, kF32BwdNW * 64)))
+void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                          const float* __restrict__ V, const float* __restrict__ dO,
+                          const float* __restrict__ LSE, const float* __restrict__ Dlt,
+                          const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
+                          int causal, float* __restrict__ dQ, int B, int H, int N,
+                          int n_qtiles) {
+  using C = F32BwdCfg<D>;
+  constexpr int NT = kF32BwdNW * 64;
+  constexpr int BC = 32;            // keys per tile
+  __shared__ __attribute__((aligned(16))) float Ks[BC * C::PITCH];
+  __shared__ __attribute__((aligned(16))) float Vs[BC * C::PITCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
+  const size_t head = (size_t)tc.b * H + tc.h;
+  const float* Qh = Q + head * (size_t)N * D;
+  const float* Kh = K + head * (size_t)N * D;
+  const float* Vh = V + head * (size_t)N * D;
+  const float* dOh = dO + head * (size_t)N * D;
+  const int kv_len = key_length(seqlens_k, tc.b, N);
+  const int q0 = tc.qt * kF32BwdRows;
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + l32;
+
+  // this lane's query row: Q and dO as B operands, LSE and D in registers
+  float qf[C::KS], of[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    qf[ks] = qrow < N ? Qh[(size_t)qrow * D + 2 * ks + hi] : 0.f;
+    of[ks] = qrow < N ? dOh[(size_t)qrow * D + 2 * ks + hi] : 0.f;
+  }
+  const float lse2 = qrow < N ? LSE[head * (size_t)N + qrow] * kLog2e : 0.f;
+  const float drow = qrow < N ? Dlt[head * (size_t)N + qrow] : 0.f;
+
+  int kv_end = kv_len;
+  if (causal) kv_end = min(kv_end, min(q0 + kF32BwdRows, N));
+  const int n_kt = (kv_end + BC - 1) / BC;
+
+  f32x16 dqacc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) dqacc[db] = f32x16{};
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int key0 = kt * BC;
+    __syncthreads();
+    load_rows<D>(Ks, Kh, key0, BC, kv_len, tid, NT);
+    load_rows<D>(Vs, Vh, key0, BC, kv_len, tid, NT);
+    __syncthreads();
+    const bool active = qw0 < N && (!causal || key0 <= qw0 + 31);
+    if (!active) continue;
+
+    // S^T = K Q^T, dP^T = V dO^T: lane = query, v = key
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll 8
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int col = 2 * ks + hi;
+      sacc = mfma_f32(Ks[l32 * C::PITCH + col], qf[ks], sacc);
+      pacc = mfma_f32(Vs[l32 * C::PITCH + col], of[ks], pacc);
+    }
+    const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0);
+    float ds[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = key0 + c_row(v, lane);
+      float x = fast_exp2(__builtin_fmaf(sacc[v], scale_log2, -lse2));
+      if (need_mask) {
+        const bool vis = key < kv_len && (!causal || key <= qrow);
+        x = vis ? x : 0.f;
+      }
+      ds[v] = x * (pacc[v] - drow);
+    }
+    // dQ^T += K^T dS^T: step v contracts over keys c_row(v, .)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int kr = c_row(v, lane);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+        dqacc[db] = mfma_f32(Ks[kr * C::PITCH + db * 32 + l32], ds[v], dqacc[db]);
+    }
+  }
+
+  // dQ^T accumulator lane l holds query l % 32 and features
+  // 32 db + 8 (v / 4) + 4 (l / 32) + v % 4
+  if (qrow < N) {
+    float* dQh = dQ + head * (size_t)N * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int d0 = db * 32 + 8 * v4 + 4 * hi;
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = dqacc[db][4 * v4 + e] * scale;
+        *reinterpret_cast<f32x4*>(dQh + (size_t)qrow * D + d0) = w;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_preprocess_f32_d(const BwdArgs& a) {
+  const long long rows = (long long)a.B * a.H * a.N;
+  const long long threads = rows * (D / 4);
+  hipLaunchKernelGGL((fa_bwd_rowdot_f32_kernel<D>), dim3((unsigned)((threads + 255) / 256)),
+                     dim3(256), 0, a.stream, static_cast<const float*>(a.o),
+                     static_cast<const float*>(a.dout), a.delta, rows);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dkdv_f32_d(const BwdArgs& a) {
+  const int n_kblocks = (a.N + kF32BwdRows - 1) / kF32BwdRows;
+  hipLaunchKernelGGL((fa_bwd_dkdv_f32_kernel<D>),
+                     dim3((unsigned)((long long)n_kblocks * a.B * a.H)), dim3(kF32BwdNW * 64), 0,
+                     a.stream, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                     static_cast<const float*>(a.v), static_cast<const float*>(a.dout), a.lse,
+                     a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
+                     static_cast<float*>(a.dk), static_cast<float*>(a.dv), a.B, a.H, a.N,
+                     n_kblocks);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dq_f32_d(const BwdArgs& a) {
+  const int n_qtiles = (a.N + kF32BwdRows - 1) / kF32BwdRows;
+  hipLaunchKernelGGL((fa_bwd_dq_f32_kernel<D>),
+                     dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(kF32BwdNW * 64), 0,
+                     a.stream, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                     static_cast<const float*>(a.v), static_cast<const float*>(a.dout), a.lse,
+                     a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
+                     static_cast<float*>(a.dq), a.B, a.H, a.N, n_qtiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+long long bwd_f32_grid(int B, int H, int N, int d) {
+  (void)d;
+  const long long tiles = (N + kF32BwdRows - 1) / kF32BwdRows;
+  const long long rows_wg = ((long long)B * H * N * (d / 4) + 255) / 256;
+  const long long m = tiles * B * H;
+  return rows_wg > m ? rows_wg : m;
+}
+
+hipError_t launch_bwd_preprocess_f32(const BwdArgs& a) {
+  if (a.d == 64) return launch_preprocess_f32_d<64>(a);
+  if (a.d == 128) return launch_preprocess_f32_d<128>(a);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dkdv_f32(const BwdArgs& a) {
+  if (a.d == 64) return launch_dkdv_f32_d<64>(a);
+  if (a.d == 128) return launch_dkdv_f32_d<128>(a);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq_f32(const BwdArgs& a) {
+  if (a.d == 64) return launch_dq_f32_d<64>(a);
+  if (a.d == 128) return launch_dq_f32_d<128>(a);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_f32(const BwdArgs& a) {
+  hipError_t r = launch_bwd_preprocess_f32(a);
+  if (r != hipSuccess) return r;
+  r = launch_bwd_dkdv_f32(a);
+  if (r != hipSuccess) return r;
+  return launch_bwd_dq_f32(a);
+}
+
+}  // namespace fa

@@ -334,8 +334,10 @@ hipError_t launch_merge(int rows, int n_parts, int d, const float* o_parts,
                         const float* lse_parts, void* o, float* lse, Elt elt,
                         hipStream_t stream) {
   switch (elt) {
-    case Elt::kBf16: return launch_merge_t<__bf16>(rows, n_parts, d, o_parts, lse_parts, o, lse, stream);
-    case Elt::kF16: return launch_merge_t<_Float16>(rows, n_parts, d, o_parts, lse_parts, o, lse, stream);
+    case Elt::kBf16:
+      return launch_merge_t<__bf16>(rows, n_parts, d, o_parts, lse_parts, o, lse, stream);
+    case Elt::kF16:
+      return launch_merge_t<_Float16>(rows, n_parts, d, o_parts, lse_parts, o, lse, stream);
     default: return launch_merge_t<float>(rows, n_parts, d, o_parts, lse_parts, o, lse, stream);
   }
 }

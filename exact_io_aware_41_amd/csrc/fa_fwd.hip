@@ -286,8 +286,10 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
       const int r1 = r0 + 8;
       const int col = db * 32 + tcol;
       const elt* vb = Vs[vbuf];
-      const s16x4 lo = read_tr16(vb + r0 * D + (((col >> 5) ^ seg_swizzle<D>(r0)) << 5) + (col & 31));
-      const s16x4 up = read_tr16(vb + r1 * D + (((col >> 5) ^ seg_swizzle<D>(r1)) << 5) + (col & 31));
+      const s16x4 lo =
+          read_tr16(vb + r0 * D + (((col >> 5) ^ seg_swizzle<D>(r0)) << 5) + (col & 31));
+      const s16x4 up =
+          read_tr16(vb + r1 * D + (((col >> 5) ^ seg_swizzle<D>(r1)) << 5) + (col & 31));
       return __builtin_bit_cast(elt8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     constexpr int kReadsPerFrag = 2;

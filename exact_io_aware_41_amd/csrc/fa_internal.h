@@ -74,6 +74,10 @@ hipError_t launch_bwd_half(const BwdArgs& a, Elt e);
 hipError_t launch_bwd_preprocess_half(const BwdArgs& a, Elt e);
 hipError_t launch_bwd_dkdv_half(const BwdArgs& a, Elt e);
 hipError_t launch_bwd_dq_half(const BwdArgs& a, Elt e);
+hipError_t launch_bwd_f32(const BwdArgs& a);
+hipError_t launch_bwd_preprocess_f32(const BwdArgs& a);
+hipError_t launch_bwd_dkdv_f32(const BwdArgs& a);
+hipError_t launch_bwd_dq_f32(const BwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a, Elt e);
 hipError_t launch_merge(int rows, int n_parts, int d, const float* o_parts,
                         const float* lse_parts, void* o, float* lse, Elt e,
@@ -84,5 +88,6 @@ hipError_t launch_merge(int rows, int n_parts, int d, const float* o_parts,
 long long fwd_half_grid(int B, int H, int N, int d);
 long long fwd_f32_grid(int B, int H, int N, int d);
 long long bwd_half_grid(int B, int H, int N, int d);
+long long bwd_f32_grid(int B, int H, int N, int d);
 
 }  // namespace fa

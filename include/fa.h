@@ -58,7 +58,8 @@
  *
  * Compiled (dtype, d) set:
  *  forward : FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128}
- *  backward: FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128}
+ *  backward: FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128}
+ *            (fp32 on the fp32 MFMA: fp32 inputs, arithmetic and outputs)
  *  decode and merge: FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in
  *  {64, 128}
  * The 16-bit formats are those the pages list for fused kernels ("What is

@@ -105,7 +105,8 @@ def test_backward_rejects_invalid_arguments(kw):
 
 
 def test_backward_unsupported_and_workspace_size():
-    assert bwd(dtype=F32, d=64) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(dtype=F32, d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(dtype=F32, d=256) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(d=96) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(dtype=F16, d=96) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(dtype=F16, B=0, q=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
@@ -136,7 +137,7 @@ def test_backward_phase_entry_points_validate():
     assert pre(o=None) == fa.FA_ERROR_INVALID_VALUE
     assert pre(delta=MIS) == fa.FA_ERROR_INVALID_VALUE
     assert pre(d=96) == fa.FA_ERROR_UNSUPPORTED
-    assert pre(dtype=F32, d=64) == fa.FA_ERROR_UNSUPPORTED
+    assert pre(dtype=F32, d=96) == fa.FA_ERROR_UNSUPPORTED
     assert pre(N=0, o=None, do=None, delta=None) == fa.FA_SUCCESS
 
     def dkdv(q=A, dk=A, dv=A, delta=A, scale=0.1, causal=0, d=128, N=16):

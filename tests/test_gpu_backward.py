@@ -5,7 +5,9 @@ The GPU backward consumes the GPU forward's O and LSE (its own saved state);
 the oracle's gradients use its own fp64 forward.  Tolerance: dQ, dK, dV
 max-abs <= 5e-2 for bf16 inputs and <= 2e-2 for f16 (fp32 accumulation; f16
 rounds P, dS and the outputs 8x finer than bf16, the bound keeps a margin for
-the accumulation order) on the training-step workload.  Edge-case shapes can
+the accumulation order) on the training-step workload; <= 1e-4 for fp32 (fp32
+throughout: sums of a few hundred products of O(1) terms with relative
+rounding 2^-24 each, plus one ulp of |ref| where the gradient is large).  Edge-case shapes can
 make a gradient large (with key length 1, dV of key 0 sums dO over every
 row), and above |x| = 16 one bf16 half-ulp alone exceeds 5e-2; there the
 bound adds one ulp of |ref| in the format.
@@ -20,9 +22,9 @@ from tests.gpu_helpers import custom, device_inputs, from_device, lib, log_case,
 
 pytestmark = pytest.mark.gpu
 
-G_TOL = {"bf16": 5e-2, "f16": 2e-2}
-O_TOL = {"bf16": 2e-2, "f16": 5e-3}
-ULP = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+G_TOL = {"bf16": 5e-2, "f16": 2e-2, "f32": 1e-4}
+O_TOL = {"bf16": 2e-2, "f16": 5e-3, "f32": 1e-5}
+ULP = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -20}
 
 
 def run_fwd_bwd(torch, cfg, inputs, lengths=None):
@@ -73,7 +75,7 @@ def compare_heads(cfg, inputs, o, dq, dk, dv, heads, strict=False):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_small_shapes_all_heads(d, causal, dtype):
     torch = torch_cuda()
     for N in (1, 17, 64, 65, 129, 200, 257):
@@ -127,4 +129,31 @@ def test_backward_is_deterministic():
     r1 = run_fwd_bwd(torch, cfg, inputs)
     r2 = run_fwd_bwd(torch, cfg, inputs)
     for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+def test_config1_fp32_backward_every_head():
+    """The fp32 workload (one head, N=256, d=64) with dO, causal and not."""
+    torch = torch_cuda()
+    for causal in (False, True):
+        cfg = custom(1, causal=causal)
+        log_case(test="config1-bwd", shape=cfg.shape, causal=causal)
+        inputs = fi.make_inputs(cfg, with_grad=True, seed=21)
+        o, lse, dq, dk, dv = run_fwd_bwd(torch, cfg, inputs)
+        worst = compare_heads(cfg, inputs, o, dq, dk, dv, [(0, 0)], strict=True)
+        print(f"config1 fp32 causal={causal} grads max abs err {worst:.3e}", flush=True)
+
+
+def test_fp32_backward_phases_match_the_single_call():
+    torch = torch_cuda()
+    fa = lib()
+    cfg = custom(1, B=2, H=3, N=200, d=128, causal=True)
+    inputs = fi.make_inputs(cfg, with_grad=True, seed=4)
+    dev = device_inputs(torch, cfg, inputs)
+    o, lse = fa.forward(dev["q"], dev["k"], dev["v"], scale=cfg.scale, causal=True)
+    g1 = fa.backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, scale=cfg.scale, causal=True)
+    g2 = fa.backward_phases(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, scale=cfg.scale,
+                            causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
         assert torch.equal(a, b)
