@@ -24,7 +24,7 @@ fa::Elt elt_of(fa_dtype dtype) {
 }
 
 bool fwd_supported(fa_dtype dtype, int d) {
-  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128);
+  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128 || d == 256);
 }
 
 bool bwd_supported(fa_dtype dtype, int d) {
@@ -51,7 +51,7 @@ hipError_t bwd_dq(fa_dtype t, const fa::BwdArgs& a) {
 }
 
 bool decode_supported(fa_dtype dtype, int d) {
-  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128);
+  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128 || d == 256);
 }
 
 

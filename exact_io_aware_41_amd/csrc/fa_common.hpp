@@ -196,7 +196,9 @@ __device__ __forceinline__ void lds_barrier() {
 // a bank period, leaving 8 slots for 16 lanes).
 template <int D>
 __device__ __forceinline__ int row_swizzle(int row) {
-  if constexpr (D == 128)
+  // d = 256: rows of 512 bytes repeat the 256-byte bank pattern, so the
+  // d = 128 XOR of the low four chunk bits serves unchanged
+  if constexpr (D >= 128)
     return (row & 15) ^ (((row >> 4) & 1) * 12) ^ (((row >> 5) & 1) * 2);
   else
     return (row ^ (row >> 2)) & (D / 8 - 1);
@@ -224,7 +226,7 @@ __device__ __forceinline__ int tile_swizzle(int row) {
 // 4 x 64 bytes on 4 distinct 64-byte bank ranges (measured conflict-free).
 template <int D>
 __device__ __forceinline__ int seg_swizzle(int row) {
-  if constexpr (D == 128)
+  if constexpr (D >= 128)
     return row & 3;
   else
     return (row >> 1) & 1;

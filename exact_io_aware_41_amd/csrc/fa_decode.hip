@@ -312,8 +312,9 @@ DecodePlan decode_plan(int B, int H, int N) {
 template <typename T>
 hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, float* o_parts,
                            float* lse_parts) {
-  return a.d == 64 ? launch_decode_split<T, 64>(a, p, o_parts, lse_parts)
-                   : launch_decode_split<T, 128>(a, p, o_parts, lse_parts);
+  if (a.d == 64) return launch_decode_split<T, 64>(a, p, o_parts, lse_parts);
+  if (a.d == 128) return launch_decode_split<T, 128>(a, p, o_parts, lse_parts);
+  return launch_decode_split<T, 256>(a, p, o_parts, lse_parts);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, Elt elt) {

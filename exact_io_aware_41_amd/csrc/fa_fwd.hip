@@ -93,7 +93,7 @@ constexpr float kRescaleThreshold = 8.0f;
 
 template <class E, int D, int QB, int NW, int BC>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu(QB == 1 && D <= 128 ? 2 : 1, QB == 1 && D <= 128 ? 2 : 1)))
 void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
                         const typename E::T* __restrict__ V, const int32_t* __restrict__ seqlens_k,
                         float scale_log2, int causal, typename E::T* __restrict__ O,
@@ -515,6 +515,10 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   float m = kNegInf, l = 0.f;
 
   f32x4 kreg[C::KU], vreg[C::KU];
+  // up to d = 128 the next tile's K/V wait in registers during the compute;
+  // at d = 256 they would not fit beside Q and O, so the tile is copied
+  // after the compute instead
+  constexpr bool kStage = D <= 128;
   auto load_tile = [&](int kt) FA_INLINE {
     const int key0 = kt * BC;
 #pragma unroll
@@ -543,6 +547,29 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     }
   };
 
+  // unstaged copy (d = 256): each 16-byte chunk goes to LDS as soon as it
+  // arrives, so only a few registers are live
+  auto copy_tile = [&](int kt, int buf) FA_INLINE {
+    const int key0 = kt * BC;
+#pragma unroll 4
+    for (int i = 0; i < C::KU; ++i) {
+      const int u = tid + i * C::NT;
+      const int r = u / (D / 4);
+      const int c4 = u % (D / 4);
+      const int key = key0 + r;
+      const bool ok = key < kv_len;
+      const size_t at = (size_t)key * D + c4 * 4;
+      const f32x4 kx = ok ? *reinterpret_cast<const f32x4*>(Kh + at) : f32x4{};
+      const f32x4 vx = ok ? *reinterpret_cast<const f32x4*>(Vh + at) : f32x4{};
+      float* kd = &Ks[buf][r * C::KPITCH + c4 * 4];
+      kd[0] = kx[0];
+      kd[1] = kx[1];
+      kd[2] = kx[2];
+      kd[3] = kx[3];
+      *reinterpret_cast<f32x4*>(&Vs[buf][r * C::VPITCH + c4 * 4]) = vx;
+    }
+  };
+
   if (n_kt > 0) {
     load_tile(0);
     store_tile(0);
@@ -551,7 +578,7 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (kStage && kt + 1 < n_kt) load_tile(kt + 1);
     const int key0 = kt * BC;
     const bool wave_active = (qw0 < N) && (!causal || key0 <= qw0 + 31);
     if (wave_active) {
@@ -610,7 +637,12 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
             oacc[db] = mfma_f32(Vs[buf][key * C::VPITCH + db * 32 + l32], sacc[c][v], oacc[db]);
         }
     }
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    if (kt + 1 < n_kt) {
+      if (kStage)
+        store_tile(buf ^ 1);
+      else
+        copy_tile(kt + 1, buf ^ 1);
+    }
     __syncthreads();
   }
 
@@ -631,21 +663,27 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   }
 }
 
-constexpr int kBf16QB = FA_FWD_QB, kBf16NW = FA_FWD_NW;
+constexpr int kBf16QB = FA_FWD_QB;
+// Up to d = 128 a wave fits 256 VGPRs: 8 waves, two per SIMD in opposite
+// phases, 128-key tiles.  At d = 256 the O accumulators and Q fragments alone
+// take 192 VGPRs: 4 waves, one per SIMD with up to 512 VGPRs, 64-key tiles
+// (K and V two slots each: 128 KiB of LDS).
 template <int D>
 struct Bf16Tile {
-  static constexpr int BC = FA_FWD_BC;
+  static constexpr int BC = D <= 128 ? FA_FWD_BC : 64;
+  static constexpr int NW = D <= 128 ? FA_FWD_NW : 4;
 };
 constexpr int kF32NW = 2, kF32BC = 32;
 
 template <class E, int D>
 hipError_t launch_half_d(const FwdArgs& a) {
   constexpr int BC = Bf16Tile<D>::BC;
-  using C = FwdBf16Cfg<D, kBf16QB, kBf16NW, BC>;
+  constexpr int NW = Bf16Tile<D>::NW;
+  using C = FwdBf16Cfg<D, kBf16QB, NW, BC>;
   using T = typename E::T;
   const int n_qtiles = (a.N + C::BR - 1) / C::BR;
   const dim3 grid((unsigned)((long long)n_qtiles * a.B * a.H));
-  hipLaunchKernelGGL((fa_fwd_half_kernel<E, D, kBf16QB, kBf16NW, BC>), grid, dim3(C::NT), 0,
+  hipLaunchKernelGGL((fa_fwd_half_kernel<E, D, kBf16QB, NW, BC>), grid, dim3(C::NT), 0,
                      a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), a.seqlens_k, a.scale * kLog2e, a.causal,
                      static_cast<T*>(a.o), a.lse, a.B, a.H, a.N, n_qtiles);
@@ -657,6 +695,7 @@ hipError_t launch_half_e(const FwdArgs& a) {
   switch (a.d) {
     case 64: return launch_half_d<E, 64>(a);
     case 128: return launch_half_d<E, 128>(a);
+    case 256: return launch_half_d<E, 256>(a);
     default: return hipErrorInvalidValue;
   }
 }
@@ -676,8 +715,7 @@ hipError_t launch_f32_d(const FwdArgs& a) {
 }  // namespace
 
 long long fwd_half_grid(int B, int H, int N, int d) {
-  const int BR = kBf16NW * kBf16QB * 32;
-  (void)d;
+  const int BR = (d <= 128 ? Bf16Tile<128>::NW : Bf16Tile<256>::NW) * kBf16QB * 32;
   return (long long)((N + BR - 1) / BR) * B * H;
 }
 
@@ -697,6 +735,7 @@ hipError_t launch_fwd_f32(const FwdArgs& a) {
   switch (a.d) {
     case 64: return launch_f32_d<64>(a);
     case 128: return launch_f32_d<128>(a);
+    case 256: return launch_f32_d<256>(a);
     default: return hipErrorInvalidValue;
   }
 }

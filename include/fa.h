@@ -57,14 +57,15 @@
  *                          kernel surface at the caller's next synchronise.
  *
  * Compiled (dtype, d) set:
- *  forward : FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128}
+ *  forward : FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128, 256}
  *  backward: FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128}
  *            (fp32 on the fp32 MFMA: fp32 inputs, arithmetic and outputs)
  *  decode and merge: FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in
- *  {64, 128}
- * The 16-bit formats are those the pages list for fused kernels ("What is
- * FlashAttention?", "Trade-offs and edge cases"); both run the same kernels,
- * on the MFMA of their format, with fp32 accumulation and statistics.
+ *  {64, 128, 256}
+ * The 16-bit formats and head dimensions up to 256 are those the pages list
+ * for fused kernels ("What is FlashAttention?", "Trade-offs and edge cases");
+ * both 16-bit formats run the same kernels, on the MFMA of their format, with
+ * fp32 accumulation and statistics.
  */
 #ifndef FA_MI355X_FA_H
 #define FA_MI355X_FA_H

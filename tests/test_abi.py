@@ -73,8 +73,8 @@ def test_forward_rejects_invalid_arguments(kw):
     assert fwd(**kw) == fa.FA_ERROR_INVALID_VALUE
 
 
-@pytest.mark.parametrize("dtype,d", [(BF16, 96), (BF16, 256), (BF16, 32), (F32, 96), (F32, 16),
-                                     (F16, 96), (F16, 256)])
+@pytest.mark.parametrize("dtype,d", [(BF16, 96), (BF16, 512), (BF16, 32), (F32, 96), (F32, 16),
+                                     (F32, 192), (F16, 96), (F16, 512)])
 def test_forward_unsupported_shapes_fail_loudly(dtype, d):
     assert fwd(dtype=dtype, d=d) == fa.FA_ERROR_UNSUPPORTED
 
@@ -107,6 +107,7 @@ def test_backward_rejects_invalid_arguments(kw):
 def test_backward_unsupported_and_workspace_size():
     assert bwd(dtype=F32, d=96) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(dtype=F32, d=256) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(d=256) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(d=96) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(dtype=F16, d=96) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(dtype=F16, B=0, q=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
@@ -177,7 +178,7 @@ def test_decode_rejects_invalid_arguments(kw):
 
 def test_decode_unsupported_and_empty():
     assert dec(d=96) == fa.FA_ERROR_UNSUPPORTED
-    assert dec(dtype=F32, d=256) == fa.FA_ERROR_UNSUPPORTED
+    assert dec(dtype=F32, d=512) == fa.FA_ERROR_UNSUPPORTED
     assert dec(B=0, q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
     assert dec(N=0, q=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
     assert dec(dtype=F16, d=96) == fa.FA_ERROR_UNSUPPORTED

@@ -60,7 +60,7 @@ def oracle_decode(cfg, inputs, heads=None):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N,lengths", [
     (1, None), (63, None), (300, "zero_then_uniform"), (300, [300, 1, 0]), (5000, None),
     (5000, [4097, 4096, 64]), (9000, "zero_then_uniform"),
