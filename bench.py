@@ -76,6 +76,10 @@ def parse_args():
     p.add_argument("--workload", default="attention", choices=["attention", "decode"],
                    help="attention: the --config workload (default, the headline metric); "
                         "decode: one query row per head against an 8192-position cache")
+    p.add_argument("--dtype", default=None, choices=["bf16", "f16", "f32"],
+                   help="run the --config workload in another element format (default: its own)")
+    p.add_argument("--head-dim", type=int, default=None, choices=[64, 128, 256],
+                   help="run the --config workload with another head dimension")
     p.add_argument("--decode-lengths", default=None, choices=[None, "zero_then_uniform"],
                    help="cached lengths of the decode workload (default: all full)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -166,6 +170,14 @@ def main():
         decode_main(args)
         return
     cfg = fi.CONFIGS[args.config]
+    variant = {}
+    if args.dtype is not None and args.dtype != cfg.dtype:
+        variant["dtype"] = args.dtype
+    if args.head_dim is not None and args.head_dim != cfg.d:
+        variant["d"] = args.head_dim
+    if variant:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, **variant)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -174,8 +186,9 @@ def main():
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s: {cfg.name}")
 
     def up(a):
-        if cfg.dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        if cfg.dtype in fi.HALF_DTYPES:
+            half = torch.bfloat16 if cfg.dtype == "bf16" else torch.float16
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(half)
         return torch.from_numpy(a).to(dev)
 
     q, k, v = up(inputs["q"]), up(inputs["k"]), up(inputs["v"])
@@ -225,7 +238,8 @@ def main():
     lengths = inputs["lengths"]
     flops = step_flops(cfg, lengths)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    # bf16 and f16 share the dense MFMA peak; fp32 runs on the fp32 MFMA
+    peak = PEAK_BF16_TFLOPS if cfg.dtype in fi.HALF_DTYPES else PEAK_F32_TFLOPS
 
     # credited FLOPs per launch of each compute kernel
     if lengths is None:
@@ -240,7 +254,7 @@ def main():
     achieved = kernel_flops[dominant] / (per_kernel[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic(dominant, args.config)}
+                "traffic": None if variant else measured_traffic(dominant, args.config)}
 
     extra = {
         "per_launch_ms": {n: round(t, 4) for n, t in per_kernel.items()},
