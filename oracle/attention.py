@@ -6,15 +6,21 @@ works on float64 NumPy arrays holding the exact values the GPU receives
 (bf16 or fp32 inputs widened without rounding); it shares no code with the
 HIP kernels.
 
-Layout: q, k, v, o, do are [B, H, N, d]; lse is [B, H, N]; lengths is a
-length-B integer array of key lengths (or None for "all N keys valid").
+Layout: q, o, do are [B, H, Nq, d]; k, v are [B, H, Nk, d]; lse is
+[B, H, Nq]; lengths is a length-B integer array of key lengths (or None for
+"all Nk keys valid").  Usually Nq == Nk == N.
 
 Semantics (the plain definition the tiled method reaches exactly):
-  s_ij = scale * q_i . k_j, visible(i, j) = j < L_b and (not causal or j <= i);
+  s_ij = scale * q_i . k_j,
+  visible(i, j) = j < L_b and (not causal or j <= i + Nk - Nq);
   for a row with a non-empty visible set V_i:
       m_i = max_{j in V_i} s_ij,  l_i = sum_{j in V_i} exp(s_ij - m_i),
       O_i = sum_{j in V_i} exp(s_ij - m_i) v_j / l_i,  LSE_i = m_i + ln l_i;
   for a row with nothing visible: O_i = 0, LSE_i = -inf.
+The pages define the causal mask for square problems (j <= i).  With Nq !=
+Nk the queries are read as the last Nq positions of a sequence of Nk
+("bottom-right" alignment: the last query sees every key), which keeps the
+square case unchanged and makes one query against a cache see all of it.
 
 Citations are to the three source pages:
   [clozo]  "What is FlashAttention?" (interview.clozo.ai)
@@ -53,10 +59,11 @@ def _clamp_length(length, n):
     return int(min(max(int(length), 0), n))
 
 
-def visible_mask(rows, n_keys, causal, length=None, keys=None):
+def visible_mask(rows, n_keys, causal, length=None, keys=None, offset=0):
     """Boolean [len(rows), len(keys)] mask of visible (query, key) pairs.
 
-    `keys` are absolute key positions (default: all n_keys of them).
+    `keys` are absolute key positions (default: all n_keys of them); query
+    row i sits at sequence position i + offset (offset = Nk - Nq).
     Positions are absolute sequence positions, never tile-local ones
     ([infra] "Executable recurrence, with an empty-state policy": the causal
     mask uses global query and key positions across tile boundaries).  The
@@ -68,7 +75,7 @@ def visible_mask(rows, n_keys, causal, length=None, keys=None):
     vis = np.broadcast_to(keys[None, :] < _clamp_length(length, n_keys),
                           (rows.size, keys.size)).copy()
     if causal:
-        vis &= keys[None, :] <= rows[:, None]
+        vis &= keys[None, :] <= rows[:, None] + int(offset)
     return vis
 
 
@@ -85,7 +92,7 @@ def scaled_scores(q_rows, k, scale):
 # Route A: materialised stable softmax (the plain definition)
 # ---------------------------------------------------------------------------
 
-def _rows_materialised(q_rows, rows, k, v, scale, causal, length):
+def _rows_materialised(q_rows, rows, k, v, scale, causal, length, offset=0):
     """O and LSE for the given absolute query rows of one head.
 
     Stable softmax with the row maximum subtracted before exponentiation
@@ -93,7 +100,7 @@ def _rows_materialised(q_rows, rows, k, v, scale, causal, length):
     exp representable without changing the ratio).
     """
     s = scaled_scores(q_rows, k, scale)
-    vis = visible_mask(rows, k.shape[0], causal, length)
+    vis = visible_mask(rows, k.shape[0], causal, length, offset=offset)
     s = np.where(vis, s, -np.inf)
     nonempty = vis.any(axis=1)
     m = np.where(nonempty, s.max(axis=1, initial=-np.inf), 0.0)
@@ -117,6 +124,7 @@ def attention_materialised(q, k, v, scale, causal=False, lengths=None, row_block
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     B, H, N, d = q.shape
+    offset = k.shape[2] - N
     o = np.zeros((B, H, N, v.shape[3]))
     lse = np.empty((B, H, N))
     for b in range(B):
@@ -125,7 +133,7 @@ def attention_materialised(q, k, v, scale, causal=False, lengths=None, row_block
             for r0 in range(0, N, row_block):
                 rows = np.arange(r0, min(N, r0 + row_block))
                 o[b, h, rows], lse[b, h, rows] = _rows_materialised(
-                    q[b, h, rows], rows, k[b, h], v[b, h], scale, causal, length)
+                    q[b, h, rows], rows, k[b, h], v[b, h], scale, causal, length, offset)
     return o, lse
 
 
@@ -135,10 +143,11 @@ def attention_rows(q_head, k_head, v_head, rows, scale, causal=False, length=Non
     Used to check sampled outputs of full-size problems row by row.
     """
     rows = np.asarray(rows, dtype=np.int64)
+    offset = np.asarray(k_head).shape[0] - np.asarray(q_head).shape[0]
     return _rows_materialised(np.asarray(q_head, np.float64)[rows], rows,
                               np.asarray(k_head, np.float64),
                               np.asarray(v_head, np.float64),
-                              scale, causal, length)
+                              scale, causal, length, offset)
 
 
 # ---------------------------------------------------------------------------
@@ -251,7 +260,7 @@ def attention_online(q, k, v, scale, causal=False, lengths=None, tile=64,
             for j0 in range(0, Nk, tile):
                 cols = slice(j0, min(Nk, j0 + tile))
                 vis = visible_mask(rows, Nk, causal, length,
-                                   keys=np.arange(j0, min(Nk, j0 + tile)))
+                                   keys=np.arange(j0, min(Nk, j0 + tile)), offset=Nk - N)
                 live = vis.any(axis=1)            # rows with something visible here
                 if not live.any():
                     continue
@@ -305,7 +314,7 @@ def attention_backward(q, k, v, o, do, lse, scale, causal=False, lengths=None,
             for r0 in range(0, N, row_block):
                 rows = np.arange(r0, min(N, r0 + row_block))
                 s = scaled_scores(q[b, h, rows], k[b, h], scale)
-                vis = visible_mask(rows, k.shape[2], causal, length)
+                vis = visible_mask(rows, k.shape[2], causal, length, offset=k.shape[2] - N)
                 row_lse = lse[b, h, rows]
                 ok = vis & np.isfinite(row_lse)[:, None]
                 p = np.where(ok, np.exp(np.where(ok, s - row_lse[:, None], 0.0)), 0.0)

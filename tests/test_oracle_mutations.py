@@ -40,12 +40,12 @@ def test_transposed_operand_is_caught(monkeypatch):
 def test_causal_off_by_one_is_caught(monkeypatch):
     real = oa.visible_mask
 
-    def strict(rows, n_keys, causal, length=None, keys=None):
-        vis = real(rows, n_keys, causal, length, keys)
+    def strict(rows, n_keys, causal, length=None, keys=None, offset=0):
+        vis = real(rows, n_keys, causal, length, keys, offset)
         if causal:
             rows_a = np.asarray(rows).reshape(-1)
             keys_a = np.arange(n_keys) if keys is None else np.asarray(keys).reshape(-1)
-            vis &= keys_a[None, :] < rows_a[:, None]
+            vis &= keys_a[None, :] < rows_a[:, None] + offset
         return vis
 
     monkeypatch.setattr(oa, "visible_mask", strict)
@@ -56,8 +56,9 @@ def test_causal_off_by_one_is_caught(monkeypatch):
 def test_length_off_by_one_is_caught(monkeypatch):
     real = oa.visible_mask
 
-    def loose(rows, n_keys, causal, length=None, keys=None):
-        return real(rows, n_keys, causal, None if length is None else int(length) + 1, keys)
+    def loose(rows, n_keys, causal, length=None, keys=None, offset=0):
+        return real(rows, n_keys, causal, None if length is None else int(length) + 1, keys,
+                    offset)
 
     monkeypatch.setattr(oa, "visible_mask", loose)
     assert _fails(pins.test_brute_force_every_mask_combination_tiny)
@@ -119,3 +120,17 @@ def test_decode_key_range_off_by_one_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "attention_decode", one_more)
     assert _fails(pins.test_decode_matches_torch_sdpa_with_lengths, 7)
     assert _fails(pins.test_decode_closed_forms)
+
+
+def test_top_left_rectangular_alignment_is_caught(monkeypatch):
+    """Dropping the Nk - Nq offset (top-left alignment) breaks the rectangular
+    pins while every square pin still holds."""
+    real = oa.visible_mask
+
+    def top_left(rows, n_keys, causal, length=None, keys=None, offset=0):
+        return real(rows, n_keys, causal, length, keys, 0)
+
+    monkeypatch.setattr(oa, "visible_mask", top_left)
+    assert _fails(pins.test_fewer_queries_are_the_last_rows_of_the_square_problem)
+    assert _fails(pins.test_one_causal_query_sees_the_whole_cache)
+    assert _fails(pins.test_more_queries_than_keys_leave_the_first_rows_empty)

@@ -321,7 +321,8 @@ def _brute_force_decimal(q, k, v, scale, causal, length):
         num = [Decimal(0)] * v.shape[1]
         den = Decimal(0)
         for j in range(Nk):
-            if j >= L or (causal and j > i):
+            # query i sits at sequence position i + Nk - N (bottom-right)
+            if j >= L or (causal and j > i + Nk - N):
                 continue
             s = sc * sum(Decimal(float(q[i, t])) * Decimal(float(k[j, t])) for t in range(d))
             w = s.exp()
@@ -376,6 +377,71 @@ def test_online_row_matches_brute_force_with_masks():
         for T in (1, 2, 3, 5, 16):
             out = oracle.online_row(s, vals, tile=T)
             assert np.max(np.abs(out - ref)) <= 1e-14
+
+
+def test_fewer_queries_are_the_last_rows_of_the_square_problem():
+    """Causal attention of Nq queries against Nk keys equals the last Nq rows
+    of the square causal problem whose queries end with them (the rows before
+    do not influence later rows), for every key length."""
+    rng = np.random.default_rng(31)
+    Nk, Nq, d = 23, 7, 5
+    k, v = rng.standard_normal((2, 1, 1, Nk, d))
+    q_full = rng.standard_normal((1, 1, Nk, d))
+    for length in (None, np.array([0]), np.array([3]), np.array([20]), np.array([23])):
+        o_sq, l_sq = oracle.attention_materialised(q_full, k, v, 0.7, True, length)
+        o_r, l_r = oracle.attention_materialised(q_full[:, :, Nk - Nq:], k, v, 0.7, True, length)
+        assert np.array_equal(np.isneginf(l_r), np.isneginf(l_sq[:, :, Nk - Nq:]))
+        assert np.max(np.abs(o_r - o_sq[:, :, Nk - Nq:])) <= 1e-13
+        fin = np.isfinite(l_r)
+        if fin.any():
+            assert np.max(np.abs(l_r[fin] - l_sq[:, :, Nk - Nq:][fin])) <= 1e-13
+        # the online route agrees
+        o_b, l_b = oracle.attention_online(q_full[:, :, Nk - Nq:], k, v, 0.7, True, length, tile=4)
+        assert np.max(np.abs(o_b - o_r)) <= 1e-13
+
+
+def test_more_queries_than_keys_leave_the_first_rows_empty():
+    """With Nq > Nk the first Nq - Nk queries precede every key: O = 0 and
+    LSE = -inf; the remaining rows are the square problem over the Nk keys."""
+    rng = np.random.default_rng(32)
+    Nk, Nq, d = 9, 14, 4
+    q = rng.standard_normal((1, 2, Nq, d))
+    k, v = rng.standard_normal((2, 1, 2, Nk, d))
+    o, lse = oracle.attention_materialised(q, k, v, 0.5, True)
+    assert np.all(o[:, :, :Nq - Nk] == 0.0) and np.all(np.isneginf(lse[:, :, :Nq - Nk]))
+    o_sq, l_sq = oracle.attention_materialised(q[:, :, Nq - Nk:], k, v, 0.5, True)
+    assert np.max(np.abs(o[:, :, Nq - Nk:] - o_sq)) <= 1e-14
+    assert np.max(np.abs(lse[:, :, Nq - Nk:] - l_sq)) <= 1e-14
+
+
+def test_one_causal_query_sees_the_whole_cache():
+    """Nq = 1 with the causal mask is decoding: the query sees every valid key,
+    as the independent decode routine computes it."""
+    rng = np.random.default_rng(33)
+    B, H, Nk, d = 3, 2, 40, 6
+    q = rng.standard_normal((B, H, 1, d))
+    k, v = rng.standard_normal((2, B, H, Nk, d))
+    lengths = np.array([40, 17, 0])
+    o, lse = oracle.attention_materialised(q, k, v, 0.3, True, lengths)
+    o_d, l_d = oracle.attention_decode(q[:, :, 0], k, v, 0.3, lengths)
+    assert np.max(np.abs(o[:, :, 0] - o_d)) <= 1e-13
+    assert np.array_equal(np.isneginf(lse[:, :, 0]), np.isneginf(l_d))
+    fin = np.isfinite(l_d)
+    assert fin.sum() == 4        # sequence 2 has an empty cache
+    assert np.max(np.abs(lse[:, :, 0][fin] - l_d[fin])) <= 1e-13
+
+
+def test_rectangular_backward_matches_finite_differences():
+    rng = np.random.default_rng(34)
+    for Nq, Nk, lengths in ((3, 7, None), (6, 4, None), (4, 8, np.array([5]))):
+        q = rng.standard_normal((1, 1, Nq, 3))
+        k, v = rng.standard_normal((2, 1, 1, Nk, 3))
+        do = rng.standard_normal((1, 1, Nq, 3))
+        o, lse = oracle.attention_materialised(q, k, v, 0.8, True, lengths)
+        g = oracle.attention_backward(q, k, v, o, do, lse, 0.8, True, lengths)
+        fd = oracle.finite_difference_grads(q, k, v, do, 0.8, True, lengths)
+        for a, b in zip(g, fd):
+            assert np.max(np.abs(a - b)) <= 1e-6
 
 
 def test_rectangular_and_rows_helper():
