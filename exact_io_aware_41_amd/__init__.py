@@ -75,20 +75,21 @@ def load_library():
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [i32]
     lib.fa_forward.restype = i32
-    lib.fa_forward.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, f32, i32, vp, vp, vp]
+    lib.fa_forward.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, f32, i32, vp, vp,
+                               vp]
     lib.fa_backward_workspace_size.restype = sz
     lib.fa_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_backward.restype = i32
-    lib.fa_backward.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, i32,
-                                vp, vp, vp, vp, sz, vp]
+    lib.fa_backward.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32,
+                                i32, vp, vp, vp, vp, sz, vp]
     lib.fa_backward_preprocess.restype = i32
     lib.fa_backward_preprocess.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.fa_backward_dkdv.restype = i32
-    lib.fa_backward_dkdv.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32,
-                                     i32, vp, vp, vp]
+    lib.fa_backward_dkdv.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                     f32, i32, vp, vp, vp]
     lib.fa_backward_dq.restype = i32
-    lib.fa_backward_dq.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, i32,
-                                   vp, vp]
+    lib.fa_backward_dq.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32,
+                                   i32, vp, vp]
     lib.fa_decode_workspace_size.restype = sz
     lib.fa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_decode.restype = i32
@@ -111,35 +112,37 @@ def fa_status_string(status: int) -> str:
     return load_library().fa_status_string(int(status)).decode()
 
 
-def fa_forward(dtype, B, H, N, d, q, k, v, seqlens_k, scale, causal, o, lse, stream=0) -> int:
-    return load_library().fa_forward(dtype, B, H, N, d, q, k, v, seqlens_k, scale, causal, o,
-                                     lse, stream)
+def fa_forward(dtype, B, H, Nq, Nk, d, q, k, v, seqlens_k, scale, causal, o, lse,
+               stream=0) -> int:
+    return load_library().fa_forward(dtype, B, H, Nq, Nk, d, q, k, v, seqlens_k, scale, causal,
+                                     o, lse, stream)
 
 
 def fa_backward_workspace_size(dtype, B, H, N, d) -> int:
     return load_library().fa_backward_workspace_size(dtype, B, H, N, d)
 
 
-def fa_backward(dtype, B, H, N, d, q, k, v, o, dout, lse, seqlens_k, scale, causal, dq, dk, dv,
-                workspace, workspace_bytes, stream=0) -> int:
-    return load_library().fa_backward(dtype, B, H, N, d, q, k, v, o, dout, lse, seqlens_k, scale,
-                                      causal, dq, dk, dv, workspace, workspace_bytes, stream)
+def fa_backward(dtype, B, H, Nq, Nk, d, q, k, v, o, dout, lse, seqlens_k, scale, causal, dq, dk,
+                dv, workspace, workspace_bytes, stream=0) -> int:
+    return load_library().fa_backward(dtype, B, H, Nq, Nk, d, q, k, v, o, dout, lse, seqlens_k,
+                                      scale, causal, dq, dk, dv, workspace, workspace_bytes,
+                                      stream)
 
 
 def fa_backward_preprocess(dtype, B, H, N, d, o, dout, delta, stream=0) -> int:
     return load_library().fa_backward_preprocess(dtype, B, H, N, d, o, dout, delta, stream)
 
 
-def fa_backward_dkdv(dtype, B, H, N, d, q, k, v, dout, lse, delta, seqlens_k, scale, causal, dk,
-                     dv, stream=0) -> int:
-    return load_library().fa_backward_dkdv(dtype, B, H, N, d, q, k, v, dout, lse, delta,
+def fa_backward_dkdv(dtype, B, H, Nq, Nk, d, q, k, v, dout, lse, delta, seqlens_k, scale, causal,
+                     dk, dv, stream=0) -> int:
+    return load_library().fa_backward_dkdv(dtype, B, H, Nq, Nk, d, q, k, v, dout, lse, delta,
                                            seqlens_k, scale, causal, dk, dv, stream)
 
 
-def fa_backward_dq(dtype, B, H, N, d, q, k, v, dout, lse, delta, seqlens_k, scale, causal, dq,
-                   stream=0) -> int:
-    return load_library().fa_backward_dq(dtype, B, H, N, d, q, k, v, dout, lse, delta, seqlens_k,
-                                         scale, causal, dq, stream)
+def fa_backward_dq(dtype, B, H, Nq, Nk, d, q, k, v, dout, lse, delta, seqlens_k, scale, causal,
+                   dq, stream=0) -> int:
+    return load_library().fa_backward_dq(dtype, B, H, Nq, Nk, d, q, k, v, dout, lse, delta,
+                                         seqlens_k, scale, causal, dq, stream)
 
 
 def fa_decode_workspace_size(dtype, B, H, N, d) -> int:
@@ -179,6 +182,18 @@ def _check_like(name, t, ref):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_keys(name, t, k, q):
+    """k-shaped tensors: [B, H, Nk, d] with q's batch, heads, head dim, dtype
+    and device."""
+    if (t.dim() != 4 or t.shape != k.shape or t.shape[0] != q.shape[0]
+            or t.shape[1] != q.shape[1] or t.shape[3] != q.shape[3]
+            or t.dtype != q.dtype or t.device != q.device):
+        raise ValueError(f"{name} must be [B, H, Nk, d] like k, with q's B, H, d, dtype and "
+                         f"device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -199,17 +214,21 @@ def _lengths(seqlens_k, q):
 
 
 def forward(q, k, v, scale=None, causal=False, seqlens_k=None, out=None, lse=None):
-    """O, LSE = attention(q, k, v) for [B, H, N, d] CUDA tensors.
+    """O, LSE = attention(q, k, v) for CUDA tensors q [B, H, Nq, d] and
+    k, v [B, H, Nk, d] (usually Nq == Nk).
 
     ``scale`` defaults to 1/sqrt(d); ``seqlens_k`` is an optional int32 [B]
-    tensor of key lengths.  Returns (o, lse) with lse fp32 [B, H, N].
+    tensor of key lengths; with ``causal`` query i sees keys j <= i + Nk - Nq.
+    Returns (o, lse) with o like q and lse fp32 [B, H, Nq].
     """
     import torch
-    if q.dim() != 4:
-        raise ValueError("q must be [B, H, N, d]")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_like(name, t, q)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d] and k [B, H, Nk, d]")
+    _check_like("q", q, q)
+    for name, t in (("k", k), ("v", v)):
+        _check_keys(name, t, k, q)
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     seqlens_k = _lengths(seqlens_k, q)
@@ -220,7 +239,7 @@ def forward(q, k, v, scale=None, causal=False, seqlens_k=None, out=None, lse=Non
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
-    st = fa_forward(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens_k),
+    st = fa_forward(_dtype_code(q), B, H, N, Nk, d, _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens_k),
                     float(scale), int(bool(causal)), _ptr(out), _ptr(lse), _stream(q.device))
     if st != FA_SUCCESS:
         raise FAError(st, "fa_forward")
@@ -229,26 +248,31 @@ def forward(q, k, v, scale=None, causal=False, seqlens_k=None, out=None, lse=Non
 
 def backward(q, k, v, o, do, lse, scale=None, causal=False, seqlens_k=None,
              dq=None, dk=None, dv=None, workspace=None):
-    """dQ, dK, dV of <dO, O> for the tensors of a previous ``forward`` call."""
+    """dQ, dK, dV of <dO, O> for the tensors of a previous ``forward`` call
+    (q, o, do, dq [B, H, Nq, d]; k, v, dk, dv [B, H, Nk, d])."""
     import torch
-    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+    for name, t in (("o", o), ("do", do)):
         _check_like(name, t, q)
+    for name, t in (("k", k), ("v", v)):
+        _check_keys(name, t, k, q)
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     seqlens_k = _lengths(seqlens_k, q)
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
     dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_like(name, t, q)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    _check_like("dq", dq, q)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check_keys(name, t, k, q)
     code = _dtype_code(q)
     ws_bytes = fa_backward_workspace_size(code, B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-    st = fa_backward(code, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+    st = fa_backward(code, B, H, N, Nk, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
                      _ptr(seqlens_k), float(scale), int(bool(causal)), _ptr(dq), _ptr(dk),
                      _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
                      _stream(q.device))
@@ -266,15 +290,21 @@ def backward_phases(q, k, v, o, do, lse, scale=None, causal=False, seqlens_k=Non
     launch can be timed on the stream it runs on.
     """
     import torch
-    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+    for name, t in (("o", o), ("do", do)):
         _check_like(name, t, q)
+    for name, t in (("k", k), ("v", v)):
+        _check_keys(name, t, k, q)
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     seqlens_k = _lengths(seqlens_k, q)
     dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    _check_like("dq", dq, q)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check_keys(name, t, k, q)
     if delta is None:
         delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     code = _dtype_code(q)
@@ -285,13 +315,13 @@ def backward_phases(q, k, v, o, do, lse, scale=None, causal=False, seqlens_k=Non
     if st != FA_SUCCESS:
         raise FAError(st, "fa_backward_preprocess")
     rec(1)
-    st = fa_backward_dkdv(code, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+    st = fa_backward_dkdv(code, B, H, N, Nk, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
                           _ptr(delta), _ptr(seqlens_k), float(scale), int(bool(causal)), _ptr(dk),
                           _ptr(dv), stream)
     if st != FA_SUCCESS:
         raise FAError(st, "fa_backward_dkdv")
     rec(2)
-    st = fa_backward_dq(code, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+    st = fa_backward_dq(code, B, H, N, Nk, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
                         _ptr(delta), _ptr(seqlens_k), float(scale), int(bool(causal)), _ptr(dq),
                         stream)
     if st != FA_SUCCESS:

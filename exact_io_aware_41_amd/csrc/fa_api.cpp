@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr long long kMaxGrid = 0x7fffffffLL;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -90,23 +90,25 @@ const char* fa_status_string(fa_status s) {
   return "FA_ERROR_UNKNOWN";
 }
 
-fa_status fa_forward(fa_dtype dtype, int B, int H, int N, int d, const void* q, const void* k,
-                     const void* v, const int32_t* seqlens_k, float scale, int causal, void* o,
-                     float* lse, hipStream_t stream) {
+fa_status fa_forward(fa_dtype dtype, int B, int H, int Nq, int Nk, int d, const void* q,
+                     const void* k, const void* v, const int32_t* seqlens_k, float scale,
+                     int causal, void* o, float* lse, hipStream_t stream) {
   bool empty = false;
-  fa_status st = check_common(dtype, B, H, N, d, scale, causal, &empty);
+  fa_status st = check_common(dtype, B, H, Nq, d, scale, causal, &empty);
   if (st != FA_SUCCESS) return st;
+  if (Nk < 0) return FA_ERROR_INVALID_VALUE;
   if (!fwd_supported(dtype, d)) return FA_ERROR_UNSUPPORTED;
-  if (empty) return FA_SUCCESS;
-  if (!q || !k || !v || !o || !lse) return FA_ERROR_INVALID_VALUE;
+  if (empty) return FA_SUCCESS;   // no query rows: nothing to write
+  // with no keys the rows are written empty and k, v are never read
+  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA_ERROR_INVALID_VALUE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERROR_INVALID_VALUE;
   if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
-  const long long grid = is_half(dtype) ? fa::fwd_half_grid(B, H, N, d)
-                                        : fa::fwd_f32_grid(B, H, N, d);
+  const long long grid = is_half(dtype) ? fa::fwd_half_grid(B, H, Nq, d)
+                                        : fa::fwd_f32_grid(B, H, Nq, d);
   if (grid > kMaxGrid) return FA_ERROR_INVALID_VALUE;
 
-  fa::FwdArgs a{B, H, N, d, q, k, v, seqlens_k, scale, causal, o, lse, stream};
+  fa::FwdArgs a{B, H, Nq, d, Nk, q, k, v, seqlens_k, scale, causal, o, lse, stream};
   const hipError_t e =
       is_half(dtype) ? fa::launch_fwd_half(a, elt_of(dtype)) : fa::launch_fwd_f32(a);
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
@@ -119,28 +121,32 @@ size_t fa_backward_workspace_size(fa_dtype dtype, int B, int H, int N, int d) {
   return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
 }
 
-fa_status fa_backward(fa_dtype dtype, int B, int H, int N, int d, const void* q, const void* k,
-                      const void* v, const void* o, const void* dout, const float* lse,
-                      const int32_t* seqlens_k, float scale, int causal, void* dq, void* dk,
-                      void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+fa_status fa_backward(fa_dtype dtype, int B, int H, int Nq, int Nk, int d, const void* q,
+                      const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, const int32_t* seqlens_k, float scale, int causal,
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
   bool empty = false;
-  fa_status st = check_common(dtype, B, H, N, d, scale, causal, &empty);
+  fa_status st = check_common(dtype, B, H, Nq, d, scale, causal, &empty);
   if (st != FA_SUCCESS) return st;
+  if (Nk < 0) return FA_ERROR_INVALID_VALUE;
   if (!bwd_supported(dtype, d)) return FA_ERROR_UNSUPPORTED;
-  if (empty) return FA_SUCCESS;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
-    return FA_ERROR_INVALID_VALUE;
+  // with no query rows dK and dV are still written (zeros); with no keys, dQ.
+  // Buffers of a side without rows are never touched and may be NULL.
+  if (B == 0 || H == 0 || (Nq == 0 && Nk == 0)) return FA_SUCCESS;
+  if (Nq > 0 && (!q || !o || !dout || !lse || !dq || !workspace)) return FA_ERROR_INVALID_VALUE;
+  if (Nk > 0 && (!k || !v || !dk || !dv)) return FA_ERROR_INVALID_VALUE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       !aligned16(workspace))
     return FA_ERROR_INVALID_VALUE;
   if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
-  if (workspace_bytes < fa_backward_workspace_size(dtype, B, H, N, d))
+  if (workspace_bytes < fa_backward_workspace_size(dtype, B, H, Nq, d))
     return FA_ERROR_INVALID_VALUE;
-  if (bwd_grid(dtype, B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  if (bwd_grid(dtype, B, H, Nq > Nk ? Nq : Nk, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
 
-  fa::BwdArgs a{B,     H,       N,          d,      q,  k,  v,  o,  dout,
-                lse,   seqlens_k, scale,    causal, dq, dk, dv, static_cast<float*>(workspace),
+  fa::BwdArgs a{B,  H,  Nq, d,    Nk,        q,     k,      v,  o,  dout,
+                lse, seqlens_k, scale, causal, dq, dk, dv, static_cast<float*>(workspace),
                 stream};
   const hipError_t e = bwd_all(dtype, a);
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
@@ -157,54 +163,62 @@ fa_status fa_backward_preprocess(fa_dtype dtype, int B, int H, int N, int d, con
   if (!o || !dout || !delta) return FA_ERROR_INVALID_VALUE;
   if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return FA_ERROR_INVALID_VALUE;
   if (bwd_grid(dtype, B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
-  fa::BwdArgs a{B, H, N, d, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, 1.f, 0,
+  fa::BwdArgs a{B, H, N, d, N, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, 1.f, 0,
                 nullptr, nullptr, nullptr, delta, stream};
   return bwd_pre(dtype, a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
 namespace {
-fa_status check_bwd_phase(fa_dtype dtype, int B, int H, int N, int d, const void* q,
+// Checks of the dK/dV and dQ launches.  `keys_out` says which outputs the
+// launch writes: dk/dv (one row per key) or dq (one row per query); the
+// launch has nothing to do when its output has no rows, and buffers of a
+// side without rows may be NULL.
+fa_status check_bwd_phase(fa_dtype dtype, int B, int H, int Nq, int Nk, int d, const void* q,
                           const void* k, const void* v, const void* dout, const float* lse,
                           const float* delta, const int32_t* seqlens_k, float scale, int causal,
-                          const void* out0, const void* out1, bool* empty) {
-  fa_status st = check_common(dtype, B, H, N, d, scale, causal, empty);
+                          const void* out0, const void* out1, bool keys_out, bool* empty) {
+  fa_status st = check_common(dtype, B, H, Nq, d, scale, causal, empty);
   if (st != FA_SUCCESS) return st;
+  if (Nk < 0) return FA_ERROR_INVALID_VALUE;
   if (!bwd_supported(dtype, d)) return FA_ERROR_UNSUPPORTED;
+  *empty = B == 0 || H == 0 || (keys_out ? Nk == 0 : Nq == 0);
   if (*empty) return FA_SUCCESS;
-  if (!q || !k || !v || !dout || !lse || !delta || !out0 || !out1) return FA_ERROR_INVALID_VALUE;
+  if (!out0 || !out1) return FA_ERROR_INVALID_VALUE;
+  if (Nq > 0 && (!q || !dout || !lse || !delta)) return FA_ERROR_INVALID_VALUE;
+  if (Nk > 0 && (!k || !v)) return FA_ERROR_INVALID_VALUE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
       !aligned16(delta) || !aligned16(out0) || !aligned16(out1))
     return FA_ERROR_INVALID_VALUE;
   if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
-  if (bwd_grid(dtype, B, H, N, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  if (bwd_grid(dtype, B, H, Nq > Nk ? Nq : Nk, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
   return FA_SUCCESS;
 }
 }  // namespace
 
-fa_status fa_backward_dkdv(fa_dtype dtype, int B, int H, int N, int d, const void* q,
+fa_status fa_backward_dkdv(fa_dtype dtype, int B, int H, int Nq, int Nk, int d, const void* q,
                            const void* k, const void* v, const void* dout, const float* lse,
                            const float* delta, const int32_t* seqlens_k, float scale, int causal,
                            void* dk, void* dv, hipStream_t stream) {
   bool empty = false;
-  fa_status st = check_bwd_phase(dtype, B, H, N, d, q, k, v, dout, lse, delta, seqlens_k, scale,
-                                 causal, dk, dv, &empty);
+  fa_status st = check_bwd_phase(dtype, B, H, Nq, Nk, d, q, k, v, dout, lse, delta, seqlens_k,
+                                 scale, causal, dk, dv, true, &empty);
   if (st != FA_SUCCESS || empty) return st;
-  fa::BwdArgs a{B,     H,         N,     d,      q,       k,  v,  nullptr, dout,
-                lse,   seqlens_k, scale, causal, nullptr, dk, dv, const_cast<float*>(delta),
+  fa::BwdArgs a{B,   H,         Nq,    d,      Nk,      q,  k,  v, nullptr, dout,
+                lse, seqlens_k, scale, causal, nullptr, dk, dv, const_cast<float*>(delta),
                 stream};
   return bwd_dkdv(dtype, a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
-fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int N, int d, const void* q, const void* k,
-                         const void* v, const void* dout, const float* lse, const float* delta,
-                         const int32_t* seqlens_k, float scale, int causal, void* dq,
-                         hipStream_t stream) {
+fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int Nq, int Nk, int d, const void* q,
+                         const void* k, const void* v, const void* dout, const float* lse,
+                         const float* delta, const int32_t* seqlens_k, float scale, int causal,
+                         void* dq, hipStream_t stream) {
   bool empty = false;
-  fa_status st = check_bwd_phase(dtype, B, H, N, d, q, k, v, dout, lse, delta, seqlens_k, scale,
-                                 causal, dq, dq, &empty);
+  fa_status st = check_bwd_phase(dtype, B, H, Nq, Nk, d, q, k, v, dout, lse, delta, seqlens_k,
+                                 scale, causal, dq, dq, false, &empty);
   if (st != FA_SUCCESS || empty) return st;
-  fa::BwdArgs a{B,     H,         N,     d,      q,  k,       v,       nullptr, dout,
-                lse,   seqlens_k, scale, causal, dq, nullptr, nullptr, const_cast<float*>(delta),
+  fa::BwdArgs a{B,   H,         Nq,    d,      Nk, q,       k,       v, nullptr, dout,
+                lse, seqlens_k, scale, causal, dq, nullptr, nullptr, const_cast<float*>(delta),
                 stream};
   return bwd_dq(dtype, a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }

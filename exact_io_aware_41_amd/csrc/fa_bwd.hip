@@ -115,7 +115,8 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
                              const float* __restrict__ LSE, const float* __restrict__ Dlt,
                              const int32_t* __restrict__ seqlens_k, float scale,
                              float scale_log2, int causal, typename E::T* __restrict__ dK,
-                             typename E::T* __restrict__ dV, int B, int H, int N, int n_ktiles) {
+                             typename E::T* __restrict__ dV, int B, int H, int N, int Nk,
+                             int n_ktiles) {
   using elt = typename E::T;
   using elt8 = typename E::V8;
   using elt4 = typename E::V4;
@@ -142,26 +143,28 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
   const int h = bh - b * H;
   const size_t head = (size_t)b * H + h;
   const elt* Qh = Q + head * (size_t)N * D;
-  const elt* Kh = K + head * (size_t)N * D;
-  const elt* Vh = V + head * (size_t)N * D;
+  const elt* Kh = K + head * (size_t)Nk * D;
+  const elt* Vh = V + head * (size_t)Nk * D;
   const elt* dOh = dO + head * (size_t)N * D;
   const float* Lh = LSE + head * (size_t)N;
   const float* Dh = Dlt + head * (size_t)N;
-  elt* dKh = dK + head * (size_t)N * D;
-  elt* dVh = dV + head * (size_t)N * D;
+  elt* dKh = dK + head * (size_t)Nk * D;
+  elt* dVh = dV + head * (size_t)Nk * D;
 
-  const int kv_len = key_length(seqlens_k, b, N);
+  const int kv_len = key_length(seqlens_k, b, Nk);
+  const int off = Nk - N;   // query i sits at key position i + off
   const int k0 = kt * C::BK;
   const int kw0 = k0 + pr * 32;
   const int my_key = kw0 + l32;
-  const int q_begin = causal ? (k0 / BQ) * BQ : 0;
-  const int n_qt = (k0 < kv_len) ? (N - q_begin + BQ - 1) / BQ : 0;
+  // the first query tile that sees key k0: query k0 - off, causally
+  const int q_begin = causal ? (max(0, k0 - off) / BQ) * BQ : 0;
+  const int n_qt = (k0 < kv_len && q_begin < N) ? (N - q_begin + BQ - 1) / BQ : 0;
 
   // the pair's K and V rows (B operands of S = Q K^T and dP = dO V^T)
   elt8 kf[C::KS], vf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    if (my_key < N) {
+    if (my_key < Nk) {
       kf[ks] = *reinterpret_cast<const elt8*>(Kh + (size_t)my_key * D + ks * 16 + hi * 8);
       vf[ks] = *reinterpret_cast<const elt8*>(Vh + (size_t)my_key * D + ks * 16 + hi * 8);
     } else {
@@ -251,7 +254,7 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
     const int qt0 = q_begin + qi * BQ;
     const bool more = qi + 1 < n_qt;
     if (more) issue_tile(qi + 1, buf ^ 1);
-    const bool pair_active = pair_keys_valid && (!causal || qt0 + BQ - 1 >= kw0);
+    const bool pair_active = pair_keys_valid && (!causal || qt0 + BQ - 1 + off >= kw0);
 
     elt8 pa[2], dsa[2];
     if (pair_active) {
@@ -269,7 +272,8 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
       }
       // this lane's key is visible from tile row 32 half + 8 a4 + 4 hi + e iff
       // 32 half + 8 a4 + e >= first_vis
-      const int first_vis = my_key >= kv_len ? BQ : (causal ? my_key - qt0 - 4 * hi : -BQ);
+      const int first_vis =
+          my_key >= kv_len ? BQ : (causal ? my_key - off - qt0 - 4 * hi : -BQ);
       auto p_and_ds = [&](auto masked_tag) FA_INLINE {
         constexpr bool kMasked = decltype(masked_tag)::value;
 #pragma unroll
@@ -287,7 +291,7 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
           }
         }
       };
-      if ((kw0 + 31 >= kv_len) || (causal && qt0 + 32 * half < kw0 + 31))
+      if ((kw0 + 31 >= kv_len) || (causal && qt0 + 32 * half + off < kw0 + 31))
         p_and_ds(std::true_type{});
       else
         p_and_ds(std::false_type{});
@@ -334,7 +338,7 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int key = kw0 + c_row(v, lane);
-      if (key < N) {
+      if (key < Nk) {
         dKh[(size_t)key * D + db * 32 + l32] = E::cvt(dkacc[j][v] * scale);
         dVh[(size_t)key * D + db * 32 + l32] = E::cvt(dvacc[j][v]);
       }
@@ -362,7 +366,7 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
                       const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
                       const float* __restrict__ LSE, const float* __restrict__ Dlt,
                       const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
-                      int causal, typename E::T* __restrict__ dQ, int B, int H, int N,
+                      int causal, typename E::T* __restrict__ dQ, int B, int H, int N, int Nk,
                       int n_qtiles) {
   using elt = typename E::T;
   using elt8 = typename E::V8;
@@ -381,17 +385,18 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
   const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
   const size_t head = (size_t)tc.b * H + tc.h;
   const elt* Qh = Q + head * (size_t)N * D;
-  const elt* Kh = K + head * (size_t)N * D;
-  const elt* Vh = V + head * (size_t)N * D;
+  const elt* Kh = K + head * (size_t)Nk * D;
+  const elt* Vh = V + head * (size_t)Nk * D;
   const elt* dOh = dO + head * (size_t)N * D;
   elt* dQh = dQ + head * (size_t)N * D;
 
-  const int kv_len = key_length(seqlens_k, tc.b, N);
+  const int kv_len = key_length(seqlens_k, tc.b, Nk);
+  const int off = Nk - N;   // query i sits at key position i + off
   const int q0 = tc.qt * C::BR;
   const int qw0 = q0 + wave * 32;
   const int qrow = qw0 + l32;
   int kv_end = kv_len;
-  if (causal) kv_end = min(kv_end, min(q0 + C::BR, N));
+  if (causal) kv_end = min(kv_end, max(0, min(q0 + C::BR + off, Nk)));
   const int n_kt = (kv_end + BC - 1) / BC;
 
   elt8 qf[C::KS], of[C::KS];
@@ -427,7 +432,7 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
   constexpr int kBlksPerTensor = BC / kRowsPerBlk;
   constexpr int kBlksPerWave = 2 * kBlksPerTensor / NW;
   static_assert(2 * kBlksPerTensor % NW == 0 && kBlksPerWave >= 1, "whole 1 KiB blocks per wave");
-  const int head_bytes = N * D * 2;
+  const int head_bytes = Nk * D * 2;
   const u32x4 k_rsrc = buffer_rsrc_words(Kh, (uint32_t)head_bytes);
   const u32x4 v_rsrc = buffer_rsrc_words(Vh, (uint32_t)head_bytes);
   // per-lane byte offsets inside a tile, computed once; the tile's position
@@ -475,7 +480,7 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
     const int slot = kt & 1;
     if (kt + 1 < n_kt) issue_tile(kt + 1, slot ^ 1);
     const int key0 = kt * BC;
-    const bool wave_active = (qw0 < N) && (!causal || key0 <= qw0 + 31);
+    const bool wave_active = (qw0 < N) && (!causal || key0 <= qw0 + 31 + off);
     if (wave_active) {
       // ---- S^T = K Q^T, dP^T = V dO^T (C: one query per lane, rows = keys)
       f32x16 sacc[C::NCB], pacc[C::NCB];
@@ -498,8 +503,8 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
       // only tiles crossing the key length or the wave's diagonal are masked:
       // key key0 + 32c + 4hi + p, p = 8(v/4) + v%4, is visible iff it is at
       // most min(L - 1, this lane's query); S = -inf gives P = 0
-      if ((key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0)) {
-        const int lim = (causal ? min(kv_len - 1, qrow) : kv_len - 1) - key0 - 4 * hi;
+      if ((key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0 + off)) {
+        const int lim = (causal ? min(kv_len - 1, qrow + off) : kv_len - 1) - key0 - 4 * hi;
 #pragma unroll
         for (int c = 0; c < C::NCB; ++c) {
           const uint32_t vis = prefix_bits(lim - 32 * c);
@@ -550,6 +555,7 @@ template <class E, int D>
 hipError_t launch_preprocess_d(const BwdArgs& a) {
   using T = typename E::T;
   const long long rows = (long long)a.B * a.H * a.N;
+  if (rows == 0) return hipSuccess;
   const long long threads = rows * (D / 8);
   hipLaunchKernelGGL((fa_bwd_rowdot_kernel<E, D>), dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, a.stream, static_cast<const T*>(a.o),
@@ -561,13 +567,14 @@ template <class E, int D>
 hipError_t launch_dkdv_d(const BwdArgs& a) {
   using CK = DkdvPairCfg<D, 64>;
   using T = typename E::T;
-  const int n_ktiles = (a.N + CK::BK - 1) / CK::BK;
+  const int n_ktiles = (a.Nk + CK::BK - 1) / CK::BK;
+  if (n_ktiles == 0) return hipSuccess;   // no keys: dK and dV have no rows
   hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<E, D, 64>),
                      dim3((unsigned)((long long)n_ktiles * a.B * a.H)), dim3(CK::NT), 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
                      a.seqlens_k, a.scale, a.scale * kLog2e, a.causal, static_cast<T*>(a.dk),
-                     static_cast<T*>(a.dv), a.B, a.H, a.N, n_ktiles);
+                     static_cast<T*>(a.dv), a.B, a.H, a.N, a.Nk, n_ktiles);
   return hipGetLastError();
 }
 
@@ -576,12 +583,13 @@ hipError_t launch_dq_d(const BwdArgs& a) {
   using CQ = DqCfg<D, kDqNW, kDqBC>;
   using T = typename E::T;
   const int n_qtiles = (a.N + CQ::BR - 1) / CQ::BR;
+  if (n_qtiles == 0) return hipSuccess;   // no queries: dQ has no rows
   hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, kDqNW, kDqBC>),
                      dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(CQ::NT), 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
                      a.seqlens_k, a.scale, a.scale * kLog2e, a.causal, static_cast<T*>(a.dq),
-                     a.B, a.H, a.N, n_qtiles);
+                     a.B, a.H, a.N, a.Nk, n_qtiles);
   return hipGetLastError();
 }
 

@@ -96,7 +96,7 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
                             const float* __restrict__ LSE, const float* __restrict__ Dlt,
                             const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
                             int causal, float* __restrict__ dK, float* __restrict__ dV, int B,
-                            int H, int N, int n_kblocks) {
+                            int H, int N, int Nk, int n_kblocks) {
   using C = F32BwdCfg<D>;
   constexpr int NT = kF32BwdNW * 64;
   constexpr int BK = kF32BwdRows;   // keys per work-group
@@ -120,12 +120,13 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
   const int b = bh / H;
   const size_t head = (size_t)bh;
   const float* Qh = Q + head * (size_t)N * D;
-  const float* Kh = K + head * (size_t)N * D;
-  const float* Vh = V + head * (size_t)N * D;
+  const float* Kh = K + head * (size_t)Nk * D;
+  const float* Vh = V + head * (size_t)Nk * D;
   const float* dOh = dO + head * (size_t)N * D;
   const float* Lh = LSE + head * (size_t)N;
   const float* Dh = Dlt + head * (size_t)N;
-  const int kv_len = key_length(seqlens_k, b, N);
+  const int kv_len = key_length(seqlens_k, b, Nk);
+  const int off = Nk - N;   // query i sits at key position i + off
   const int k0 = kb * BK;
   const int kw0 = k0 + wave * 32;           // this wave's first key
   const int my_key = kw0 + l32;
@@ -142,8 +143,8 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
 
   // query tiles that see any key of the block: under the causal mask the
   // first is the one holding row k0; keys past the length are never visible
-  const int q_begin = causal ? (k0 / QT) * QT : 0;
-  const bool block_live = k0 < kv_len;
+  const int q_begin = causal ? (max(0, k0 - off) / QT) * QT : 0;
+  const bool block_live = k0 < kv_len && q_begin < N;
   const int n_qt = block_live ? (N - q_begin + QT - 1) / QT : 0;
   const bool wave_keys_live = kw0 < kv_len;
   const float* Kw = Ks + wave * 32 * C::PITCH;
@@ -161,7 +162,7 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
     }
     __syncthreads();
     // causal: the tile's last row precedes this wave's first key
-    const bool active = wave_keys_live && (!causal || qt0 + QT - 1 >= kw0);
+    const bool active = wave_keys_live && (!causal || qt0 + QT - 1 + off >= kw0);
     if (!active) continue;
 
     // S[q][key] = Q K^T and dP[q][key] = dO V^T: lane = key, v = query row
@@ -174,7 +175,8 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
       sacc = mfma_f32(Qs[l32 * C::PITCH + col], kb_op, sacc);
       pacc = mfma_f32(dOs[l32 * C::PITCH + col], vb_op, pacc);
     }
-    const bool need_mask = (kw0 + 31 >= kv_len) || (causal && qt0 < kw0 + 31) || qt0 + QT > N;
+    const bool need_mask =
+        (kw0 + 31 >= kv_len) || (causal && qt0 + off < kw0 + 31) || qt0 + QT > N;
     float p[16], ds[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -182,7 +184,7 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
       float x = fast_exp2(__builtin_fmaf(sacc[v], scale_log2, -Ls[r] * kLog2e));
       if (need_mask) {
         const int q = qt0 + r;
-        const bool vis = my_key < kv_len && (!causal || my_key <= q) && q < N;
+        const bool vis = my_key < kv_len && (!causal || my_key <= q + off) && q < N;
         x = vis ? x : 0.f;
       }
       p[v] = x;
@@ -203,14 +205,14 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
 
   // dV[key][feature], dK = scale * acc: accumulator lane l holds feature
   // 32 db + l % 32 of keys kw0 + c_row(v, l)
-  float* dKh = dK + head * (size_t)N * D;
-  float* dVh = dV + head * (size_t)N * D;
+  float* dKh = dK + head * (size_t)Nk * D;
+  float* dVh = dV + head * (size_t)Nk * D;
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int key = kw0 + c_row(v, lane);
-      if (key < N) {
+      if (key < Nk) {
         dVh[(size_t)key * D + db * 32 + l32] = dvacc[db][v];
         dKh[(size_t)key * D + db * 32 + l32] = dkacc[db][v] * scale;
       }
@@ -223,7 +225,7 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
                           const float* __restrict__ V, const float* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Dlt,
                           const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
-                          int causal, float* __restrict__ dQ, int B, int H, int N,
+                          int causal, float* __restrict__ dQ, int B, int H, int N, int Nk,
                           int n_qtiles) {
   using C = F32BwdCfg<D>;
   constexpr int NT = kF32BwdNW * 64;
@@ -240,10 +242,11 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
   const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
   const size_t head = (size_t)tc.b * H + tc.h;
   const float* Qh = Q + head * (size_t)N * D;
-  const float* Kh = K + head * (size_t)N * D;
-  const float* Vh = V + head * (size_t)N * D;
+  const float* Kh = K + head * (size_t)Nk * D;
+  const float* Vh = V + head * (size_t)Nk * D;
   const float* dOh = dO + head * (size_t)N * D;
-  const int kv_len = key_length(seqlens_k, tc.b, N);
+  const int kv_len = key_length(seqlens_k, tc.b, Nk);
+  const int off = Nk - N;   // query i sits at key position i + off
   const int q0 = tc.qt * kF32BwdRows;
   const int qw0 = q0 + wave * 32;
   const int qrow = qw0 + l32;
@@ -259,7 +262,7 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
   const float drow = qrow < N ? Dlt[head * (size_t)N + qrow] : 0.f;
 
   int kv_end = kv_len;
-  if (causal) kv_end = min(kv_end, min(q0 + kF32BwdRows, N));
+  if (causal) kv_end = min(kv_end, max(0, min(q0 + kF32BwdRows + off, Nk)));
   const int n_kt = (kv_end + BC - 1) / BC;
 
   f32x16 dqacc[C::NDB];
@@ -272,7 +275,7 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
     load_rows<D>(Ks, Kh, key0, BC, kv_len, tid, NT);
     load_rows<D>(Vs, Vh, key0, BC, kv_len, tid, NT);
     __syncthreads();
-    const bool active = qw0 < N && (!causal || key0 <= qw0 + 31);
+    const bool active = qw0 < N && (!causal || key0 <= qw0 + 31 + off);
     if (!active) continue;
 
     // S^T = K Q^T, dP^T = V dO^T: lane = query, v = key
@@ -283,14 +286,14 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
       sacc = mfma_f32(Ks[l32 * C::PITCH + col], qf[ks], sacc);
       pacc = mfma_f32(Vs[l32 * C::PITCH + col], of[ks], pacc);
     }
-    const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0);
+    const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0 + off);
     float ds[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int key = key0 + c_row(v, lane);
       float x = fast_exp2(__builtin_fmaf(sacc[v], scale_log2, -lse2));
       if (need_mask) {
-        const bool vis = key < kv_len && (!causal || key <= qrow);
+        const bool vis = key < kv_len && (!causal || key <= qrow + off);
         x = vis ? x : 0.f;
       }
       ds[v] = x * (pacc[v] - drow);
@@ -325,6 +328,7 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
 template <int D>
 hipError_t launch_preprocess_f32_d(const BwdArgs& a) {
   const long long rows = (long long)a.B * a.H * a.N;
+  if (rows == 0) return hipSuccess;
   const long long threads = rows * (D / 4);
   hipLaunchKernelGGL((fa_bwd_rowdot_f32_kernel<D>), dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, a.stream, static_cast<const float*>(a.o),
@@ -334,13 +338,14 @@ hipError_t launch_preprocess_f32_d(const BwdArgs& a) {
 
 template <int D>
 hipError_t launch_dkdv_f32_d(const BwdArgs& a) {
-  const int n_kblocks = (a.N + kF32BwdRows - 1) / kF32BwdRows;
+  const int n_kblocks = (a.Nk + kF32BwdRows - 1) / kF32BwdRows;
+  if (n_kblocks == 0) return hipSuccess;
   hipLaunchKernelGGL((fa_bwd_dkdv_f32_kernel<D>),
                      dim3((unsigned)((long long)n_kblocks * a.B * a.H)), dim3(kF32BwdNW * 64), 0,
                      a.stream, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), static_cast<const float*>(a.dout), a.lse,
                      a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
-                     static_cast<float*>(a.dk), static_cast<float*>(a.dv), a.B, a.H, a.N,
+                     static_cast<float*>(a.dk), static_cast<float*>(a.dv), a.B, a.H, a.N, a.Nk,
                      n_kblocks);
   return hipGetLastError();
 }
@@ -348,12 +353,13 @@ hipError_t launch_dkdv_f32_d(const BwdArgs& a) {
 template <int D>
 hipError_t launch_dq_f32_d(const BwdArgs& a) {
   const int n_qtiles = (a.N + kF32BwdRows - 1) / kF32BwdRows;
+  if (n_qtiles == 0) return hipSuccess;
   hipLaunchKernelGGL((fa_bwd_dq_f32_kernel<D>),
                      dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(kF32BwdNW * 64), 0,
                      a.stream, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), static_cast<const float*>(a.dout), a.lse,
                      a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
-                     static_cast<float*>(a.dq), a.B, a.H, a.N, n_qtiles);
+                     static_cast<float*>(a.dq), a.B, a.H, a.N, a.Nk, n_qtiles);
   return hipGetLastError();
 }
 

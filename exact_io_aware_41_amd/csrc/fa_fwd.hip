@@ -97,7 +97,8 @@ __attribute__((amdgpu_waves_per_eu(QB == 1 && D <= 128 ? 2 : 1, QB == 1 && D <= 
 void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
                         const typename E::T* __restrict__ V, const int32_t* __restrict__ seqlens_k,
                         float scale_log2, int causal, typename E::T* __restrict__ O,
-                        float* __restrict__ LSE, int B, int H, int N, int n_qtiles) {
+                        float* __restrict__ LSE, int B, int H, int N, int Nk,
+                        int n_qtiles) {
   using elt = typename E::T;
   using elt8 = typename E::V8;
   using elt4 = typename E::V4;
@@ -125,24 +126,27 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
   const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
   const size_t head = (size_t)tc.b * H + tc.h;
   const elt* Qh = Q + head * (size_t)N * D;
-  const elt* Kh = K + head * (size_t)N * D;
-  const elt* Vh = V + head * (size_t)N * D;
+  const elt* Kh = K + head * (size_t)Nk * D;
+  const elt* Vh = V + head * (size_t)Nk * D;
   elt* Oh = O + head * (size_t)N * D;
   float* Lh = LSE + head * (size_t)N;
 
-  const int kv_len = key_length(seqlens_k, tc.b, N);
+  const int kv_len = key_length(seqlens_k, tc.b, Nk);
+  // N queries, Nk keys: query i sits at key position i + off (the queries are
+  // the last N positions), so causally it sees keys j <= i + off
+  const int off = Nk - N;
   const int q0 = tc.qt * C::BR;
   const int qw0 = q0 + wave * QB * 32;
   const int qw_last = qw0 + QB * 32 - 1;
   // key tiles the work-group loads: up to its last visible key
   int kv_end = kv_len;
-  if (causal) kv_end = min(kv_end, min(q0 + C::BR, N));
+  if (causal) kv_end = min(kv_end, max(0, min(q0 + C::BR + off, Nk)));
   const int n_kt = (kv_end + BC - 1) / BC;
   // key tiles this wave computes (a prefix): under the causal mask a tile whose
   // first key lies past the wave's last query is skipped
   int n_act = n_kt;
   if (qw0 >= N) n_act = 0;
-  else if (causal) n_act = min(n_kt, qw_last / BC + 1);
+  else if (causal) n_act = qw_last + off < 0 ? 0 : min(n_kt, (qw_last + off) / BC + 1);
 
   // ---- Q fragments (B operand of S^T = K Q^T): query l32, features 8*hi + [0..7]
   elt8 qf[QB][C::KS];
@@ -186,7 +190,7 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
   constexpr int kBlksPerTensor = BC / kRowsPerBlk;
   constexpr int kBlksPerWave = 2 * kBlksPerTensor / NW;
   static_assert(2 * kBlksPerTensor % NW == 0 && kBlksPerWave >= 1, "whole 1 KiB blocks per wave");
-  const int head_bytes = N * D * 2;
+  const int head_bytes = Nk * D * 2;
   const u32x4 k_rsrc = buffer_rsrc_words(Kh, (uint32_t)head_bytes);
   const u32x4 v_rsrc = buffer_rsrc_words(Vh, (uint32_t)head_bytes);
   // per-lane byte offsets inside a tile, computed once: the loads' address
@@ -320,7 +324,7 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
   // softmax with lazy rescaling, P^T as bf16; rescales O when a maximum jumped
   auto stage_softmax = [&](int kt) FA_INLINE {
     const int key0 = kt * BC;
-    const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0);
+    const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0 + off);
     if (need_mask) {
 #pragma unroll
       for (int c = 0; c < C::NCB; ++c)
@@ -329,7 +333,7 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
           // key key0 + 32c + 4hi + p, p = 8(v/4) + v%4, is visible iff it is
           // at most min(L - 1, query): bit p of a per-lane prefix mask
           const int query = qw0 + qb * 32 + l32;
-          const int lim = (causal ? min(kv_len - 1, query) : kv_len - 1) - key0 - 4 * hi;
+          const int lim = (causal ? min(kv_len - 1, query + off) : kv_len - 1) - key0 - 4 * hi;
           const uint32_t vis = prefix_bits(lim - 32 * c);
 #pragma unroll
           for (int v = 0; v < 16; ++v)
@@ -478,7 +482,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, const int32_t* __restrict__ seqlens_k,
                        float scale_log2, int causal, float* __restrict__ O,
-                       float* __restrict__ LSE, int B, int H, int N, int n_qtiles) {
+                       float* __restrict__ LSE, int B, int H, int N, int Nk,
+                       int n_qtiles) {
   using C = FwdF32Cfg<D, NW, BC>;
   __shared__ __attribute__((aligned(16))) float Ks[2][BC * C::KPITCH];
   __shared__ __attribute__((aligned(16))) float Vs[2][BC * C::VPITCH];
@@ -492,16 +497,17 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
   const size_t head = (size_t)tc.b * H + tc.h;
   const float* Qh = Q + head * (size_t)N * D;
-  const float* Kh = K + head * (size_t)N * D;
-  const float* Vh = V + head * (size_t)N * D;
+  const float* Kh = K + head * (size_t)Nk * D;
+  const float* Vh = V + head * (size_t)Nk * D;
   float* Oh = O + head * (size_t)N * D;
   float* Lh = LSE + head * (size_t)N;
 
-  const int kv_len = key_length(seqlens_k, tc.b, N);
+  const int kv_len = key_length(seqlens_k, tc.b, Nk);
+  const int off = Nk - N;   // query i sits at key position i + off
   const int q0 = tc.qt * C::BR;
   const int qw0 = q0 + wave * 32;
   int kv_end = kv_len;
-  if (causal) kv_end = min(kv_end, min(q0 + C::BR, N));
+  if (causal) kv_end = min(kv_end, max(0, min(q0 + C::BR + off, Nk)));
   const int n_kt = (kv_end + BC - 1) / BC;
 
   const int qrow = qw0 + l32;
@@ -580,7 +586,7 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int buf = kt & 1;
     if (kStage && kt + 1 < n_kt) load_tile(kt + 1);
     const int key0 = kt * BC;
-    const bool wave_active = (qw0 < N) && (!causal || key0 <= qw0 + 31);
+    const bool wave_active = (qw0 < N) && (!causal || key0 <= qw0 + 31 + off);
     if (wave_active) {
       f32x16 sacc[C::NCB];
 #pragma unroll
@@ -591,14 +597,14 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         for (int c = 0; c < C::NCB; ++c)
           sacc[c] = mfma_f32(Ks[buf][(c * 32 + l32) * C::KPITCH + 2 * ks + hi], qf[ks], sacc[c]);
 
-      const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0);
+      const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0 + off);
       if (need_mask) {
 #pragma unroll
         for (int c = 0; c < C::NCB; ++c)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int key = key0 + c * 32 + c_row(v, lane);
-            const bool vis = key < kv_len && (!causal || key <= qrow);
+            const bool vis = key < kv_len && (!causal || key <= qrow + off);
             if (!vis) sacc[c][v] = kNegInf;
           }
       }
@@ -686,7 +692,7 @@ hipError_t launch_half_d(const FwdArgs& a) {
   hipLaunchKernelGGL((fa_fwd_half_kernel<E, D, kBf16QB, NW, BC>), grid, dim3(C::NT), 0,
                      a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), a.seqlens_k, a.scale * kLog2e, a.causal,
-                     static_cast<T*>(a.o), a.lse, a.B, a.H, a.N, n_qtiles);
+                     static_cast<T*>(a.o), a.lse, a.B, a.H, a.N, a.Nk, n_qtiles);
   return hipGetLastError();
 }
 
@@ -708,7 +714,7 @@ hipError_t launch_f32_d(const FwdArgs& a) {
   hipLaunchKernelGGL((fa_fwd_f32_kernel<D, kF32NW, kF32BC>), grid, dim3(C::NT), 0, a.stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), a.seqlens_k, a.scale * kLog2e, a.causal,
-                     static_cast<float*>(a.o), a.lse, a.B, a.H, a.N, n_qtiles);
+                     static_cast<float*>(a.o), a.lse, a.B, a.H, a.N, a.Nk, n_qtiles);
   return hipGetLastError();
 }
 

@@ -13,7 +13,8 @@ namespace fa {
 enum class Elt { kF32, kBf16, kF16 };
 
 struct FwdArgs {
-  int B, H, N, d;
+  int B, H, N, d;   // N: query rows per head
+  int Nk;           // key/value rows per head
   const void* q;
   const void* k;
   const void* v;
@@ -26,7 +27,8 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
-  int B, H, N, d;
+  int B, H, N, d;   // N: query rows per head
+  int Nk;           // key/value rows per head
   const void* q;
   const void* k;
   const void* v;

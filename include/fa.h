@@ -107,26 +107,33 @@ const char* fa_status_string(fa_status s);
  * masked for a query tile are skipped, never loaded.
  *
  *   dtype      element type of q, k, v and o
- *   B, H, N, d batch, heads, sequence length, head dimension (d in the
- *              compiled set)
- *   q, k, v    [B][H][N][d] inputs (read only)
- *   seqlens_k  [B] int32 key lengths on the device, or NULL for all N;
- *              each value is clamped to [0, N] inside the kernel
+ *   B, H       batch, heads
+ *   Nq, Nk     query rows and key/value rows per head (usually equal)
+ *   d          head dimension (in the compiled set)
+ *   q          [B][H][Nq][d] queries; k, v [B][H][Nk][d] (read only)
+ *   seqlens_k  [B] int32 key lengths on the device, or NULL for all Nk;
+ *              each value is clamped to [0, Nk] inside the kernel
  *   scale      multiplier of q . k; finite and > 0 (1/sqrt(d) is usual)
- *   causal     0 or 1; 1 masks keys j > i (absolute positions)
- *   o          [B][H][N][d] output, same dtype as q, rounded to nearest even
- *   lse        [B][H][N] fp32 output (natural log); the backward needs it
+ *   causal     0 or 1; 1 masks keys j > i + Nk - Nq (absolute positions;
+ *              the pages state the mask for Nq = Nk, j > i, and the queries
+ *              are read as the last Nq positions of the sequence, so with
+ *              Nq = 1 the query sees every key, and with Nq > Nk the first
+ *              Nq - Nk rows see none)
+ *   o          [B][H][Nq][d] output, same dtype as q, rounded to nearest even
+ *   lse        [B][H][Nq] fp32 output (natural log); the backward needs it
  *   stream     HIP stream the work is enqueued on (0 = default stream)
+ * Rows that see no key get o = 0 and lse = -inf.  Nq = 0 writes nothing;
+ * Nk = 0 writes those empty rows.
  */
-fa_status fa_forward(fa_dtype dtype, int B, int H, int N, int d,
+fa_status fa_forward(fa_dtype dtype, int B, int H, int Nq, int Nk, int d,
                      const void* q, const void* k, const void* v,
                      const int32_t* seqlens_k, float scale, int causal,
                      void* o, float* lse, hipStream_t stream);
 
 /*
  * Bytes of device workspace fa_backward needs for this problem (0 for an
- * empty problem).  The workspace holds the fp32 row dot products
- * D_i = sum_t dO_it O_it, one per query row.
+ * empty problem); N is the number of query rows.  The workspace holds the
+ * fp32 row dot products D_i = sum_t dO_it O_it, one per query row.
  */
 size_t fa_backward_workspace_size(fa_dtype dtype, int B, int H, int N, int d);
 
@@ -138,17 +145,19 @@ size_t fa_backward_workspace_size(fa_dtype dtype, int B, int H, int N, int d);
  * dV = P^T dO, dP = dO V^T, D_i = sum_t dO_it O_it, dS = P * (dP - D),
  * dQ = scale dS K, dK = scale dS^T Q, all accumulated in fp32.
  *
- *   q, k, v, o, dout   [B][H][N][d] (o and lse as written by fa_forward)
- *   lse                [B][H][N] fp32
- *   seqlens_k, scale, causal  exactly as passed to fa_forward
- *   dq, dk, dv         [B][H][N][d] outputs, same dtype as q
+ *   q, o, dout         [B][H][Nq][d]; k, v [B][H][Nk][d] (o and lse as
+ *                      written by fa_forward)
+ *   lse                [B][H][Nq] fp32
+ *   Nq, Nk, seqlens_k, scale, causal  exactly as passed to fa_forward
+ *   dq                 [B][H][Nq][d] output; dk, dv [B][H][Nk][d] outputs;
+ *                      same dtype as q (keys no query sees get zeros)
  *   workspace          device buffer of at least
  *                      fa_backward_workspace_size(...) bytes, 16-byte
  *                      aligned; its contents on entry do not matter
  *   workspace_bytes    size of that buffer
  * The result is deterministic: it does not depend on scheduling order.
  */
-fa_status fa_backward(fa_dtype dtype, int B, int H, int N, int d,
+fa_status fa_backward(fa_dtype dtype, int B, int H, int Nq, int Nk, int d,
                       const void* q, const void* k, const void* v,
                       const void* o, const void* dout, const float* lse,
                       const int32_t* seqlens_k, float scale, int causal,
@@ -163,7 +172,8 @@ fa_status fa_backward(fa_dtype dtype, int B, int H, int N, int d,
  * concurrently on two streams once preprocess has finished.
  *
  * fa_backward_preprocess: delta[b][h][i] = sum_t dout_it o_it in fp32 (the
- *   row term D of dS = P * (dP - D)); delta is [B][H][N] fp32, 16-byte aligned.
+ *   row term D of dS = P * (dP - D)); N is Nq; delta is [B][H][Nq] fp32,
+ *   16-byte aligned.
  * fa_backward_dkdv: dk and dv.  Each work-group keeps a block of keys and
  *   their gradient accumulators on chip and streams query tiles past them,
  *   recomputing S and P per tile.
@@ -173,12 +183,12 @@ fa_status fa_backward(fa_dtype dtype, int B, int H, int N, int d,
 fa_status fa_backward_preprocess(fa_dtype dtype, int B, int H, int N, int d,
                                  const void* o, const void* dout, float* delta,
                                  hipStream_t stream);
-fa_status fa_backward_dkdv(fa_dtype dtype, int B, int H, int N, int d,
+fa_status fa_backward_dkdv(fa_dtype dtype, int B, int H, int Nq, int Nk, int d,
                            const void* q, const void* k, const void* v,
                            const void* dout, const float* lse, const float* delta,
                            const int32_t* seqlens_k, float scale, int causal,
                            void* dk, void* dv, hipStream_t stream);
-fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int N, int d,
+fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int Nq, int Nk, int d,
                          const void* q, const void* k, const void* v,
                          const void* dout, const float* lse, const float* delta,
                          const int32_t* seqlens_k, float scale, int causal,

@@ -41,7 +41,7 @@ def test_header_declarations_are_exported():
 
 
 def test_version_and_status_strings():
-    assert fa.fa_abi_version() == 1
+    assert fa.fa_abi_version() == 2
     assert fa.fa_status_string(fa.FA_SUCCESS) == "FA_SUCCESS"
     assert fa.fa_status_string(fa.FA_ERROR_INVALID_VALUE) == "FA_ERROR_INVALID_VALUE"
     assert fa.fa_status_string(fa.FA_ERROR_UNSUPPORTED) == "FA_ERROR_UNSUPPORTED"
@@ -50,16 +50,19 @@ def test_version_and_status_strings():
 
 
 def fwd(dtype=BF16, B=1, H=1, N=16, d=128, q=A, k=A, v=A, lens=None, scale=0.1, causal=0, o=A,
-        lse=A):
-    return fa.fa_forward(dtype, B, H, N, d, q, k, v, lens, scale, causal, o, lse, None)
+        lse=A, Nk=None):
+    Nk = N if Nk is None else Nk
+    return fa.fa_forward(dtype, B, H, N, Nk, d, q, k, v, lens, scale, causal, o, lse, None)
 
 
 def bwd(dtype=BF16, B=1, H=1, N=16, d=128, scale=0.1, causal=0, ws=A, ws_bytes=1 << 20,
-        **ptrs):
+        Nk=None, **ptrs):
+    Nk = N if Nk is None else Nk
     p = dict(q=A, k=A, v=A, o=A, do=A, lse=A, lens=None, dq=A, dk=A, dv=A)
     p.update(ptrs)
-    return fa.fa_backward(dtype, B, H, N, d, p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"],
-                          p["lens"], scale, causal, p["dq"], p["dk"], p["dv"], ws, ws_bytes, None)
+    return fa.fa_backward(dtype, B, H, N, Nk, d, p["q"], p["k"], p["v"], p["o"], p["do"],
+                          p["lse"], p["lens"], scale, causal, p["dq"], p["dk"], p["dv"], ws,
+                          ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw", [
@@ -87,6 +90,17 @@ def test_forward_empty_problems_succeed_without_pointers():
     # f16 is a known format; an unknown code is an invalid value
     assert fwd(dtype=F16, N=0, q=None, k=None, v=None, o=None, lse=None) == fa.FA_SUCCESS
     assert fwd(dtype=3) == fa.FA_ERROR_INVALID_VALUE
+
+
+def test_rectangular_problems_validate():
+    assert fwd(Nk=-1) == fa.FA_ERROR_INVALID_VALUE
+    # no query rows: nothing to write, pointers may be absent
+    assert fwd(N=0, Nk=32, q=None, k=None, v=None, o=None, lse=None) == fa.FA_SUCCESS
+    # queries without keys still write empty rows, so they need their buffers
+    assert fwd(N=8, Nk=0, q=None) == fa.FA_ERROR_INVALID_VALUE
+    assert bwd(Nk=-3) == fa.FA_ERROR_INVALID_VALUE
+    assert bwd(N=0, Nk=0, q=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
+    assert bwd(N=0, Nk=16, dk=None) == fa.FA_ERROR_INVALID_VALUE
 
 
 def test_forward_grid_too_large_is_rejected():
@@ -141,13 +155,15 @@ def test_backward_phase_entry_points_validate():
     assert pre(dtype=F32, d=96) == fa.FA_ERROR_UNSUPPORTED
     assert pre(N=0, o=None, do=None, delta=None) == fa.FA_SUCCESS
 
-    def dkdv(q=A, dk=A, dv=A, delta=A, scale=0.1, causal=0, d=128, N=16):
-        return fa.fa_backward_dkdv(BF16, 1, 1, N, d, q, A, A, A, A, delta, None, scale, causal,
-                                   dk, dv, None)
+    def dkdv(q=A, dk=A, dv=A, delta=A, scale=0.1, causal=0, d=128, N=16, Nk=None):
+        Nk = N if Nk is None else Nk
+        return fa.fa_backward_dkdv(BF16, 1, 1, N, Nk, d, q, A, A, A, A, delta, None, scale,
+                                   causal, dk, dv, None)
 
-    def dq(q=A, out=A, delta=A, scale=0.1, causal=0, d=128, N=16):
-        return fa.fa_backward_dq(BF16, 1, 1, N, d, q, A, A, A, A, delta, None, scale, causal,
-                                 out, None)
+    def dq(q=A, out=A, delta=A, scale=0.1, causal=0, d=128, N=16, Nk=None):
+        Nk = N if Nk is None else Nk
+        return fa.fa_backward_dq(BF16, 1, 1, N, Nk, d, q, A, A, A, A, delta, None, scale,
+                                 causal, out, None)
 
     for f in (dkdv, dq):
         assert f(q=None) == fa.FA_ERROR_INVALID_VALUE
@@ -156,6 +172,13 @@ def test_backward_phase_entry_points_validate():
         assert f(causal=5) == fa.FA_ERROR_INVALID_VALUE
         assert f(d=80) == fa.FA_ERROR_UNSUPPORTED
         assert f(N=0, q=None, delta=None) == fa.FA_SUCCESS
+        assert f(Nk=-1) == fa.FA_ERROR_INVALID_VALUE
+    # keys without queries still have dK/dV rows; queries without keys, dQ rows
+    assert dkdv(N=0, Nk=16, dk=None) == fa.FA_ERROR_INVALID_VALUE
+    assert dq(N=16, Nk=0, out=None) == fa.FA_ERROR_INVALID_VALUE
+    # a launch whose output has no rows does nothing, whatever the pointers
+    assert dkdv(N=16, Nk=0, q=None, dk=None, dv=None) == fa.FA_SUCCESS
+    assert dq(N=0, Nk=16, q=None, out=None) == fa.FA_SUCCESS
     assert dkdv(dk=None) == fa.FA_ERROR_INVALID_VALUE
     assert dkdv(dv=MIS) == fa.FA_ERROR_INVALID_VALUE
     assert dq(out=None) == fa.FA_ERROR_INVALID_VALUE
