@@ -28,7 +28,7 @@ bool fwd_supported(fa_dtype dtype, int d) {
 }
 
 bool bwd_supported(fa_dtype dtype, int d) {
-  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128);
+  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128 || d == 256);
 }
 
 long long bwd_grid(fa_dtype dtype, int B, int H, int N, int d) {

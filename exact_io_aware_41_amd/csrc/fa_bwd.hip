@@ -92,10 +92,11 @@ void fa_bwd_rowdot_kernel(const typename E::T* __restrict__ O, const typename E:
 // other's MFMAs, measured slower: the accumulators held across the extra
 // barrier did not fit without spills.)
 // ---------------------------------------------------------------------------
-template <int D, int BQ>
+template <int D, int BQ, int NW_>
 struct DkdvPairCfg {
-  static constexpr int NW = 8;
-  static constexpr int BK = 128;           // keys per work-group (4 pairs x 32)
+  static constexpr int NW = NW_;           // 8 up to d = 128 (two waves per SIMD), 4 at d = 256
+  static constexpr int NP = NW / 2;        // pairs; waves w and w + NP share 32 keys
+  static constexpr int BK = NP * 32;       // keys per work-group
   static constexpr int NT = NW * 64;
   static constexpr int KS = D / 16;
   static constexpr int NG = BQ / 16;       // 16-query groups per tile
@@ -105,9 +106,9 @@ struct DkdvPairCfg {
   static_assert(NDB % 2 == 0, "head dimension splits in two halves of 32-feature blocks");
 };
 
-template <class E, int D, int BQ>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
-__attribute__((amdgpu_waves_per_eu(2, 2)))
+template <class E, int D, int BQ, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+__attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1)))
 void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
                              const typename E::T* __restrict__ K,
                              const typename E::T* __restrict__ V,
@@ -120,7 +121,7 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
   using elt = typename E::T;
   using elt8 = typename E::V8;
   using elt4 = typename E::V4;
-  using C = DkdvPairCfg<D, BQ>;
+  using C = DkdvPairCfg<D, BQ, NW>;
   __shared__ __attribute__((aligned(16))) elt Qs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) elt dOs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
@@ -133,8 +134,8 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int pr = wave & 3;      // key block of the pair
-  const int half = wave >> 2;   // query half for S/dP, feature half for dK/dV
+  const int pr = wave % C::NP;   // key block of the pair
+  const int half = wave / C::NP; // query half for S/dP, feature half for dK/dV
 
   const int bh_count = B * H;
   const int kt = blockIdx.x / bh_count;
@@ -304,7 +305,7 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
     if (more) store_stats(buf ^ 1);
     if (pair_active) {
       // ---- phase 2: dV += P^T dO, dK += dS^T Q over all 64 rows, own feature half
-      const int partner = wave ^ 4;
+      const int partner = wave ^ C::NP;
       elt8 po[2], dso[2];
       po[0] = Xs[partner][0][lane];
       po[1] = Xs[partner][1][lane];
@@ -549,7 +550,14 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
   }
 }
 
-constexpr int kDqNW = FA_DQ_NW, kDqBC = FA_DQ_BC;
+constexpr int kDqBC = FA_DQ_BC;
+// waves per work-group of the two main backward kernels: up to d = 128 two
+// waves share a SIMD; at d = 256 one wave per SIMD holds the larger operands
+template <int D>
+struct BwdWaves {
+  static constexpr int DKDV = D <= 128 ? 8 : 4;
+  static constexpr int DQ = D <= 128 ? FA_DQ_NW : 4;
+};
 
 template <class E, int D>
 hipError_t launch_preprocess_d(const BwdArgs& a) {
@@ -565,11 +573,11 @@ hipError_t launch_preprocess_d(const BwdArgs& a) {
 
 template <class E, int D>
 hipError_t launch_dkdv_d(const BwdArgs& a) {
-  using CK = DkdvPairCfg<D, 64>;
+  using CK = DkdvPairCfg<D, 64, BwdWaves<D>::DKDV>;
   using T = typename E::T;
   const int n_ktiles = (a.Nk + CK::BK - 1) / CK::BK;
   if (n_ktiles == 0) return hipSuccess;   // no keys: dK and dV have no rows
-  hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<E, D, 64>),
+  hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<E, D, 64, BwdWaves<D>::DKDV>),
                      dim3((unsigned)((long long)n_ktiles * a.B * a.H)), dim3(CK::NT), 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
@@ -580,11 +588,11 @@ hipError_t launch_dkdv_d(const BwdArgs& a) {
 
 template <class E, int D>
 hipError_t launch_dq_d(const BwdArgs& a) {
-  using CQ = DqCfg<D, kDqNW, kDqBC>;
+  using CQ = DqCfg<D, BwdWaves<D>::DQ, kDqBC>;
   using T = typename E::T;
   const int n_qtiles = (a.N + CQ::BR - 1) / CQ::BR;
   if (n_qtiles == 0) return hipSuccess;   // no queries: dQ has no rows
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, kDqNW, kDqBC>),
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, BwdWaves<D>::DQ, kDqBC>),
                      dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(CQ::NT), 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
@@ -596,9 +604,11 @@ hipError_t launch_dq_d(const BwdArgs& a) {
 }  // namespace
 
 long long bwd_half_grid(int B, int H, int N, int d) {
-  (void)d;
-  const long long kt = (N + 127) / 128;
-  const long long qt = (N + kDqNW * 32 - 1) / (kDqNW * 32);
+  const int bk = d <= 128 ? DkdvPairCfg<128, 64, BwdWaves<128>::DKDV>::BK
+                          : DkdvPairCfg<256, 64, BwdWaves<256>::DKDV>::BK;
+  const int br = 32 * (d <= 128 ? BwdWaves<128>::DQ : BwdWaves<256>::DQ);
+  const long long kt = (N + bk - 1) / bk;
+  const long long qt = (N + br - 1) / br;
   const long long rows_wg = ((long long)B * H * N * 16 + 255) / 256;
   long long m = kt * B * H;
   if (qt * B * H > m) m = qt * B * H;
@@ -607,29 +617,41 @@ long long bwd_half_grid(int B, int H, int N, int d) {
 }
 
 hipError_t launch_bwd_preprocess_half(const BwdArgs& a, Elt e) {
-  if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
+  if (a.d != 64 && a.d != 128 && a.d != 256) return hipErrorInvalidValue;
   if (e == Elt::kBf16)
-    return a.d == 64 ? launch_preprocess_d<EltBf16, 64>(a) : launch_preprocess_d<EltBf16, 128>(a);
+    return a.d == 64    ? launch_preprocess_d<EltBf16, 64>(a)
+           : a.d == 128 ? launch_preprocess_d<EltBf16, 128>(a)
+                        : launch_preprocess_d<EltBf16, 256>(a);
   if (e == Elt::kF16)
-    return a.d == 64 ? launch_preprocess_d<EltF16, 64>(a) : launch_preprocess_d<EltF16, 128>(a);
+    return a.d == 64    ? launch_preprocess_d<EltF16, 64>(a)
+           : a.d == 128 ? launch_preprocess_d<EltF16, 128>(a)
+                        : launch_preprocess_d<EltF16, 256>(a);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dkdv_half(const BwdArgs& a, Elt e) {
-  if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
+  if (a.d != 64 && a.d != 128 && a.d != 256) return hipErrorInvalidValue;
   if (e == Elt::kBf16)
-    return a.d == 64 ? launch_dkdv_d<EltBf16, 64>(a) : launch_dkdv_d<EltBf16, 128>(a);
+    return a.d == 64    ? launch_dkdv_d<EltBf16, 64>(a)
+           : a.d == 128 ? launch_dkdv_d<EltBf16, 128>(a)
+                        : launch_dkdv_d<EltBf16, 256>(a);
   if (e == Elt::kF16)
-    return a.d == 64 ? launch_dkdv_d<EltF16, 64>(a) : launch_dkdv_d<EltF16, 128>(a);
+    return a.d == 64    ? launch_dkdv_d<EltF16, 64>(a)
+           : a.d == 128 ? launch_dkdv_d<EltF16, 128>(a)
+                        : launch_dkdv_d<EltF16, 256>(a);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq_half(const BwdArgs& a, Elt e) {
-  if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
+  if (a.d != 64 && a.d != 128 && a.d != 256) return hipErrorInvalidValue;
   if (e == Elt::kBf16)
-    return a.d == 64 ? launch_dq_d<EltBf16, 64>(a) : launch_dq_d<EltBf16, 128>(a);
+    return a.d == 64    ? launch_dq_d<EltBf16, 64>(a)
+           : a.d == 128 ? launch_dq_d<EltBf16, 128>(a)
+                        : launch_dq_d<EltBf16, 256>(a);
   if (e == Elt::kF16)
-    return a.d == 64 ? launch_dq_d<EltF16, 64>(a) : launch_dq_d<EltF16, 128>(a);
+    return a.d == 64    ? launch_dq_d<EltF16, 64>(a)
+           : a.d == 128 ? launch_dq_d<EltF16, 128>(a)
+                        : launch_dq_d<EltF16, 256>(a);
   return hipErrorInvalidValue;
 }
 

@@ -36,8 +36,13 @@ namespace fa {
 
 namespace {
 
-constexpr int kF32BwdNW = 2;   // waves per work-group in both kernels
-constexpr int kF32BwdRows = kF32BwdNW * 32;
+// waves per work-group: two (64 keys or query rows); the dK/dV kernel uses
+// one at d = 256, where K, V, Q and dO tiles of 64 rows would not fit in LDS
+template <int D>
+struct F32BwdWaves {
+  static constexpr int DKDV = D <= 128 ? 2 : 1;
+  static constexpr int DQ = 2;
+};
 
 // Row pitches in floats: +2 makes the 32-row x 2-column fragment reads
 // (row l % 32, column 2 ks + l / 32) hit 64 distinct banks.
@@ -89,8 +94,8 @@ __device__ __forceinline__ void load_rows(float* tile, const float* head, int r0
   }
 }
 
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kF32BwdNW * 64, kF32BwdNW * 64)))
+template <int D, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                             const float* __restrict__ V, const float* __restrict__ dO,
                             const float* __restrict__ LSE, const float* __restrict__ Dlt,
@@ -98,8 +103,8 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
                             int causal, float* __restrict__ dK, float* __restrict__ dV, int B,
                             int H, int N, int Nk, int n_kblocks) {
   using C = F32BwdCfg<D>;
-  constexpr int NT = kF32BwdNW * 64;
-  constexpr int BK = kF32BwdRows;   // keys per work-group
+  constexpr int NT = NW * 64;
+  constexpr int BK = NW * 32;       // keys per work-group
   constexpr int QT = 32;            // query rows per tile
   __shared__ __attribute__((aligned(16))) float Ks[BK * C::PITCH];
   __shared__ __attribute__((aligned(16))) float Vs[BK * C::PITCH];
@@ -219,8 +224,8 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
     }
 }
 
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kF32BwdNW * 64, kF32BwdNW * 64)))
+template <int D, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                           const float* __restrict__ V, const float* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Dlt,
@@ -228,7 +233,8 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
                           int causal, float* __restrict__ dQ, int B, int H, int N, int Nk,
                           int n_qtiles) {
   using C = F32BwdCfg<D>;
-  constexpr int NT = kF32BwdNW * 64;
+  constexpr int NT = NW * 64;
+  constexpr int BR = NW * 32;       // query rows per work-group
   constexpr int BC = 32;            // keys per tile
   __shared__ __attribute__((aligned(16))) float Ks[BC * C::PITCH];
   __shared__ __attribute__((aligned(16))) float Vs[BC * C::PITCH];
@@ -247,7 +253,7 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
   const float* dOh = dO + head * (size_t)N * D;
   const int kv_len = key_length(seqlens_k, tc.b, Nk);
   const int off = Nk - N;   // query i sits at key position i + off
-  const int q0 = tc.qt * kF32BwdRows;
+  const int q0 = tc.qt * BR;
   const int qw0 = q0 + wave * 32;
   const int qrow = qw0 + l32;
 
@@ -262,7 +268,7 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
   const float drow = qrow < N ? Dlt[head * (size_t)N + qrow] : 0.f;
 
   int kv_end = kv_len;
-  if (causal) kv_end = min(kv_end, max(0, min(q0 + kF32BwdRows + off, Nk)));
+  if (causal) kv_end = min(kv_end, max(0, min(q0 + BR + off, Nk)));
   const int n_kt = (kv_end + BC - 1) / BC;
 
   f32x16 dqacc[C::NDB];
@@ -278,9 +284,10 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
     const bool active = qw0 < N && (!causal || key0 <= qw0 + 31 + off);
     if (!active) continue;
 
-    // S^T = K Q^T, dP^T = V dO^T: lane = query, v = key
+    // S^T = K Q^T, dP^T = V dO^T: lane = query, v = key (fully unrolled, so
+    // the Q and dO rows stay in registers)
     f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll 8
+#pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const int col = 2 * ks + hi;
       sacc = mfma_f32(Ks[l32 * C::PITCH + col], qf[ks], sacc);
@@ -338,10 +345,11 @@ hipError_t launch_preprocess_f32_d(const BwdArgs& a) {
 
 template <int D>
 hipError_t launch_dkdv_f32_d(const BwdArgs& a) {
-  const int n_kblocks = (a.Nk + kF32BwdRows - 1) / kF32BwdRows;
+  constexpr int NW = F32BwdWaves<D>::DKDV;
+  const int n_kblocks = (a.Nk + NW * 32 - 1) / (NW * 32);
   if (n_kblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((fa_bwd_dkdv_f32_kernel<D>),
-                     dim3((unsigned)((long long)n_kblocks * a.B * a.H)), dim3(kF32BwdNW * 64), 0,
+  hipLaunchKernelGGL((fa_bwd_dkdv_f32_kernel<D, NW>),
+                     dim3((unsigned)((long long)n_kblocks * a.B * a.H)), dim3(NW * 64), 0,
                      a.stream, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), static_cast<const float*>(a.dout), a.lse,
                      a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
@@ -352,10 +360,11 @@ hipError_t launch_dkdv_f32_d(const BwdArgs& a) {
 
 template <int D>
 hipError_t launch_dq_f32_d(const BwdArgs& a) {
-  const int n_qtiles = (a.N + kF32BwdRows - 1) / kF32BwdRows;
+  constexpr int NW = F32BwdWaves<D>::DQ;
+  const int n_qtiles = (a.N + NW * 32 - 1) / (NW * 32);
   if (n_qtiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((fa_bwd_dq_f32_kernel<D>),
-                     dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(kF32BwdNW * 64), 0,
+  hipLaunchKernelGGL((fa_bwd_dq_f32_kernel<D, NW>),
+                     dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(NW * 64), 0,
                      a.stream, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), static_cast<const float*>(a.dout), a.lse,
                      a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
@@ -367,7 +376,7 @@ hipError_t launch_dq_f32_d(const BwdArgs& a) {
 
 long long bwd_f32_grid(int B, int H, int N, int d) {
   (void)d;
-  const long long tiles = (N + kF32BwdRows - 1) / kF32BwdRows;
+  const long long tiles = (N + 31) / 32;   // the smallest row block of either kernel
   const long long rows_wg = ((long long)B * H * N * (d / 4) + 255) / 256;
   const long long m = tiles * B * H;
   return rows_wg > m ? rows_wg : m;
@@ -376,18 +385,21 @@ long long bwd_f32_grid(int B, int H, int N, int d) {
 hipError_t launch_bwd_preprocess_f32(const BwdArgs& a) {
   if (a.d == 64) return launch_preprocess_f32_d<64>(a);
   if (a.d == 128) return launch_preprocess_f32_d<128>(a);
+  if (a.d == 256) return launch_preprocess_f32_d<256>(a);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dkdv_f32(const BwdArgs& a) {
   if (a.d == 64) return launch_dkdv_f32_d<64>(a);
   if (a.d == 128) return launch_dkdv_f32_d<128>(a);
+  if (a.d == 256) return launch_dkdv_f32_d<256>(a);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq_f32(const BwdArgs& a) {
   if (a.d == 64) return launch_dq_f32_d<64>(a);
   if (a.d == 128) return launch_dq_f32_d<128>(a);
+  if (a.d == 256) return launch_dq_f32_d<256>(a);
   return hipErrorInvalidValue;
 }
 

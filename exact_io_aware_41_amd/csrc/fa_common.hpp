@@ -212,7 +212,7 @@ __device__ __forceinline__ int row_swizzle(int row) {
 // under the measured grouping rules).
 template <int D>
 __device__ __forceinline__ int tile_swizzle(int row) {
-  if constexpr (D == 128)
+  if constexpr (D >= 128)
     return ((row & 3) << 2) ^ ((row >> 2) & 3) ^ (((row >> 4) & 1) * 3);
   else
     return (((row >> 1) & 1) << 2) ^ ((row >> 3) & 1) ^ (((row >> 4) & 1) << 1);

@@ -120,8 +120,8 @@ def test_backward_rejects_invalid_arguments(kw):
 
 def test_backward_unsupported_and_workspace_size():
     assert bwd(dtype=F32, d=96) == fa.FA_ERROR_UNSUPPORTED
-    assert bwd(dtype=F32, d=256) == fa.FA_ERROR_UNSUPPORTED
-    assert bwd(d=256) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(dtype=F32, d=512) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(d=192) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(d=96) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(dtype=F16, d=96) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(dtype=F16, B=0, q=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS

@@ -157,3 +157,21 @@ def test_fp32_backward_phases_match_the_single_call():
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_head_dim_256_backward(dtype):
+    """d = 256: four waves per work-group, one per SIMD, in the 16-bit
+    kernels; one-wave dK/dV blocks in the fp32 kernel."""
+    torch = torch_cuda()
+    for N in (1, 65, 200):
+        for causal in (False, True):
+            lengths = np.array([0, 1, N, max(N - 3, 0)], np.int32) if N > 1 else None
+            B = 2 if lengths is None else 4
+            cfg = custom(5, B=B, H=2, N=N, d=256, causal=causal, dtype=dtype)
+            log_case(test="bwd-d256", N=N, causal=causal, dtype=dtype)
+            inputs = fi.make_inputs(cfg, seed=300 + N)
+            inputs["lengths"] = lengths
+            o, lse, dq, dk, dv = run_fwd_bwd(torch, cfg, inputs)
+            heads = [(b, h) for b in range(B) for h in range(2)]
+            compare_heads(cfg, inputs, o, dq, dk, dv, heads)

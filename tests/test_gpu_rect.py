@@ -82,6 +82,22 @@ def test_rectangular_forward_and_backward(dtype, d, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rectangular_d256_backward(dtype):
+    torch = torch_cuda()
+    for Nq, Nk in ((33, 150), (150, 40)):
+        log_case(test="rect-d256-bwd", dtype=dtype, Nq=Nq, Nk=Nk)
+        cfg, t = rect_inputs(dtype, 2, 2, Nq, Nk, 256, seed=Nq * 7 + Nk)
+        o, lse, (dq, dk, dv) = run(torch, dtype, t, cfg.scale, True, None, True)
+        w = {n: fi.widen(t[n], dtype) for n in t}
+        ref_o, ref_l = oracle.attention_materialised(w["q"], w["k"], w["v"], cfg.scale, True)
+        rq, rk, rv = oracle.attention_backward(w["q"], w["k"], w["v"], ref_o, w["do"], ref_l,
+                                               cfg.scale, True)
+        for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+            g = from_device(got, dtype)
+            assert np.all(np.abs(g - ref) <= G_TOL[dtype] + ULP[dtype] * np.abs(ref))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_rectangular_d256_forward(dtype):
     torch = torch_cuda()
     for Nq, Nk in ((33, 300), (300, 100)):
