@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd/bwd TFLOP/s at N=8192,d=128 bf16; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3          # MI355X fp32 MFMA, published
+KV_LEN = None                    # key rows when they differ from the query rows
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("fa_common.hpp", "fa_fwd.hip", "fa_bwd.hip")
@@ -80,6 +81,9 @@ def parse_args():
                    help="run the --config workload in another element format (default: its own)")
     p.add_argument("--head-dim", type=int, default=None, choices=[64, 128, 256],
                    help="run the --config workload with another head dimension")
+    p.add_argument("--kv-len", type=int, default=None, metavar="NK",
+                   help="give keys and values NK rows instead of the queries' N (causal: query "
+                        "i sees keys j <= i + NK - N)")
     p.add_argument("--decode-lengths", default=None, choices=[None, "zero_then_uniform"],
                    help="cached lengths of the decode workload (default: all full)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -119,7 +123,7 @@ def cpu_baseline(cfg, inputs, budget_s):
             oracle.attention_backward(w["q"], w["k"], w["v"], o, w["do"], lse, cfg.scale,
                                       cfg.causal, lb)
         elapsed += time.perf_counter() - t0
-        flops += step_flops(cfg, lb, heads=1)
+        flops += step_flops(cfg, lb, heads=1, Nk=KV_LEN)
         done += 1
         if elapsed >= budget_s:
             break
@@ -131,11 +135,17 @@ def cpu_baseline(cfg, inputs, budget_s):
             "seconds": round(elapsed, 2)}
 
 
-def step_flops(cfg, lengths=None, heads=None):
-    """Credited FLOPs of one step (all heads, or `heads` heads)."""
+def step_flops(cfg, lengths=None, heads=None, Nk=None):
+    """Credited FLOPs of one step (all heads, or `heads` heads).  With Nk keys
+    (Nk != N) every visible pair is counted."""
     import fa_inputs as fi
     H = cfg.H if heads is None else 1
     B = cfg.B if heads is None else heads
+    if Nk is not None:
+        f = fi.useful_flops(B, H, cfg.N, cfg.d, cfg.causal, lengths, Nk=Nk)
+        if cfg.backward:
+            f += fi.useful_flops(B, H, cfg.N, cfg.d, cfg.causal, lengths, backward=True, Nk=Nk)
+        return f
     if lengths is not None:
         f = fi.useful_flops(B, H, cfg.N, cfg.d, cfg.causal, lengths)
         if cfg.backward:
@@ -183,7 +193,13 @@ def main():
 
     t0 = time.perf_counter()
     inputs = fi.make_inputs(cfg)
-    log(f"inputs generated in {time.perf_counter() - t0:.1f} s: {cfg.name}")
+    global KV_LEN
+    KV_LEN = args.kv_len if args.kv_len is not None and args.kv_len != cfg.N else None
+    if KV_LEN is not None:
+        for n in ("k", "v"):
+            inputs[n] = fi.make_tensor(cfg, n, 0, N=KV_LEN)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s: {cfg.name}"
+        + (f", {KV_LEN} keys" if KV_LEN else ""))
 
     def up(a):
         if cfg.dtype in fi.HALF_DTYPES:
@@ -197,7 +213,7 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev)
     if cfg.backward:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
         delta = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev)
 
     n_ev = 5 if cfg.backward else 2
@@ -236,13 +252,15 @@ def main():
         + f"; wall {wall * 1e3 / args.steps:.4f} ms/step")
 
     lengths = inputs["lengths"]
-    flops = step_flops(cfg, lengths)
+    flops = step_flops(cfg, lengths, Nk=KV_LEN)
     value = flops / (ms_per_step * 1e-3) / 1e12
     # bf16 and f16 share the dense MFMA peak; fp32 runs on the fp32 MFMA
     peak = PEAK_BF16_TFLOPS if cfg.dtype in fi.HALF_DTYPES else PEAK_F32_TFLOPS
 
     # credited FLOPs per launch of each compute kernel
-    if lengths is None:
+    if KV_LEN is not None:
+        fwd_f = fi.useful_flops(cfg.B, cfg.H, cfg.N, cfg.d, cfg.causal, lengths, Nk=KV_LEN)
+    elif lengths is None:
         fwd_f = fi.credited_flops(cfg.B, cfg.H, cfg.N, cfg.d, cfg.causal)
     else:
         fwd_f = fi.useful_flops(cfg.B, cfg.H, cfg.N, cfg.d, cfg.causal, lengths)
@@ -254,7 +272,7 @@ def main():
     achieved = kernel_flops[dominant] / (per_kernel[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": None if variant else measured_traffic(dominant, args.config)}
+                "traffic": None if variant or KV_LEN else measured_traffic(dominant, args.config)}
 
     extra = {
         "per_launch_ms": {n: round(t, 4) for n, t in per_kernel.items()},
@@ -292,7 +310,8 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded iid N(0,1) inputs)",
-        "config": {"workload": workload, "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d,
+        "config": {"workload": workload, "B": cfg.B, "H": cfg.H, "N": cfg.N,
+                   **({"kv_len": KV_LEN} if KV_LEN else {}), "d": cfg.d,
                    "causal": cfg.causal,
                    "key_lengths": None if lengths is None else [int(x) for x in lengths],
                    "credited_flops_per_step": flops},

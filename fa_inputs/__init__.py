@@ -211,23 +211,25 @@ def credited_flops(B, H, N, d, causal, backward=False):
     return total // 2 if causal else total
 
 
-def useful_pairs(N, causal, lengths=None, B=1):
-    """Visible (query, key) pairs per head, summed over the batch: with key
-    length L (clamped to [0, N]) and the causal mask, row i sees min(i+1, L)
-    keys; without it, L keys."""
+def useful_pairs(N, causal, lengths=None, B=1, Nk=None):
+    """Visible (query, key) pairs per head, summed over the batch: N query
+    rows, Nk keys (default N), key length L (clamped to [0, Nk]); with the
+    causal mask row i sees min(L, max(0, i + Nk - N + 1)) keys, without it L."""
+    Nk = N if Nk is None else Nk
+    rows = np.arange(N, dtype=np.int64)
     total = 0
     for b in range(B):
-        L = N if lengths is None else int(min(max(int(lengths[b]), 0), N))
+        L = Nk if lengths is None else int(min(max(int(lengths[b]), 0), Nk))
         if causal:
-            total += L * (L + 1) // 2 + (N - L) * L
+            total += int(np.clip(rows + (Nk - N) + 1, 0, L).sum())
         else:
             total += N * L
     return total
 
 
-def useful_flops(B, H, N, d, causal, lengths=None, backward=False):
+def useful_flops(B, H, N, d, causal, lengths=None, backward=False, Nk=None):
     """FLOPs on visible pairs only: 4d (forward) or 10d (backward) per pair."""
-    return (10 if backward else 4) * d * H * useful_pairs(N, causal, lengths, B)
+    return (10 if backward else 4) * d * H * useful_pairs(N, causal, lengths, B, Nk)
 
 
 def min_bytes(B, H, N, d, es, backward=False):

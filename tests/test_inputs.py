@@ -175,3 +175,12 @@ def test_f16_tensors_are_the_rounded_float32_draws():
     # the f16 value is the nearest binary16 value: within half an ulp
     ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(b), 2.0 ** -14))) - 10)
     assert np.all(np.abs(a - b) <= ulp / 2)
+
+
+def test_useful_pairs_rectangular_brute_force():
+    for N, Nk in ((5, 9), (9, 5), (1, 7), (7, 1), (6, 6)):
+        for causal in (False, True):
+            for L in (None, 0, 1, 3, Nk):
+                lens = None if L is None else np.array([L])
+                vis = oracle.visible_mask(np.arange(N), Nk, causal, L, offset=Nk - N)
+                assert fi.useful_pairs(N, causal, lens, Nk=Nk) == int(vis.sum())
