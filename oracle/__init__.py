@@ -26,6 +26,8 @@ from .attention import (
     finite_difference_grads,
     merge_states,
     attention_decode,
+    attention_packed,
+    attention_backward_packed,
 )
 
 __all__ = [
@@ -39,4 +41,6 @@ __all__ = [
     "finite_difference_grads",
     "merge_states",
     "attention_decode",
+    "attention_packed",
+    "attention_backward_packed",
 ]

@@ -8,7 +8,10 @@ HIP kernels.
 
 Layout: q, o, do are [B, H, Nq, d]; k, v are [B, H, Nk, d]; lse is
 [B, H, Nq]; lengths is a length-B integer array of key lengths (or None for
-"all Nk keys valid").  Usually Nq == Nk == N.
+"all Nk keys valid").  Usually Nq == Nk == N.  Packed batches (the *_packed
+routines) hold the sequences back to back, head-major: q, o, do are
+[H, total_q, d], k, v are [H, total_k, d], lse is [H, total_q], and sequence
+b owns query rows cu_q[b]:cu_q[b+1] and key rows cu_k[b]:cu_k[b+1].
 
 Semantics (the plain definition the tiled method reaches exactly):
   s_ij = scale * q_i . k_j,
@@ -45,6 +48,8 @@ __all__ = [
     "finite_difference_grads",
     "merge_states",
     "attention_decode",
+    "attention_packed",
+    "attention_backward_packed",
 ]
 
 
@@ -427,3 +432,57 @@ def attention_decode(q, k, v, scale, lengths=None, chunk=None):
                 parts_lse.append(m + np.log(e.sum()))
             o[b, h], lse[b, h] = merge_states(np.array(parts_o), np.array(parts_lse))
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Packed batches
+# ---------------------------------------------------------------------------
+#
+# The pages treat one sequence at a time; a packed batch is read as a set of
+# independent problems of that definition, one per sequence (its own Nq_b
+# queries, its own Nk_b keys, the causal offset Nk_b - Nq_b of its own).
+# Rows that belong to no sequence are left at O = 0, LSE = -inf and zero
+# gradients.
+
+def _packed_spans(cu):
+    cu = np.asarray(cu, dtype=np.int64).reshape(-1)
+    return [(int(cu[b]), int(cu[b + 1])) for b in range(cu.size - 1)]
+
+
+def attention_packed(q, k, v, cu_q, cu_k, scale, causal=False):
+    """Forward over a packed batch: each sequence is one problem of the plain
+    definition (attention_materialised on its rows).  Returns (O, LSE)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    H, total_q, _ = q.shape
+    o = np.zeros((H, total_q, v.shape[2]))
+    lse = np.full((H, total_q), -np.inf)
+    for (q0, q1), (k0, k1) in zip(_packed_spans(cu_q), _packed_spans(cu_k)):
+        if q1 <= q0:
+            continue
+        ob, lb = attention_materialised(q[None, :, q0:q1], k[None, :, k0:k1],
+                                        v[None, :, k0:k1], scale, causal)
+        o[:, q0:q1] = ob[0]
+        lse[:, q0:q1] = lb[0]
+    return o, lse
+
+
+def attention_backward_packed(q, k, v, o, do, lse, cu_q, cu_k, scale, causal=False):
+    """Gradients over a packed batch, one attention_backward per sequence.
+    Returns (dq, dk, dv) in the packed layout."""
+    q, k, v, o, do = (np.asarray(t, np.float64) for t in (q, k, v, o, do))
+    lse = np.asarray(lse, np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for (q0, q1), (k0, k1) in zip(_packed_spans(cu_q), _packed_spans(cu_k)):
+        if q1 <= q0 or k1 <= k0:
+            continue
+        g = attention_backward(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1],
+                               o[None, :, q0:q1], do[None, :, q0:q1], lse[None, :, q0:q1],
+                               scale, causal)
+        dq[:, q0:q1] = g[0][0]
+        dk[:, k0:k1] = g[1][0]
+        dv[:, k0:k1] = g[2][0]
+    return dq, dk, dv

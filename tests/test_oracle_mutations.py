@@ -134,3 +134,15 @@ def test_top_left_rectangular_alignment_is_caught(monkeypatch):
     assert _fails(pins.test_fewer_queries_are_the_last_rows_of_the_square_problem)
     assert _fails(pins.test_one_causal_query_sees_the_whole_cache)
     assert _fails(pins.test_more_queries_than_keys_leave_the_first_rows_empty)
+
+
+def test_packed_keys_taken_from_query_offsets_is_caught(monkeypatch):
+    """Slicing each sequence's keys with the query offsets (a plausible
+    mix-up of the two offset arrays) breaks the packed pins."""
+    real = oa.attention_packed
+
+    def mixed(q, k, v, cu_q, cu_k, scale, causal=False):
+        return real(q, k, v, cu_q, cu_q, scale, causal)
+
+    monkeypatch.setattr(oracle, "attention_packed", mixed)
+    assert _fails(pins.test_packed_queries_are_the_last_rows_of_each_sequence)

@@ -455,6 +455,110 @@ def test_rectangular_and_rows_helper():
 
 
 # ---------------------------------------------------------------------------
+# Packed batches: each sequence is its own problem
+# ---------------------------------------------------------------------------
+
+def _pack(t, starts, lens):
+    """Rows starts[b] .. starts[b] + lens[b] of each padded [B, H, L, d]
+    sequence, back to back: [H, sum(lens), d]."""
+    return np.concatenate([t[b, :, s0:s0 + n] for b, (s0, n) in enumerate(zip(starts, lens))],
+                          axis=1)
+
+
+def _cu(lens):
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+
+
+def test_packed_batch_equals_the_padded_batch_with_key_lengths():
+    """Sequences of lengths L_b packed back to back give, row for row, what the
+    padded batch with key lengths L_b gives on its first L_b rows: the padded
+    route masks keys by length, the packed one slices each sequence out."""
+    rng = np.random.default_rng(41)
+    H, d, Lmax = 2, 4, 11
+    lens = [5, 0, 11, 1, 7]
+    B = len(lens)
+    qp, kp, vp = (rng.standard_normal((B, H, Lmax, d)) for _ in range(3))
+    zero = [0] * B
+    q, k, v = (_pack(t, zero, lens) for t in (qp, kp, vp))
+    for causal in (False, True):
+        o, lse = oracle.attention_packed(q, k, v, _cu(lens), _cu(lens), 0.6, causal)
+        o_p, l_p = oracle.attention_materialised(qp, kp, vp, 0.6, causal, np.array(lens))
+        assert np.max(np.abs(o - _pack(o_p, zero, lens))) <= 1e-13
+        assert np.max(np.abs(lse - _pack(l_p[..., None], zero, lens)[..., 0])) <= 1e-13
+
+
+def test_packed_queries_are_the_last_rows_of_each_sequence():
+    """Sequence b holding the last nq_b of its Lk_b query positions against
+    its Lk_b keys equals rows Lk_b - nq_b .. Lk_b of the padded batch with
+    key lengths Lk_b (causal: the per-sequence offset is Lk_b - nq_b); a
+    sequence with more queries than keys leaves its first rows empty."""
+    rng = np.random.default_rng(42)
+    H, d, Lmax = 2, 3, 12
+    lk = [6, 9, 3, 12, 4]
+    lq = [6, 2, 0, 1, 4]
+    B = len(lk)
+    qp, kp, vp = (rng.standard_normal((B, H, Lmax, d)) for _ in range(3))
+    starts = [a - b for a, b in zip(lk, lq)]
+    q = _pack(qp, starts, lq)
+    k, v = (_pack(t, [0] * B, lk) for t in (kp, vp))
+    for causal in (False, True):
+        o, lse = oracle.attention_packed(q, k, v, _cu(lq), _cu(lk), 0.45, causal)
+        o_p, l_p = oracle.attention_materialised(qp, kp, vp, 0.45, causal, np.array(lk))
+        assert np.max(np.abs(o - _pack(o_p, starts, lq))) <= 1e-13
+        assert np.max(np.abs(lse - _pack(l_p[..., None], starts, lq)[..., 0])) <= 1e-13
+    # 7 queries against 3 keys: the first 4 precede every key
+    q7 = rng.standard_normal((H, 7, d))
+    k3, v3 = rng.standard_normal((2, H, 3, d))
+    o, lse = oracle.attention_packed(q7, k3, v3, [0, 7], [0, 3], 0.5, True)
+    assert np.all(o[:, :4] == 0.0) and np.all(np.isneginf(lse[:, :4]))
+    assert np.all(np.isfinite(lse[:, 4:]))
+
+
+def test_packed_backward_equals_the_padded_backward():
+    """Gradients of a packed batch equal those of the padded batch with key
+    lengths L_b when dO is zero on the padding rows (padding queries then add
+    nothing to dK and dV); the padded backward is pinned by finite
+    differences."""
+    rng = np.random.default_rng(43)
+    H, d, Lmax = 1, 3, 8
+    lens = [3, 8, 0, 5]
+    B = len(lens)
+    qp, kp, vp, dop = (rng.standard_normal((B, H, Lmax, d)) for _ in range(4))
+    for b, n in enumerate(lens):
+        dop[b, :, n:] = 0.0
+    zero = [0] * B
+    q, k, v, do = (_pack(t, zero, lens) for t in (qp, kp, vp, dop))
+    for causal in (False, True):
+        o, lse = oracle.attention_packed(q, k, v, _cu(lens), _cu(lens), 0.7, causal)
+        got = oracle.attention_backward_packed(q, k, v, o, do, lse, _cu(lens), _cu(lens), 0.7,
+                                               causal)
+        o_p, l_p = oracle.attention_materialised(qp, kp, vp, 0.7, causal, np.array(lens))
+        ref = oracle.attention_backward(qp, kp, vp, o_p, dop, l_p, 0.7, causal, np.array(lens))
+        for a, r in zip(got, ref):
+            assert np.max(np.abs(a - _pack(r, zero, lens))) <= 1e-13
+
+
+def test_packed_rows_outside_every_sequence_stay_empty():
+    """Rows that no sequence owns (a gap, a tail) get O = 0, LSE = -inf and
+    zero gradients; a packed sequence never reads them."""
+    rng = np.random.default_rng(44)
+    q, k, v, do = (rng.standard_normal((2, 10, 4)) for _ in range(4))
+    cu_q, cu_k = [1, 4, 4, 8], [0, 5, 6, 9]
+    o, lse = oracle.attention_packed(q, k, v, cu_q, cu_k, 0.5, True)
+    assert np.all(o[:, [0, 8, 9]] == 0.0) and np.all(np.isneginf(lse[:, [0, 8, 9]]))
+    dq, dk, dv = oracle.attention_backward_packed(q, k, v, o, do, lse, cu_q, cu_k, 0.5, True)
+    assert np.all(dq[:, [0, 8, 9]] == 0.0) and np.all(dk[:, 9] == 0.0) and np.all(dv[:, 9] == 0.0)
+    # sequence 2 (keys 5 .. 6, no queries) has zero key gradients
+    assert np.all(dk[:, 5] == 0.0) and np.all(dv[:, 5] == 0.0)
+    # changing the unowned rows changes nothing owned
+    q2, k2 = q.copy(), k.copy()
+    q2[:, [0, 8, 9]] = 9.0
+    k2[:, 9] = -7.0
+    o2, lse2 = oracle.attention_packed(q2, k2, v, cu_q, cu_k, 0.5, True)
+    assert np.array_equal(o2[:, 1:8], o[:, 1:8]) and np.array_equal(lse2[:, 1:8], lse[:, 1:8])
+
+
+# ---------------------------------------------------------------------------
 # Backward: finite differences and invariants
 # ---------------------------------------------------------------------------
 
