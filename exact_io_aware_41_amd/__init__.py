@@ -26,8 +26,9 @@ __all__ = [
     "FAError", "FALibraryMissing", "LIB_PATH", "load_library",
     "fa_abi_version", "fa_status_string", "fa_forward", "fa_backward",
     "fa_backward_workspace_size", "fa_backward_preprocess", "fa_backward_dkdv",
-    "fa_backward_dq", "fa_decode_workspace_size", "fa_decode", "fa_merge_states",
-    "forward", "backward", "backward_phases", "decode", "merge_states",
+    "fa_backward_dq", "fa_forward_varlen", "fa_backward_varlen", "fa_decode_workspace_size",
+    "fa_decode", "fa_merge_states", "forward", "backward", "backward_phases", "forward_varlen",
+    "backward_varlen", "decode", "merge_states",
 ]
 
 FA_SUCCESS = 0
@@ -40,8 +41,9 @@ FA_DTYPE_F16 = 2
 
 EXPORTED_SYMBOLS = ("fa_abi_version", "fa_status_string", "fa_forward",
                     "fa_backward_workspace_size", "fa_backward", "fa_backward_preprocess",
-                    "fa_backward_dkdv", "fa_backward_dq", "fa_decode_workspace_size",
-                    "fa_decode", "fa_merge_states")
+                    "fa_backward_dkdv", "fa_backward_dq", "fa_forward_varlen",
+                    "fa_backward_varlen", "fa_decode_workspace_size", "fa_decode",
+                    "fa_merge_states")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_mi355x.so")
 
@@ -90,6 +92,12 @@ def load_library():
     lib.fa_backward_dq.restype = i32
     lib.fa_backward_dq.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32,
                                    i32, vp, vp]
+    lib.fa_forward_varlen.restype = i32
+    lib.fa_forward_varlen.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                      f32, i32, vp, vp, vp]
+    lib.fa_backward_varlen.restype = i32
+    lib.fa_backward_varlen.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                       vp, vp, vp, f32, i32, vp, vp, vp, vp, sz, vp]
     lib.fa_decode_workspace_size.restype = sz
     lib.fa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_decode.restype = i32
@@ -143,6 +151,22 @@ def fa_backward_dq(dtype, B, H, Nq, Nk, d, q, k, v, dout, lse, delta, seqlens_k,
                    dq, stream=0) -> int:
     return load_library().fa_backward_dq(dtype, B, H, Nq, Nk, d, q, k, v, dout, lse, delta,
                                          seqlens_k, scale, causal, dq, stream)
+
+
+def fa_forward_varlen(dtype, B, H, total_q, total_k, max_seqlen_q, max_seqlen_k, d, q, k, v,
+                      cu_seqlens_q, cu_seqlens_k, scale, causal, o, lse, stream=0) -> int:
+    return load_library().fa_forward_varlen(dtype, B, H, total_q, total_k, max_seqlen_q,
+                                            max_seqlen_k, d, q, k, v, cu_seqlens_q, cu_seqlens_k,
+                                            scale, causal, o, lse, stream)
+
+
+def fa_backward_varlen(dtype, B, H, total_q, total_k, max_seqlen_q, max_seqlen_k, d, q, k, v, o,
+                       dout, lse, cu_seqlens_q, cu_seqlens_k, scale, causal, dq, dk, dv,
+                       workspace, workspace_bytes, stream=0) -> int:
+    return load_library().fa_backward_varlen(dtype, B, H, total_q, total_k, max_seqlen_q,
+                                             max_seqlen_k, d, q, k, v, o, dout, lse,
+                                             cu_seqlens_q, cu_seqlens_k, scale, causal, dq, dk,
+                                             dv, workspace, workspace_bytes, stream)
 
 
 def fa_decode_workspace_size(dtype, B, H, N, d) -> int:
@@ -278,6 +302,92 @@ def backward(q, k, v, o, do, lse, scale=None, causal=False, seqlens_k=None,
                      _stream(q.device))
     if st != FA_SUCCESS:
         raise FAError(st, "fa_backward")
+    return dq, dk, dv
+
+
+def _check_packed(q, k, v, cu_seqlens_q, cu_seqlens_k):
+    """q [H, total_q, d]; k, v [H, total_k, d] with q's H, d, dtype, device;
+    int32 [B + 1] offsets on q's device.  Returns B."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or k.shape[0] != q.shape[0] \
+            or k.shape[2] != q.shape[2]:
+        raise ValueError("q must be [H, total_q, d] and k, v [H, total_k, d]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with q's dtype and device")
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if (cu.dtype != torch.int32 or cu.device != q.device or cu.dim() != 1
+                or cu.numel() < 1 or not cu.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 [B + 1] tensor on q's device")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    return cu_seqlens_q.numel() - 1
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None,
+                   causal=False, out=None, lse=None):
+    """Attention over a packed batch: sequence b owns query rows
+    cu_seqlens_q[b]:cu_seqlens_q[b+1] of q [H, total_q, d] and key rows
+    cu_seqlens_k[b]:cu_seqlens_k[b+1] of k, v [H, total_k, d]; each sequence
+    is its own problem (causal: query i of the sequence sees its keys
+    j <= i + nk_b - nq_b).  ``max_seqlen_q`` / ``max_seqlen_k`` bound every
+    sequence's lengths.  Returns (o like q, lse fp32 [H, total_q]); rows of
+    no sequence are o = 0, lse = -inf when the outputs are allocated here.
+    """
+    import torch
+    B = _check_packed(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    H, total_q, d = q.shape
+    total_k = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.zeros_like(q)
+    _check_like("out", out, q)
+    if lse is None:
+        lse = torch.full((H, total_q), -math.inf, dtype=torch.float32, device=q.device)
+    if lse.shape != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [H, total_q] tensor")
+    st = fa_forward_varlen(_dtype_code(q), B, H, total_q, total_k, int(max_seqlen_q),
+                           int(max_seqlen_k), d, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                           _ptr(cu_seqlens_k), float(scale), int(bool(causal)), _ptr(out),
+                           _ptr(lse), _stream(q.device))
+    if st != FA_SUCCESS:
+        raise FAError(st, "fa_forward_varlen")
+    return out, lse
+
+
+def backward_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    scale=None, causal=False, dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV of <dO, O> for a previous ``forward_varlen`` call, in the
+    packed layout; rows of no sequence are zero when the outputs are
+    allocated here."""
+    import torch
+    B = _check_packed(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    for name, t in (("o", o), ("do", do)):
+        _check_like(name, t, q)
+    H, total_q, d = q.shape
+    total_k = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if lse.shape != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [H, total_q] tensor")
+    dq = torch.zeros_like(q) if dq is None else dq
+    dk = torch.zeros_like(k) if dk is None else dk
+    dv = torch.zeros_like(k) if dv is None else dv
+    _check_like("dq", dq, q)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check_like(name, t, k)
+    code = _dtype_code(q)
+    ws_bytes = fa_backward_workspace_size(code, 1, H, total_q, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    st = fa_backward_varlen(code, B, H, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), d,
+                            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                            _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), float(scale),
+                            int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(q.device))
+    if st != FA_SUCCESS:
+        raise FAError(st, "fa_backward_varlen")
     return dq, dk, dv
 
 

@@ -11,8 +11,11 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr long long kMaxGrid = 0x7fffffffLL;
+// one head's rows of one sequence must be addressable with 32-bit byte
+// offsets (the kernels' buffer descriptors)
+constexpr long long kMaxHeadBytes = 0x7fffffffLL;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -61,6 +64,10 @@ constexpr int kMaxDecodeN = 4096 * 4096;
 
 bool known_dtype(fa_dtype dtype) { return dtype == FA_DTYPE_F32 || is_half(dtype); }
 
+bool head_fits(fa_dtype dtype, int rows, int d) {
+  return (long long)rows * d * (is_half(dtype) ? 2 : 4) <= kMaxHeadBytes;
+}
+
 // Shared size/scale/flag checks.  Returns FA_SUCCESS when the problem is
 // well formed; *empty is set when there is nothing to compute.
 fa_status check_common(fa_dtype dtype, int B, int H, int N, int d, float scale, int causal,
@@ -98,6 +105,7 @@ fa_status fa_forward(fa_dtype dtype, int B, int H, int Nq, int Nk, int d, const 
   if (st != FA_SUCCESS) return st;
   if (Nk < 0) return FA_ERROR_INVALID_VALUE;
   if (!fwd_supported(dtype, d)) return FA_ERROR_UNSUPPORTED;
+  if (!head_fits(dtype, Nq, d) || !head_fits(dtype, Nk, d)) return FA_ERROR_UNSUPPORTED;
   if (empty) return FA_SUCCESS;   // no query rows: nothing to write
   // with no keys the rows are written empty and k, v are never read
   if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA_ERROR_INVALID_VALUE;
@@ -131,6 +139,7 @@ fa_status fa_backward(fa_dtype dtype, int B, int H, int Nq, int Nk, int d, const
   if (st != FA_SUCCESS) return st;
   if (Nk < 0) return FA_ERROR_INVALID_VALUE;
   if (!bwd_supported(dtype, d)) return FA_ERROR_UNSUPPORTED;
+  if (!head_fits(dtype, Nq, d) || !head_fits(dtype, Nk, d)) return FA_ERROR_UNSUPPORTED;
   // with no query rows dK and dV are still written (zeros); with no keys, dQ.
   // Buffers of a side without rows are never touched and may be NULL.
   if (B == 0 || H == 0 || (Nq == 0 && Nk == 0)) return FA_SUCCESS;
@@ -181,6 +190,7 @@ fa_status check_bwd_phase(fa_dtype dtype, int B, int H, int Nq, int Nk, int d, c
   if (st != FA_SUCCESS) return st;
   if (Nk < 0) return FA_ERROR_INVALID_VALUE;
   if (!bwd_supported(dtype, d)) return FA_ERROR_UNSUPPORTED;
+  if (!head_fits(dtype, Nq, d) || !head_fits(dtype, Nk, d)) return FA_ERROR_UNSUPPORTED;
   *empty = B == 0 || H == 0 || (keys_out ? Nk == 0 : Nq == 0);
   if (*empty) return FA_SUCCESS;
   if (!out0 || !out1) return FA_ERROR_INVALID_VALUE;
@@ -221,6 +231,81 @@ fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int Nq, int Nk, int d, co
                 lse, seqlens_k, scale, causal, dq, nullptr, nullptr, const_cast<float*>(delta),
                 stream};
   return bwd_dq(dtype, a) == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+}
+
+namespace {
+// Checks shared by the packed-batch calls: sizes, offsets arrays, the grid.
+fa_status check_varlen(fa_dtype dtype, int B, int H, int total_q, int total_k, int max_q,
+                       int max_k, int d, float scale, int causal, const int32_t* cu_q,
+                       const int32_t* cu_k, bool backward) {
+  bool empty = false;
+  fa_status st = check_common(dtype, B, H, total_q, d, scale, causal, &empty);
+  if (st != FA_SUCCESS) return st;
+  if (total_k < 0 || max_q < 0 || max_k < 0) return FA_ERROR_INVALID_VALUE;
+  if (!(backward ? bwd_supported(dtype, d) : fwd_supported(dtype, d)))
+    return FA_ERROR_UNSUPPORTED;
+  if (!head_fits(dtype, max_q, d) || !head_fits(dtype, max_k, d)) return FA_ERROR_UNSUPPORTED;
+  if (B == 0 || H == 0) return FA_SUCCESS;
+  if (!cu_q || !cu_k) return FA_ERROR_INVALID_VALUE;
+  if ((reinterpret_cast<uintptr_t>(cu_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_k) & 3u))
+    return FA_ERROR_INVALID_VALUE;
+  const long long grid =
+      backward ? bwd_grid(dtype, B, H, max_q > max_k ? max_q : max_k, d)
+               : (is_half(dtype) ? fa::fwd_half_grid(B, H, max_q, d)
+                                 : fa::fwd_f32_grid(B, H, max_q, d));
+  if (grid > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  return FA_SUCCESS;
+}
+}  // namespace
+
+fa_status fa_forward_varlen(fa_dtype dtype, int B, int H, int total_q, int total_k,
+                            int max_seqlen_q, int max_seqlen_k, int d, const void* q,
+                            const void* k, const void* v, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, float scale, int causal, void* o,
+                            float* lse, hipStream_t stream) {
+  fa_status st = check_varlen(dtype, B, H, total_q, total_k, max_seqlen_q, max_seqlen_k, d,
+                              scale, causal, cu_seqlens_q, cu_seqlens_k, false);
+  if (st != FA_SUCCESS) return st;
+  if (B == 0 || H == 0 || total_q == 0 || max_seqlen_q == 0) return FA_SUCCESS;
+  const bool keys = total_k > 0 && max_seqlen_k > 0;
+  if (!q || !o || !lse || (keys && (!k || !v))) return FA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERROR_INVALID_VALUE;
+  fa::FwdArgs a{B, H, max_seqlen_q, d, max_seqlen_k, q, k, v, nullptr, scale, causal, o, lse,
+                stream, cu_seqlens_q, cu_seqlens_k, total_q, total_k};
+  const hipError_t e =
+      is_half(dtype) ? fa::launch_fwd_half(a, elt_of(dtype)) : fa::launch_fwd_f32(a);
+  return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+}
+
+fa_status fa_backward_varlen(fa_dtype dtype, int B, int H, int total_q, int total_k,
+                             int max_seqlen_q, int max_seqlen_k, int d, const void* q,
+                             const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, float scale, int causal, void* dq,
+                             void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  fa_status st = check_varlen(dtype, B, H, total_q, total_k, max_seqlen_q, max_seqlen_k, d,
+                              scale, causal, cu_seqlens_q, cu_seqlens_k, true);
+  if (st != FA_SUCCESS) return st;
+  const bool queries = total_q > 0 && max_seqlen_q > 0;
+  const bool keys = total_k > 0 && max_seqlen_k > 0;
+  if (B == 0 || H == 0 || (!queries && !keys)) return FA_SUCCESS;
+  if (queries && (!q || !o || !dout || !lse || !dq || !workspace)) return FA_ERROR_INVALID_VALUE;
+  if (keys && (!k || !v || !dk || !dv)) return FA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(workspace))
+    return FA_ERROR_INVALID_VALUE;
+  if (queries && workspace_bytes < fa_backward_workspace_size(dtype, 1, H, total_q, d))
+    return FA_ERROR_INVALID_VALUE;
+  // with no query rows the row statistics are never read: nothing to compute
+  fa::BwdArgs a{B,   H,       queries ? max_seqlen_q : 0, d,  keys ? max_seqlen_k : 0,
+                q,   k,       v,       o,  dout, lse, nullptr, scale, causal, dq, dk, dv,
+                static_cast<float*>(workspace), stream, cu_seqlens_q, cu_seqlens_k,
+                queries ? total_q : 0, keys ? total_k : 0};
+  const hipError_t e = bwd_all(dtype, a);
+  return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
 }
 
 size_t fa_decode_workspace_size(fa_dtype dtype, int B, int H, int N, int d) {

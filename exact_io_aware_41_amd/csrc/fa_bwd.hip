@@ -116,8 +116,10 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
                              const float* __restrict__ LSE, const float* __restrict__ Dlt,
                              const int32_t* __restrict__ seqlens_k, float scale,
                              float scale_log2, int causal, typename E::T* __restrict__ dK,
-                             typename E::T* __restrict__ dV, int B, int H, int N, int Nk,
-                             int n_ktiles) {
+                             typename E::T* __restrict__ dV, int B, int H, int n_q, int n_k,
+                             int n_ktiles,
+                             const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                             int total_q, int total_k) {
   using elt = typename E::T;
   using elt8 = typename E::V8;
   using elt4 = typename E::V4;
@@ -142,15 +144,17 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
   const int bh = blockIdx.x - kt * bh_count;
   const int b = bh / H;
   const int h = bh - b * H;
-  const size_t head = (size_t)b * H + h;
-  const elt* Qh = Q + head * (size_t)N * D;
-  const elt* Kh = K + head * (size_t)Nk * D;
-  const elt* Vh = V + head * (size_t)Nk * D;
-  const elt* dOh = dO + head * (size_t)N * D;
-  const float* Lh = LSE + head * (size_t)N;
-  const float* Dh = Dlt + head * (size_t)N;
-  elt* dKh = dK + head * (size_t)Nk * D;
-  elt* dVh = dV + head * (size_t)Nk * D;
+  const SeqSpan sp = seq_span(b, h, H, n_q, n_k, cu_q, cu_k, total_q, total_k);
+  const int N = sp.nq, Nk = sp.nk;   // this sequence's query and key rows
+  if (kt * C::BK >= Nk) return;      // a key tile past a shorter sequence
+  const elt* Qh = Q + sp.q_row0 * D;
+  const elt* Kh = K + sp.k_row0 * D;
+  const elt* Vh = V + sp.k_row0 * D;
+  const elt* dOh = dO + sp.q_row0 * D;
+  const float* Lh = LSE + sp.q_row0;
+  const float* Dh = Dlt + sp.q_row0;
+  elt* dKh = dK + sp.k_row0 * D;
+  elt* dVh = dV + sp.k_row0 * D;
 
   const int kv_len = key_length(seqlens_k, b, Nk);
   const int off = Nk - N;   // query i sits at key position i + off
@@ -367,8 +371,9 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
                       const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
                       const float* __restrict__ LSE, const float* __restrict__ Dlt,
                       const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
-                      int causal, typename E::T* __restrict__ dQ, int B, int H, int N, int Nk,
-                      int n_qtiles) {
+                      int causal, typename E::T* __restrict__ dQ, int B, int H, int n_q, int n_k,
+                      int n_qtiles, const int32_t* __restrict__ cu_q,
+                      const int32_t* __restrict__ cu_k, int total_q, int total_k) {
   using elt = typename E::T;
   using elt8 = typename E::V8;
   using elt4 = typename E::V4;
@@ -384,12 +389,14 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
   const int hi = lane >> 5;
 
   const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
-  const size_t head = (size_t)tc.b * H + tc.h;
-  const elt* Qh = Q + head * (size_t)N * D;
-  const elt* Kh = K + head * (size_t)Nk * D;
-  const elt* Vh = V + head * (size_t)Nk * D;
-  const elt* dOh = dO + head * (size_t)N * D;
-  elt* dQh = dQ + head * (size_t)N * D;
+  const SeqSpan sp = seq_span(tc.b, tc.h, H, n_q, n_k, cu_q, cu_k, total_q, total_k);
+  const int N = sp.nq, Nk = sp.nk;   // this sequence's query and key rows
+  if (tc.qt * C::BR >= N) return;    // a query tile past a shorter sequence
+  const elt* Qh = Q + sp.q_row0 * D;
+  const elt* Kh = K + sp.k_row0 * D;
+  const elt* Vh = V + sp.k_row0 * D;
+  const elt* dOh = dO + sp.q_row0 * D;
+  elt* dQh = dQ + sp.q_row0 * D;
 
   const int kv_len = key_length(seqlens_k, tc.b, Nk);
   const int off = Nk - N;   // query i sits at key position i + off
@@ -413,9 +420,9 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
   }
   float lse2 = __builtin_huge_valf(), drow = 0.f;
   if (qrow < N) {
-    const float lse = LSE[head * (size_t)N + qrow];
+    const float lse = LSE[sp.q_row0 + qrow];
     lse2 = (lse == kNegInf) ? __builtin_huge_valf() : lse * kLog2e;
-    drow = Dlt[head * (size_t)N + qrow];
+    drow = Dlt[sp.q_row0 + qrow];
   }
 
   f32x16 dqacc[C::NDB];
@@ -562,7 +569,7 @@ struct BwdWaves {
 template <class E, int D>
 hipError_t launch_preprocess_d(const BwdArgs& a) {
   using T = typename E::T;
-  const long long rows = (long long)a.B * a.H * a.N;
+  const long long rows = a.cu_q ? (long long)a.H * a.total_q : (long long)a.B * a.H * a.N;
   if (rows == 0) return hipSuccess;
   const long long threads = rows * (D / 8);
   hipLaunchKernelGGL((fa_bwd_rowdot_kernel<E, D>), dim3((unsigned)((threads + 255) / 256)),
@@ -582,7 +589,8 @@ hipError_t launch_dkdv_d(const BwdArgs& a) {
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
                      a.seqlens_k, a.scale, a.scale * kLog2e, a.causal, static_cast<T*>(a.dk),
-                     static_cast<T*>(a.dv), a.B, a.H, a.N, a.Nk, n_ktiles);
+                     static_cast<T*>(a.dv), a.B, a.H, a.N, a.Nk, n_ktiles,
+                     a.cu_q, a.cu_k, a.total_q, a.total_k);
   return hipGetLastError();
 }
 
@@ -597,7 +605,8 @@ hipError_t launch_dq_d(const BwdArgs& a) {
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
                      a.seqlens_k, a.scale, a.scale * kLog2e, a.causal, static_cast<T*>(a.dq),
-                     a.B, a.H, a.N, a.Nk, n_qtiles);
+                     a.B, a.H, a.N, a.Nk, n_qtiles,
+                     a.cu_q, a.cu_k, a.total_q, a.total_k);
   return hipGetLastError();
 }
 

@@ -101,7 +101,9 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
                             const float* __restrict__ LSE, const float* __restrict__ Dlt,
                             const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
                             int causal, float* __restrict__ dK, float* __restrict__ dV, int B,
-                            int H, int N, int Nk, int n_kblocks) {
+                            int H, int n_q, int n_k, int n_kblocks,
+                            const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                            int total_q, int total_k) {
   using C = F32BwdCfg<D>;
   constexpr int NT = NW * 64;
   constexpr int BK = NW * 32;       // keys per work-group
@@ -123,13 +125,15 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
   const int kb = blockIdx.x / bh_count;
   const int bh = blockIdx.x - kb * bh_count;
   const int b = bh / H;
-  const size_t head = (size_t)bh;
-  const float* Qh = Q + head * (size_t)N * D;
-  const float* Kh = K + head * (size_t)Nk * D;
-  const float* Vh = V + head * (size_t)Nk * D;
-  const float* dOh = dO + head * (size_t)N * D;
-  const float* Lh = LSE + head * (size_t)N;
-  const float* Dh = Dlt + head * (size_t)N;
+  const SeqSpan sp = seq_span(b, bh - b * H, H, n_q, n_k, cu_q, cu_k, total_q, total_k);
+  const int N = sp.nq, Nk = sp.nk;   // this sequence's query and key rows
+  if (kb * BK >= Nk) return;         // a key block past a shorter sequence
+  const float* Qh = Q + sp.q_row0 * D;
+  const float* Kh = K + sp.k_row0 * D;
+  const float* Vh = V + sp.k_row0 * D;
+  const float* dOh = dO + sp.q_row0 * D;
+  const float* Lh = LSE + sp.q_row0;
+  const float* Dh = Dlt + sp.q_row0;
   const int kv_len = key_length(seqlens_k, b, Nk);
   const int off = Nk - N;   // query i sits at key position i + off
   const int k0 = kb * BK;
@@ -210,8 +214,8 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
 
   // dV[key][feature], dK = scale * acc: accumulator lane l holds feature
   // 32 db + l % 32 of keys kw0 + c_row(v, l)
-  float* dKh = dK + head * (size_t)Nk * D;
-  float* dVh = dV + head * (size_t)Nk * D;
+  float* dKh = dK + sp.k_row0 * D;
+  float* dVh = dV + sp.k_row0 * D;
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -230,8 +234,9 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
                           const float* __restrict__ V, const float* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Dlt,
                           const int32_t* __restrict__ seqlens_k, float scale, float scale_log2,
-                          int causal, float* __restrict__ dQ, int B, int H, int N, int Nk,
-                          int n_qtiles) {
+                          int causal, float* __restrict__ dQ, int B, int H, int n_q, int n_k,
+                          int n_qtiles, const int32_t* __restrict__ cu_q,
+                          const int32_t* __restrict__ cu_k, int total_q, int total_k) {
   using C = F32BwdCfg<D>;
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32;       // query rows per work-group
@@ -246,11 +251,13 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
   const int hi = lane >> 5;
 
   const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
-  const size_t head = (size_t)tc.b * H + tc.h;
-  const float* Qh = Q + head * (size_t)N * D;
-  const float* Kh = K + head * (size_t)Nk * D;
-  const float* Vh = V + head * (size_t)Nk * D;
-  const float* dOh = dO + head * (size_t)N * D;
+  const SeqSpan sp = seq_span(tc.b, tc.h, H, n_q, n_k, cu_q, cu_k, total_q, total_k);
+  const int N = sp.nq, Nk = sp.nk;   // this sequence's query and key rows
+  if (tc.qt * BR >= N) return;       // a query tile past a shorter sequence
+  const float* Qh = Q + sp.q_row0 * D;
+  const float* Kh = K + sp.k_row0 * D;
+  const float* Vh = V + sp.k_row0 * D;
+  const float* dOh = dO + sp.q_row0 * D;
   const int kv_len = key_length(seqlens_k, tc.b, Nk);
   const int off = Nk - N;   // query i sits at key position i + off
   const int q0 = tc.qt * BR;
@@ -264,8 +271,8 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
     qf[ks] = qrow < N ? Qh[(size_t)qrow * D + 2 * ks + hi] : 0.f;
     of[ks] = qrow < N ? dOh[(size_t)qrow * D + 2 * ks + hi] : 0.f;
   }
-  const float lse2 = qrow < N ? LSE[head * (size_t)N + qrow] * kLog2e : 0.f;
-  const float drow = qrow < N ? Dlt[head * (size_t)N + qrow] : 0.f;
+  const float lse2 = qrow < N ? LSE[sp.q_row0 + qrow] * kLog2e : 0.f;
+  const float drow = qrow < N ? Dlt[sp.q_row0 + qrow] : 0.f;
 
   int kv_end = kv_len;
   if (causal) kv_end = min(kv_end, max(0, min(q0 + BR + off, Nk)));
@@ -319,7 +326,7 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
   // dQ^T accumulator lane l holds query l % 32 and features
   // 32 db + 8 (v / 4) + 4 (l / 32) + v % 4
   if (qrow < N) {
-    float* dQh = dQ + head * (size_t)N * D;
+    float* dQh = dQ + sp.q_row0 * D;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -335,7 +342,7 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
 
 template <int D>
 hipError_t launch_preprocess_f32_d(const BwdArgs& a) {
-  const long long rows = (long long)a.B * a.H * a.N;
+  const long long rows = a.cu_q ? (long long)a.H * a.total_q : (long long)a.B * a.H * a.N;
   if (rows == 0) return hipSuccess;
   const long long threads = rows * (D / 4);
   hipLaunchKernelGGL((fa_bwd_rowdot_f32_kernel<D>), dim3((unsigned)((threads + 255) / 256)),
@@ -355,7 +362,8 @@ hipError_t launch_dkdv_f32_d(const BwdArgs& a) {
                      static_cast<const float*>(a.v), static_cast<const float*>(a.dout), a.lse,
                      a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
                      static_cast<float*>(a.dk), static_cast<float*>(a.dv), a.B, a.H, a.N, a.Nk,
-                     n_kblocks);
+                     n_kblocks,
+                     a.cu_q, a.cu_k, a.total_q, a.total_k);
   return hipGetLastError();
 }
 
@@ -369,7 +377,8 @@ hipError_t launch_dq_f32_d(const BwdArgs& a) {
                      a.stream, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), static_cast<const float*>(a.dout), a.lse,
                      a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
-                     static_cast<float*>(a.dq), a.B, a.H, a.N, a.Nk, n_qtiles);
+                     static_cast<float*>(a.dq), a.B, a.H, a.N, a.Nk, n_qtiles,
+                     a.cu_q, a.cu_k, a.total_q, a.total_k);
   return hipGetLastError();
 }
 

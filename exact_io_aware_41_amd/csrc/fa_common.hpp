@@ -263,6 +263,39 @@ __device__ __forceinline__ int key_length(const int32_t* seqlens_k, int b, int N
 struct TileCoord {
   int b, h, qt;
 };
+
+// Where the rows of one (sequence b, head h) live.  Padded layout
+// (cu_q == nullptr): [B][H][N][d] queries and [B][H][Nk][d] keys, every
+// sequence N query rows and Nk key rows.  Packed layout: sequence b owns
+// query rows cu_q[b] .. cu_q[b+1] of head h in [H][total_q][d] and key rows
+// cu_k[b] .. cu_k[b+1] of [H][total_k][d] (lse and the row statistics
+// [H][total_q]); offsets and lengths are clamped to the buffers and to
+// N / Nk (the longest sequences the launch covers), so malformed offsets
+// cannot move an access outside them.
+struct SeqSpan {
+  size_t q_row0, k_row0;   // first query / key row, in rows
+  int nq, nk;              // query / key rows of this sequence
+};
+__device__ __forceinline__ SeqSpan seq_span(int b, int h, int H, int N, int Nk,
+                                            const int32_t* cu_q, const int32_t* cu_k,
+                                            int total_q, int total_k) {
+  SeqSpan s;
+  if (cu_q == nullptr) {
+    const size_t head = (size_t)b * H + h;
+    s.q_row0 = head * (size_t)N;
+    s.k_row0 = head * (size_t)Nk;
+    s.nq = N;
+    s.nk = Nk;
+    return s;
+  }
+  const int q_lo = min(max(cu_q[b], 0), total_q);
+  const int k_lo = min(max(cu_k[b], 0), total_k);
+  s.nq = min(min(max(cu_q[b + 1] - q_lo, 0), total_q - q_lo), N);
+  s.nk = min(min(max(cu_k[b + 1] - k_lo, 0), total_k - k_lo), Nk);
+  s.q_row0 = (size_t)h * total_q + q_lo;
+  s.k_row0 = (size_t)h * total_k + k_lo;
+  return s;
+}
 __device__ __forceinline__ TileCoord tile_coord(int wg, int B, int H, int n_qtiles) {
   const int bh_count = B * H;
   const int qt_rev = wg / bh_count;

@@ -97,8 +97,9 @@ __attribute__((amdgpu_waves_per_eu(QB == 1 && D <= 128 ? 2 : 1, QB == 1 && D <= 
 void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
                         const typename E::T* __restrict__ V, const int32_t* __restrict__ seqlens_k,
                         float scale_log2, int causal, typename E::T* __restrict__ O,
-                        float* __restrict__ LSE, int B, int H, int N, int Nk,
-                        int n_qtiles) {
+                        float* __restrict__ LSE, int B, int H, int n_q, int n_k,
+                        int n_qtiles, const int32_t* __restrict__ cu_q,
+                        const int32_t* __restrict__ cu_k, int total_q, int total_k) {
   using elt = typename E::T;
   using elt8 = typename E::V8;
   using elt4 = typename E::V4;
@@ -124,12 +125,14 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
   const bool lagging = kPingPong && wave >= NW / 2;
 
   const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
-  const size_t head = (size_t)tc.b * H + tc.h;
-  const elt* Qh = Q + head * (size_t)N * D;
-  const elt* Kh = K + head * (size_t)Nk * D;
-  const elt* Vh = V + head * (size_t)Nk * D;
-  elt* Oh = O + head * (size_t)N * D;
-  float* Lh = LSE + head * (size_t)N;
+  const SeqSpan sp = seq_span(tc.b, tc.h, H, n_q, n_k, cu_q, cu_k, total_q, total_k);
+  const int N = sp.nq, Nk = sp.nk;   // this sequence's query and key rows
+  if (tc.qt * C::BR >= N) return;    // a query tile past a shorter sequence
+  const elt* Qh = Q + sp.q_row0 * D;
+  const elt* Kh = K + sp.k_row0 * D;
+  const elt* Vh = V + sp.k_row0 * D;
+  elt* Oh = O + sp.q_row0 * D;
+  float* Lh = LSE + sp.q_row0;
 
   const int kv_len = key_length(seqlens_k, tc.b, Nk);
   // N queries, Nk keys: query i sits at key position i + off (the queries are
@@ -482,8 +485,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, const int32_t* __restrict__ seqlens_k,
                        float scale_log2, int causal, float* __restrict__ O,
-                       float* __restrict__ LSE, int B, int H, int N, int Nk,
-                       int n_qtiles) {
+                       float* __restrict__ LSE, int B, int H, int n_q, int n_k,
+                       int n_qtiles, const int32_t* __restrict__ cu_q,
+                       const int32_t* __restrict__ cu_k, int total_q, int total_k) {
   using C = FwdF32Cfg<D, NW, BC>;
   __shared__ __attribute__((aligned(16))) float Ks[2][BC * C::KPITCH];
   __shared__ __attribute__((aligned(16))) float Vs[2][BC * C::VPITCH];
@@ -495,12 +499,14 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   const int hi = lane >> 5;
 
   const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
-  const size_t head = (size_t)tc.b * H + tc.h;
-  const float* Qh = Q + head * (size_t)N * D;
-  const float* Kh = K + head * (size_t)Nk * D;
-  const float* Vh = V + head * (size_t)Nk * D;
-  float* Oh = O + head * (size_t)N * D;
-  float* Lh = LSE + head * (size_t)N;
+  const SeqSpan sp = seq_span(tc.b, tc.h, H, n_q, n_k, cu_q, cu_k, total_q, total_k);
+  const int N = sp.nq, Nk = sp.nk;   // this sequence's query and key rows
+  if (tc.qt * C::BR >= N) return;    // a query tile past a shorter sequence
+  const float* Qh = Q + sp.q_row0 * D;
+  const float* Kh = K + sp.k_row0 * D;
+  const float* Vh = V + sp.k_row0 * D;
+  float* Oh = O + sp.q_row0 * D;
+  float* Lh = LSE + sp.q_row0;
 
   const int kv_len = key_length(seqlens_k, tc.b, Nk);
   const int off = Nk - N;   // query i sits at key position i + off
@@ -692,7 +698,8 @@ hipError_t launch_half_d(const FwdArgs& a) {
   hipLaunchKernelGGL((fa_fwd_half_kernel<E, D, kBf16QB, NW, BC>), grid, dim3(C::NT), 0,
                      a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), a.seqlens_k, a.scale * kLog2e, a.causal,
-                     static_cast<T*>(a.o), a.lse, a.B, a.H, a.N, a.Nk, n_qtiles);
+                     static_cast<T*>(a.o), a.lse, a.B, a.H, a.N, a.Nk, n_qtiles,
+                     a.cu_q, a.cu_k, a.total_q, a.total_k);
   return hipGetLastError();
 }
 
@@ -714,7 +721,8 @@ hipError_t launch_f32_d(const FwdArgs& a) {
   hipLaunchKernelGGL((fa_fwd_f32_kernel<D, kF32NW, kF32BC>), grid, dim3(C::NT), 0, a.stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), a.seqlens_k, a.scale * kLog2e, a.causal,
-                     static_cast<float*>(a.o), a.lse, a.B, a.H, a.N, a.Nk, n_qtiles);
+                     static_cast<float*>(a.o), a.lse, a.B, a.H, a.N, a.Nk, n_qtiles,
+                     a.cu_q, a.cu_k, a.total_q, a.total_k);
   return hipGetLastError();
 }
 

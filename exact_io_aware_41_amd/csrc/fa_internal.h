@@ -24,6 +24,12 @@ struct FwdArgs {
   void* o;
   float* lse;
   hipStream_t stream;
+  // packed batches (cu_q != nullptr): sequence b holds query rows
+  // cu_q[b] .. cu_q[b+1] and key rows cu_k[b] .. cu_k[b+1] of the head-major
+  // [H][total][d] tensors; N and Nk are then the longest sequence's lengths
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
 };
 
 struct BwdArgs {
@@ -41,8 +47,11 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // [B][H][N] fp32 row dot products, from the workspace
+  float* delta;  // [B][H][N] (packed: [H][total_q]) fp32 row dot products
   hipStream_t stream;
+  const int32_t* cu_q;   // packed batches, as in FwdArgs
+  const int32_t* cu_k;
+  int total_q, total_k;
 };
 
 struct DecodeArgs {

@@ -38,6 +38,7 @@ __all__ = [
     "Config", "CONFIGS", "TENSOR_IDS",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "f32_to_f16_bits", "HALF_DTYPES", "widen",
     "make_lengths", "make_head", "make_tensor", "make_inputs",
+    "packed_lengths", "offsets", "make_packed",
     "credited_flops", "useful_pairs", "useful_flops", "min_bytes",
 ]
 
@@ -192,6 +193,41 @@ def make_inputs(cfg: Config, seed: int = 0, with_grad: bool | None = None, **sha
     res["lengths"] = make_lengths(cfg, seed)
     res["scale"] = cfg.scale
     return res
+
+
+def packed_lengths(B: int, max_len: int, seed: int = 0, empty_first: bool = True):
+    """Sequence lengths of a packed batch (int32 [B]): uniform in
+    [1, max_len], the first one 0 when ``empty_first`` (an empty sequence),
+    and one of them max_len so the longest sequence is present."""
+    rng = np.random.default_rng([seed, TENSOR_IDS["lengths"], 1])
+    lens = rng.integers(1, max_len, endpoint=True, size=B)
+    if B > 1:
+        lens[rng.integers(1 if empty_first else 0, B)] = max_len
+    if empty_first and B > 0:
+        lens[0] = 0
+    return lens.astype(np.int32)
+
+
+def offsets(lengths):
+    """Cumulative offsets (int32 [B + 1]) of packed sequences."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, np.int64))]).astype(np.int32)
+
+
+def make_packed(cfg: Config, name: str, lengths, seed: int = 0, H: int | None = None,
+                d: int | None = None):
+    """Packed head-major [H, sum(lengths), d] tensor in device format:
+    sequence b's rows of head h are make_head(cfg, name, b, h) with
+    lengths[b] rows, placed back to back."""
+    H = cfg.H if H is None else H
+    d = cfg.d if d is None else d
+    lengths = [int(n) for n in lengths]
+    out = np.empty((H, sum(lengths), d), np.uint16 if cfg.dtype in HALF_DTYPES else np.float32)
+    start = 0
+    for b, n in enumerate(lengths):
+        for h in range(H):
+            out[h, start:start + n] = make_head(cfg, name, b, h, seed, n, d)
+        start += n
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -25,7 +25,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Tensors are dense, contiguous, row-major [B][H][N][d] (batch, head,
- *    position, feature).  Q, K and V share N (self-attention).
+ *    position, feature); K and V may have another row count Nk than Q
+ *    (fa_forward), and the *_varlen calls take packed, head-major
+ *    [H][total][d] batches instead.
  *  - lse is fp32 [B][H][N]: the natural-log log-sum-exp of the visible scaled
  *    scores of each query row, LSE_i = m_i + ln(l_i).
  *  - Scores are s_ij = scale * q_i . k_j.  A pair (i, j) of sequence b is
@@ -51,14 +53,16 @@
  *                          0/1, workspace missing or too small, or a problem
  *                          too large for the launch grid.
  *  FA_ERROR_UNSUPPORTED    (dtype, d) pair outside the compiled set (see
- *                          below); there is no fallback path.
+ *                          below), or one head of one sequence (N rows of d
+ *                          elements) of 2^31 bytes or more; there is no
+ *                          fallback path.
  *  FA_ERROR_LAUNCH         the HIP runtime reported an error when the kernel
  *                          was enqueued (hipGetLastError).  Faults inside a
  *                          kernel surface at the caller's next synchronise.
  *
  * Compiled (dtype, d) set:
  *  forward : FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128, 256}
- *  backward: FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128}
+ *  backward: FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128, 256}
  *            (fp32 on the fp32 MFMA: fp32 inputs, arithmetic and outputs)
  *  decode and merge: FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in
  *  {64, 128, 256}
@@ -193,6 +197,60 @@ fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int Nq, int Nk, int d,
                          const void* dout, const float* lse, const float* delta,
                          const int32_t* seqlens_k, float scale, int causal,
                          void* dq, hipStream_t stream);
+
+/*
+ * Packed batches: B sequences of different lengths stored back to back
+ * without padding.  The tensors are head-major, and sequence b owns query
+ * rows cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 and key rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1 of every head.  The pages define
+ * attention for one sequence; each packed sequence is computed as its own
+ * problem of that definition, exactly as fa_forward / fa_backward compute
+ * one (batch, head): the causal mask uses the sequence's own lengths
+ * (a query sees keys j <= i + nk_b - nq_b, positions counted from the
+ * sequence's first row), and nothing crosses from one sequence to another.
+ *
+ *   B                  number of sequences
+ *   total_q, total_k   query / key rows per head of the packed tensors
+ *   max_seqlen_q, max_seqlen_k
+ *                      the longest sequence's query / key rows: the launch
+ *                      covers that many rows per sequence, and a longer
+ *                      sequence is cut to it
+ *   q, o               [H][total_q][d]; k, v [H][total_k][d]
+ *   lse                [H][total_q] fp32
+ *   cu_seqlens_q, cu_seqlens_k
+ *                      [B + 1] int32 offsets on the device, non-decreasing,
+ *                      from >= 0 to <= total_q (total_k), 4-byte aligned.
+ *                      The kernels clamp every offset and length to the
+ *                      buffers, so a malformed array gives meaningless
+ *                      values but never an access outside q, k, v, o or lse
+ *                      (overlapping sequences write the same rows in an
+ *                      unspecified order).
+ *   dtype, d, scale, causal, stream   as for fa_forward
+ * Rows that belong to no sequence are neither read nor written.  A sequence
+ * without keys gets o = 0 and lse = -inf on its rows.
+ */
+fa_status fa_forward_varlen(fa_dtype dtype, int B, int H, int total_q, int total_k,
+                            int max_seqlen_q, int max_seqlen_k, int d,
+                            const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            float scale, int causal, void* o, float* lse,
+                            hipStream_t stream);
+
+/*
+ * Backward of fa_forward_varlen; the arguments are those of fa_forward_varlen
+ * and of fa_backward: dq, o, dout [H][total_q][d], dk, dv [H][total_k][d].
+ * The workspace needs fa_backward_workspace_size(dtype, 1, H, total_q, d)
+ * bytes.  Key rows of a sequence that no query sees get zero gradients; rows
+ * that belong to no sequence are not written.
+ */
+fa_status fa_backward_varlen(fa_dtype dtype, int B, int H, int total_q, int total_k,
+                             int max_seqlen_q, int max_seqlen_k, int d,
+                             const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             float scale, int causal, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /*
  * Decoding: one new query row per (batch, head) against a key/value cache,

@@ -41,7 +41,7 @@ def test_header_declarations_are_exported():
 
 
 def test_version_and_status_strings():
-    assert fa.fa_abi_version() == 2
+    assert fa.fa_abi_version() == 3
     assert fa.fa_status_string(fa.FA_SUCCESS) == "FA_SUCCESS"
     assert fa.fa_status_string(fa.FA_ERROR_INVALID_VALUE) == "FA_ERROR_INVALID_VALUE"
     assert fa.fa_status_string(fa.FA_ERROR_UNSUPPORTED) == "FA_ERROR_UNSUPPORTED"
@@ -130,6 +130,69 @@ def test_backward_unsupported_and_workspace_size():
     assert fa.fa_backward_workspace_size(BF16, 0, 32, 8192, 128) == 0
     assert fa.fa_backward_workspace_size(BF16, -1, 32, 8192, 128) == 0
     assert bwd(B=0, q=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
+
+
+def fwd_varlen(dtype=BF16, B=2, H=1, tq=40, tk=40, mq=20, mk=20, d=128, q=A, k=A, v=A, cq=A,
+               ck=A, scale=0.1, causal=0, o=A, lse=A):
+    return fa.fa_forward_varlen(dtype, B, H, tq, tk, mq, mk, d, q, k, v, cq, ck, scale, causal, o,
+                                lse, None)
+
+
+def bwd_varlen(dtype=BF16, B=2, H=1, tq=40, tk=40, mq=20, mk=20, d=128, scale=0.1, causal=0,
+               ws=A, ws_bytes=1 << 20, **ptrs):
+    p = dict(q=A, k=A, v=A, o=A, do=A, lse=A, cq=A, ck=A, dq=A, dk=A, dv=A)
+    p.update(ptrs)
+    return fa.fa_backward_varlen(dtype, B, H, tq, tk, mq, mk, d, p["q"], p["k"], p["v"], p["o"],
+                                 p["do"], p["lse"], p["cq"], p["ck"], scale, causal, p["dq"],
+                                 p["dk"], p["dv"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=5), dict(B=-1), dict(H=-1), dict(tq=-1), dict(tk=-1), dict(mq=-1), dict(mk=-1),
+    dict(d=0), dict(scale=0.0), dict(scale=math.inf), dict(causal=2),
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None), dict(cq=None),
+    dict(ck=None), dict(q=MIS), dict(o=MIS), dict(lse=MIS), dict(cq=A + 2), dict(ck=A + 1),
+])
+def test_forward_varlen_rejects_invalid_arguments(kw):
+    assert fwd_varlen(**kw) == fa.FA_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=5), dict(B=-1), dict(tk=-1), dict(mq=-1), dict(scale=math.nan), dict(causal=-1),
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(do=None), dict(lse=None),
+    dict(cq=None), dict(ck=None), dict(dq=None), dict(dk=None), dict(dv=None), dict(ws=None),
+    dict(dk=MIS), dict(ws=MIS), dict(cq=A + 2), dict(ws_bytes=40 * 4 - 1),
+])
+def test_backward_varlen_rejects_invalid_arguments(kw):
+    assert bwd_varlen(**kw) == fa.FA_ERROR_INVALID_VALUE
+
+
+def test_varlen_empty_unsupported_and_limits():
+    none = dict(q=None, k=None, v=None, o=None, lse=None, cq=None, ck=None)
+    for B, H in ((0, 4), (3, 0)):
+        assert fwd_varlen(B=B, H=H, **none) == fa.FA_SUCCESS
+    # no query rows: nothing to write, but the offsets are still required
+    assert fwd_varlen(tq=0, q=None, o=None, lse=None) == fa.FA_SUCCESS
+    assert fwd_varlen(mq=0, q=None, o=None, lse=None) == fa.FA_SUCCESS
+    assert fwd_varlen(tq=0, cq=None) == fa.FA_ERROR_INVALID_VALUE
+    # queries without keys still write empty rows, so o and lse are required
+    assert fwd_varlen(tk=0, k=None, v=None, lse=None) == fa.FA_ERROR_INVALID_VALUE
+    assert fwd_varlen(d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert fwd_varlen(dtype=F32, d=512) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd_varlen(d=192) == fa.FA_ERROR_UNSUPPORTED
+    # one sequence's head must stay under 2^31 bytes
+    assert fwd_varlen(mq=1 << 23, tq=1 << 23) == fa.FA_ERROR_UNSUPPORTED
+    assert fwd(N=1 << 23) == fa.FA_ERROR_UNSUPPORTED
+    assert fwd(dtype=F32, N=1 << 22) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(N=16, Nk=1 << 23) == fa.FA_ERROR_UNSUPPORTED
+    # backward: a side without rows needs no buffers
+    assert bwd_varlen(tq=0, tk=0, q=None, k=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
+    # keys without queries still write zero dK, dV rows: those are required
+    assert bwd_varlen(tq=0, q=None, o=None, do=None, lse=None, dq=None, ws=None, ws_bytes=0,
+                      dk=None) == fa.FA_ERROR_INVALID_VALUE
+    assert bwd_varlen(tk=0, k=None, v=None, dk=None, dv=None, dq=None) == \
+        fa.FA_ERROR_INVALID_VALUE
+    assert fwd_varlen(B=1 << 20, H=1 << 10, mq=1 << 16) == fa.FA_ERROR_INVALID_VALUE
 
 
 def test_torch_wrappers_validate_before_calling():

@@ -184,3 +184,17 @@ def test_useful_pairs_rectangular_brute_force():
                 lens = None if L is None else np.array([L])
                 vis = oracle.visible_mask(np.arange(N), Nk, causal, L, offset=Nk - N)
                 assert fi.useful_pairs(N, causal, lens, Nk=Nk) == int(vis.sum())
+
+
+def test_packed_generators():
+    lens = fi.packed_lengths(7, 300, seed=4)
+    assert lens.dtype == np.int32 and lens[0] == 0 and lens.max() == 300
+    assert np.all(lens[1:] >= 1) and np.all(lens <= 300)
+    assert np.array_equal(fi.packed_lengths(7, 300, seed=4), lens)
+    cu = fi.offsets(lens)
+    assert cu.dtype == np.int32 and cu[0] == 0 and np.all(np.diff(cu) == lens)
+    cfg = fi.CONFIGS[5]
+    t = fi.make_packed(cfg, "k", [3, 0, 5], seed=2, H=2, d=64)
+    assert t.shape == (2, 8, 64) and t.dtype == np.uint16
+    assert np.array_equal(t[1, 3:8], fi.make_head(cfg, "k", 2, 1, 2, 5, 64))
+    assert np.array_equal(t[0, 0:3], fi.make_head(cfg, "k", 0, 0, 2, 3, 64))
