@@ -84,6 +84,10 @@ def parse_args():
     p.add_argument("--kv-len", type=int, default=None, metavar="NK",
                    help="give keys and values NK rows instead of the queries' N (causal: query "
                         "i sees keys j <= i + NK - N)")
+    p.add_argument("--packed", type=int, default=None, metavar="NSEQ",
+                   help="pack NSEQ sequences of the --config workload's H, d and format, of "
+                        "lengths uniform in [1, N] (one of exactly N), back to back without "
+                        "padding, and time the packed entry points")
     p.add_argument("--decode-lengths", default=None, choices=[None, "zero_then_uniform"],
                    help="cached lengths of the decode workload (default: all full)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -190,6 +194,9 @@ def main():
         cfg = dataclasses.replace(cfg, **variant)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.packed is not None:
+        packed_main(args, cfg, dev)
+        return
 
     t0 = time.perf_counter()
     inputs = fi.make_inputs(cfg)
@@ -318,6 +325,143 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def packed_main(args, cfg, dev):
+    """Packed batch of variable-length sequences: fa_forward_varlen (and
+    fa_backward_varlen when the workload trains) over [H, total, d] tensors.
+    Credited FLOPs count visible pairs only (4d forward, 10d backward), so
+    the figure is comparable with the padded workload's."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_41_amd as fa
+    import fa_inputs as fi
+    import oracle
+
+    if args.packed < 1:
+        log("--packed needs at least one sequence")
+        sys.exit(2)
+    lens = fi.packed_lengths(args.packed, cfg.N, seed=0, empty_first=False)
+    cu = fi.offsets(lens)
+    total = int(cu[-1])
+    t0 = time.perf_counter()
+    names = ["q", "k", "v"] + (["do"] if cfg.backward else [])
+    host = {n: fi.make_packed(cfg, n, lens, 0) for n in names}
+    log(f"packed inputs generated in {time.perf_counter() - t0:.1f} s: {len(lens)} sequences, "
+        f"{total} rows per head, longest {int(lens.max())}")
+
+    def up(a):
+        if cfg.dtype in fi.HALF_DTYPES:
+            half = torch.bfloat16 if cfg.dtype == "bf16" else torch.float16
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(half)
+        return torch.from_numpy(a).to(dev)
+
+    t = {n: up(host[n]) for n in names}
+    cu_d = torch.from_numpy(cu).to(dev)
+    mx = int(lens.max())
+    o = torch.empty_like(t["q"])
+    lse = torch.empty(cfg.H, total, dtype=torch.float32, device=dev)
+    if cfg.backward:
+        dq, dk, dv = (torch.empty_like(t["q"]) for _ in range(3))
+        ws = torch.empty(max(fa.fa_backward_workspace_size(fa.FA_DTYPE_BF16, 1, cfg.H, total,
+                                                           cfg.d), 16),
+                         dtype=torch.uint8, device=dev)
+    n_ev = 3 if cfg.backward else 2
+
+    def step(ev):
+        ev[0].record()
+        fa.forward_varlen(t["q"], t["k"], t["v"], cu_d, cu_d, mx, mx, scale=cfg.scale,
+                          causal=cfg.causal, out=o, lse=lse)
+        ev[1].record()
+        if cfg.backward:
+            fa.backward_varlen(t["q"], t["k"], t["v"], o, t["do"], lse, cu_d, cu_d, mx, mx,
+                               scale=cfg.scale, causal=cfg.causal, dq=dq, dk=dk, dv=dv,
+                               workspace=ws)
+            ev[2].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    events = [mk() for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(events[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    groups = ["fwd", "bwd"][:n_ev - 1]
+    per = {g: sum(e[i].elapsed_time(e[i + 1]) for e in events) / args.steps
+           for i, g in enumerate(groups)}
+
+    fwd_f = sum(fi.useful_flops(1, cfg.H, int(n), cfg.d, cfg.causal) for n in lens)
+    group_flops = {"fwd": fwd_f}
+    if cfg.backward:
+        group_flops["bwd"] = sum(fi.useful_flops(1, cfg.H, int(n), cfg.d, cfg.causal,
+                                                 backward=True) for n in lens)
+    flops = sum(group_flops.values())
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype in fi.HALF_DTYPES else PEAK_F32_TFLOPS
+    dominant = max(per, key=per.get)
+    achieved = group_flops[dominant] / (per[dominant] * 1e-3) / 1e12
+    label = {"fwd": "fa_fwd (one launch)", "bwd": "backward (row dots + dK/dV + dQ launches)"}
+    roofline = {"bound": "mfma", "kernel": label[dominant], "achieved": round(achieved, 1),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": None}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("timing the fp64 CPU oracle on a sample ...")
+        elapsed, done_f, done = 0.0, 0, 0
+        for b, n in enumerate(lens):
+            for h in range(cfg.H):
+                sl = slice(int(cu[b]), int(cu[b + 1]))
+                w = {x: fi.widen(host[x][h:h + 1, sl][None], cfg.dtype) for x in names}
+                c0 = time.perf_counter()
+                ro, rl = oracle.attention_materialised(w["q"], w["k"], w["v"], cfg.scale,
+                                                       cfg.causal)
+                if cfg.backward:
+                    oracle.attention_backward(w["q"], w["k"], w["v"], ro, w["do"], rl, cfg.scale,
+                                              cfg.causal)
+                elapsed += time.perf_counter() - c0
+                done_f += fi.useful_flops(1, 1, int(n), cfg.d, cfg.causal)
+                if cfg.backward:
+                    done_f += fi.useful_flops(1, 1, int(n), cfg.d, cfg.causal, backward=True)
+                done += 1
+                if elapsed >= args.cpu_seconds:
+                    break
+            if elapsed >= args.cpu_seconds:
+                break
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                           if i.get("user_api") == "blas"), default=1)
+        except Exception:  # noqa: BLE001 - report what we can
+            threads = 1
+        cpu = {"value": done_f / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+               "kind": "oracle",
+               "sample": f"{done} (sequence, head) pairs of {len(lens) * cfg.H}, "
+                         f"{elapsed:.1f} s", "seconds": round(elapsed, 2)}
+
+    what = "causal " if cfg.causal else ""
+    what += "training step (forward + backward)" if cfg.backward else "forward"
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded iid N(0,1) inputs)",
+        "config": {"workload": f"packed variable-length {what}", "sequences": len(lens),
+                   "total_rows": total, "max_len": mx, "H": cfg.H, "d": cfg.d,
+                   "causal": cfg.causal, "lengths": [int(x) for x in lens],
+                   "credited_flops_per_step": flops},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "per_launch_ms": {g: round(x, 4) for g, x in per.items()},
+        "group_tflops": {g: round(group_flops[g] / (per[g] * 1e-3) / 1e12, 1) for g in per},
+        "pct_of_peak": round(100.0 * value / peak, 2),
     }
     print(json.dumps(line), flush=True)
 

@@ -264,6 +264,17 @@ struct TileCoord {
   int b, h, qt;
 };
 
+__device__ __forceinline__ TileCoord tile_coord(int wg, int B, int H, int n_qtiles) {
+  const int bh_count = B * H;
+  const int qt_rev = wg / bh_count;
+  const int bh = wg - qt_rev * bh_count;
+  TileCoord t;
+  t.qt = n_qtiles - 1 - qt_rev;
+  t.b = bh / H;
+  t.h = bh - t.b * H;
+  return t;
+}
+
 // Where the rows of one (sequence b, head h) live.  Padded layout
 // (cu_q == nullptr): [B][H][N][d] queries and [B][H][Nk][d] keys, every
 // sequence N query rows and Nk key rows.  Packed layout: sequence b owns
@@ -295,16 +306,6 @@ __device__ __forceinline__ SeqSpan seq_span(int b, int h, int H, int N, int Nk,
   s.q_row0 = (size_t)h * total_q + q_lo;
   s.k_row0 = (size_t)h * total_k + k_lo;
   return s;
-}
-__device__ __forceinline__ TileCoord tile_coord(int wg, int B, int H, int n_qtiles) {
-  const int bh_count = B * H;
-  const int qt_rev = wg / bh_count;
-  const int bh = wg - qt_rev * bh_count;
-  TileCoord t;
-  t.qt = n_qtiles - 1 - qt_rev;
-  t.b = bh / H;
-  t.h = bh - t.b * H;
-  return t;
 }
 
 }  // namespace fa
