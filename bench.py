@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd/bwd TFLOP/s at N=8192,d=128 bf16; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3          # MI355X fp32 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0         # MI355X dense fp8 MFMA, published
 KV_LEN = None                    # key rows when they differ from the query rows
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -77,8 +78,10 @@ def parse_args():
     p.add_argument("--workload", default="attention", choices=["attention", "decode"],
                    help="attention: the --config workload (default, the headline metric); "
                         "decode: one query row per head against an 8192-position cache")
-    p.add_argument("--dtype", default=None, choices=["bf16", "f16", "f32"],
-                   help="run the --config workload in another element format (default: its own)")
+    p.add_argument("--dtype", default=None, choices=["bf16", "f16", "f32", "e4m3"],
+                   help="run the --config workload in another element format (default: its "
+                        "own); e4m3: FP8 inputs with per-tensor descale factors and a bf16 "
+                        "output, forward workloads only")
     p.add_argument("--head-dim", type=int, default=None, choices=[64, 128, 256],
                    help="run the --config workload with another head dimension")
     p.add_argument("--kv-len", type=int, default=None, metavar="NK",
@@ -119,6 +122,7 @@ def cpu_baseline(cfg, inputs, budget_s):
     done = 0
     for (b, h) in heads:
         w = {n: fi.widen(inputs[n][b:b + 1, h:h + 1], cfg.dtype)
+                * (fi.FP8_DESCALE[n] if cfg.dtype == "e4m3" else 1.0)
              for n in ("q", "k", "v", "do") if n in inputs}
         lb = None if lengths is None else np.asarray(lengths)[b:b + 1]
         t0 = time.perf_counter()
@@ -192,6 +196,9 @@ def main():
     if variant:
         import dataclasses
         cfg = dataclasses.replace(cfg, **variant)
+    if cfg.dtype == "e4m3" and cfg.backward:
+        log("the FP8 path is a forward: use --config 1-4 with --dtype e4m3")
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.packed is not None:
@@ -217,7 +224,8 @@ def main():
     q, k, v = up(inputs["q"]), up(inputs["k"]), up(inputs["v"])
     do = up(inputs["do"]) if cfg.backward else None
     lens = None if inputs["lengths"] is None else torch.from_numpy(inputs["lengths"]).to(dev)
-    o = torch.empty_like(q)
+    fp8 = cfg.dtype == "e4m3"
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev) if fp8 else torch.empty_like(q)
     lse = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev)
     if cfg.backward:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
@@ -227,7 +235,12 @@ def main():
 
     def step(ev):
         ev[0].record()
-        fa.forward(q, k, v, scale=cfg.scale, causal=cfg.causal, seqlens_k=lens, out=o, lse=lse)
+        if fp8:
+            fa.forward_fp8(q, k, v, fi.FP8_DESCALE["q"], fi.FP8_DESCALE["k"], fi.FP8_DESCALE["v"],
+                           scale=cfg.scale, causal=cfg.causal, seqlens_k=lens, out=o, lse=lse)
+        else:
+            fa.forward(q, k, v, scale=cfg.scale, causal=cfg.causal, seqlens_k=lens, out=o,
+                       lse=lse)
         ev[1].record()
         if cfg.backward:
             fa.backward_phases(q, k, v, o, do, lse, scale=cfg.scale, causal=cfg.causal,
@@ -261,8 +274,8 @@ def main():
     lengths = inputs["lengths"]
     flops = step_flops(cfg, lengths, Nk=KV_LEN)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    # bf16 and f16 share the dense MFMA peak; fp32 runs on the fp32 MFMA
-    peak = PEAK_BF16_TFLOPS if cfg.dtype in fi.HALF_DTYPES else PEAK_F32_TFLOPS
+    # bf16 and f16 share the dense MFMA peak; fp32 and fp8 run on their own MFMAs
+    peak = {"e4m3": PEAK_FP8_TFLOPS, "f32": PEAK_F32_TFLOPS}.get(cfg.dtype, PEAK_BF16_TFLOPS)
 
     # credited FLOPs per launch of each compute kernel
     if KV_LEN is not None:
@@ -341,8 +354,8 @@ def packed_main(args, cfg, dev):
     import fa_inputs as fi
     import oracle
 
-    if args.packed < 1:
-        log("--packed needs at least one sequence")
+    if args.packed < 1 or cfg.dtype == "e4m3":
+        log("--packed needs at least one sequence and a bf16, f16 or f32 workload")
         sys.exit(2)
     lens = fi.packed_lengths(args.packed, cfg.N, seed=0, empty_first=False)
     cu = fi.offsets(lens)

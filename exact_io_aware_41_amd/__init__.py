@@ -26,9 +26,9 @@ __all__ = [
     "FAError", "FALibraryMissing", "LIB_PATH", "load_library",
     "fa_abi_version", "fa_status_string", "fa_forward", "fa_backward",
     "fa_backward_workspace_size", "fa_backward_preprocess", "fa_backward_dkdv",
-    "fa_backward_dq", "fa_forward_varlen", "fa_backward_varlen", "fa_decode_workspace_size",
+    "fa_backward_dq", "fa_forward_fp8", "fa_forward_varlen", "fa_backward_varlen", "fa_decode_workspace_size",
     "fa_decode", "fa_merge_states", "forward", "backward", "backward_phases", "forward_varlen",
-    "backward_varlen", "decode", "merge_states",
+    "backward_varlen", "forward_fp8", "decode", "merge_states",
 ]
 
 FA_SUCCESS = 0
@@ -41,7 +41,7 @@ FA_DTYPE_F16 = 2
 
 EXPORTED_SYMBOLS = ("fa_abi_version", "fa_status_string", "fa_forward",
                     "fa_backward_workspace_size", "fa_backward", "fa_backward_preprocess",
-                    "fa_backward_dkdv", "fa_backward_dq", "fa_forward_varlen",
+                    "fa_backward_dkdv", "fa_backward_dq", "fa_forward_fp8", "fa_forward_varlen",
                     "fa_backward_varlen", "fa_decode_workspace_size", "fa_decode",
                     "fa_merge_states")
 
@@ -92,6 +92,9 @@ def load_library():
     lib.fa_backward_dq.restype = i32
     lib.fa_backward_dq.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32,
                                    i32, vp, vp]
+    lib.fa_forward_fp8.restype = i32
+    lib.fa_forward_fp8.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, f32, f32, f32, f32,
+                                   i32, vp, vp, vp]
     lib.fa_forward_varlen.restype = i32
     lib.fa_forward_varlen.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                       f32, i32, vp, vp, vp]
@@ -151,6 +154,12 @@ def fa_backward_dq(dtype, B, H, Nq, Nk, d, q, k, v, dout, lse, delta, seqlens_k,
                    dq, stream=0) -> int:
     return load_library().fa_backward_dq(dtype, B, H, Nq, Nk, d, q, k, v, dout, lse, delta,
                                          seqlens_k, scale, causal, dq, stream)
+
+
+def fa_forward_fp8(B, H, Nq, Nk, d, q, k, v, seqlens_k, scale, q_descale, k_descale, v_descale,
+                   causal, o, lse, stream=0) -> int:
+    return load_library().fa_forward_fp8(B, H, Nq, Nk, d, q, k, v, seqlens_k, scale, q_descale,
+                                         k_descale, v_descale, causal, o, lse, stream)
 
 
 def fa_forward_varlen(dtype, B, H, total_q, total_k, max_seqlen_q, max_seqlen_k, d, q, k, v,
@@ -303,6 +312,40 @@ def backward(q, k, v, o, do, lse, scale=None, causal=False, seqlens_k=None,
     if st != FA_SUCCESS:
         raise FAError(st, "fa_backward")
     return dq, dk, dv
+
+
+def forward_fp8(q, k, v, q_descale, k_descale, v_descale, scale=None, causal=False,
+                seqlens_k=None, out=None, lse=None):
+    """Attention of FP8 inputs: q [B, H, Nq, d], k, v [B, H, Nk, d] hold OCP
+    E4M3 codes (torch.float8_e4m3fn, or uint8 bytes), the real values being
+    code * descale.  Returns (o bf16 like q, lse fp32 [B, H, Nq])."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[:2] != q.shape[:2] \
+            or k.shape[3] != q.shape[3]:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8) or t.device != q.device \
+                or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous E4M3 codes on q's device")
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    seqlens_k = _lengths(seqlens_k, q)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    st = fa_forward_fp8(B, H, N, Nk, d, _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens_k), float(scale),
+                        float(q_descale), float(k_descale), float(v_descale), int(bool(causal)),
+                        _ptr(out), _ptr(lse), _stream(q.device))
+    if st != FA_SUCCESS:
+        raise FAError(st, "fa_forward_fp8")
+    return out, lse
 
 
 def _check_packed(q, k, v, cu_seqlens_q, cu_seqlens_k):

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr long long kMaxGrid = 0x7fffffffLL;
 // one head's rows of one sequence must be addressable with 32-bit byte
 // offsets (the kernels' buffer descriptors)
@@ -120,6 +120,32 @@ fa_status fa_forward(fa_dtype dtype, int B, int H, int Nq, int Nk, int d, const 
   const hipError_t e =
       is_half(dtype) ? fa::launch_fwd_half(a, elt_of(dtype)) : fa::launch_fwd_f32(a);
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH;
+}
+
+fa_status fa_forward_fp8(int B, int H, int Nq, int Nk, int d, const void* q, const void* k,
+                         const void* v, const int32_t* seqlens_k, float scale, float q_descale,
+                         float k_descale, float v_descale, int causal, void* o, float* lse,
+                         hipStream_t stream) {
+  bool empty = false;
+  // the format checks of the bf16 output; scale and flags as for fa_forward
+  fa_status st = check_common(FA_DTYPE_BF16, B, H, Nq, d, scale, causal, &empty);
+  if (st != FA_SUCCESS) return st;
+  if (Nk < 0) return FA_ERROR_INVALID_VALUE;
+  for (float x : {q_descale, k_descale, v_descale})
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERROR_INVALID_VALUE;
+  if (!std::isfinite(scale * q_descale * k_descale)) return FA_ERROR_INVALID_VALUE;
+  if (d != 128) return FA_ERROR_UNSUPPORTED;
+  if ((long long)Nq * d * 2 > kMaxHeadBytes || (long long)Nk * d > kMaxHeadBytes)
+    return FA_ERROR_UNSUPPORTED;
+  if (empty) return FA_SUCCESS;
+  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERROR_INVALID_VALUE;
+  if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERROR_INVALID_VALUE;
+  if (fa::fwd_fp8_grid(B, H, Nq, d) > kMaxGrid) return FA_ERROR_INVALID_VALUE;
+  fa::FwdArgs a{B, H, Nq, d, Nk, q, k, v, seqlens_k, scale, causal, o, lse, stream};
+  return fa::launch_fwd_fp8(a, q_descale, k_descale, v_descale) == hipSuccess ? FA_SUCCESS
+                                                                              : FA_ERROR_LAUNCH;
 }
 
 size_t fa_backward_workspace_size(fa_dtype dtype, int B, int H, int N, int d) {

@@ -81,6 +81,8 @@ constexpr int kMaxMergeParts = 4096;
 // The 16-bit launchers take Elt::kBf16 or Elt::kF16.
 hipError_t launch_fwd_half(const FwdArgs& a, Elt e);
 hipError_t launch_fwd_f32(const FwdArgs& a);
+// FP8 (E4M3) q, k, v with per-tensor descale factors, bf16 o; d = 128
+hipError_t launch_fwd_fp8(const FwdArgs& a, float q_descale, float k_descale, float v_descale);
 hipError_t launch_bwd_half(const BwdArgs& a, Elt e);
 hipError_t launch_bwd_preprocess_half(const BwdArgs& a, Elt e);
 hipError_t launch_bwd_dkdv_half(const BwdArgs& a, Elt e);
@@ -98,6 +100,7 @@ hipError_t launch_merge(int rows, int n_parts, int d, const float* o_parts,
 // rejects problems whose grid would not fit in a signed 32-bit count.
 long long fwd_half_grid(int B, int H, int N, int d);
 long long fwd_f32_grid(int B, int H, int N, int d);
+long long fwd_fp8_grid(int B, int H, int N, int d);
 long long bwd_half_grid(int B, int H, int N, int d);
 long long bwd_f32_grid(int B, int H, int N, int d);
 

@@ -39,6 +39,7 @@ __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "f32_to_f16_bits", "HALF_DTYPES", "widen",
     "make_lengths", "make_head", "make_tensor", "make_inputs",
     "packed_lengths", "offsets", "make_packed",
+    "E4M3_MAX", "e4m3_bits_to_f64", "f64_to_e4m3_bits", "FP8_DESCALE", "storage_dtype",
     "credited_flops", "useful_pairs", "useful_flops", "min_bytes",
 ]
 
@@ -109,14 +110,66 @@ def bf16_bits_to_f32(bits):
 
 HALF_DTYPES = ("bf16", "f16")
 
+# FP8 workloads store E4M3 codes of x / descale, x the same N(0,1) draws as
+# the other formats; the powers of two keep |x| / descale (|x| <= ~5.5) under
+# 448 and make dequantisation exact.  O (the dequantised V times softmax) and
+# dO stay bf16.
+FP8_DESCALE = {"q": 2.0 ** -4, "k": 2.0 ** -5, "v": 2.0 ** -6}
+
+
+def storage_dtype(dtype):
+    """NumPy storage of a device format: bf16 / f16 bits, E4M3 codes, fp32."""
+    return {"bf16": np.uint16, "f16": np.uint16, "e4m3": np.uint8}.get(dtype, np.float32)
+
 
 def f32_to_f16_bits(x):
     """Round float32 values to IEEE binary16 (nearest, ties to even); uint16 bits."""
     return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
+E4M3_MAX = 448.0
+
+
+def e4m3_bits_to_f64(bits):
+    """Exact values of OCP FP8 E4M3 codes (uint8): sign, 4 exponent bits with
+    bias 7, 3 mantissa bits; exponent field 0 is subnormal (m * 2^-9); no
+    infinities; S.1111.111 is NaN, so the largest finite value is 448."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m, -9), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((b & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def f64_to_e4m3_bits(x):
+    """Round values to OCP FP8 E4M3 (nearest, ties to even) and return the
+    uint8 codes.  Values whose rounding exceeds 448 in magnitude, and NaN,
+    raise ValueError: the generators never produce them."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.isnan(x)):
+        raise ValueError("NaN has no E4M3 encoding here")
+    a = np.abs(x)
+    # quantum of the binade: 2^(e - 3) for normals (e >= -6), 2^-9 below
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    q = np.ldexp(1.0, (np.maximum(e, -6) - 3).astype(np.int64))
+    r = np.round(a / q) * q                      # numpy rounds halves to even
+    if np.any(r > E4M3_MAX):
+        raise ValueError("value outside the E4M3 range")
+    e_r = np.floor(np.log2(np.where(r > 0, r, 1.0)))
+    normal = r >= 2.0 ** -6
+    exp_field = np.where(normal, e_r + 7, 0).astype(np.int64)
+    mant = np.where(normal, r / np.ldexp(1.0, e_r.astype(np.int64)) * 8 - 8, r / 2.0 ** -9)
+    code = (exp_field << 3) | np.rint(mant).astype(np.int64)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
 def widen(arr, dtype):
-    """Exact float64 values of a device-format array (fp32, or bf16 / f16 bits)."""
+    """Exact float64 values of a device-format array (fp32, or bf16 / f16 /
+    E4M3 codes)."""
+    if dtype == "e4m3":
+        return e4m3_bits_to_f64(arr)
     if dtype == "bf16":
         return bf16_bits_to_f32(arr).astype(np.float64)
     if dtype == "f16":
@@ -152,6 +205,8 @@ def make_head(cfg: Config, name: str, b: int, h: int, seed: int = 0, N: int | No
         return f32_to_bf16_bits(x)
     if cfg.dtype == "f16":
         return f32_to_f16_bits(x)
+    if cfg.dtype == "e4m3":
+        return f64_to_e4m3_bits(x.astype(np.float64) / FP8_DESCALE[name])
     return x
 
 
@@ -167,7 +222,7 @@ def make_tensor(cfg: Config, name: str, seed: int = 0, threads: int | None = Non
     H = cfg.H if H is None else H
     N = cfg.N if N is None else N
     d = cfg.d if d is None else d
-    out = np.empty((B, H, N, d), np.uint16 if cfg.dtype in HALF_DTYPES else np.float32)
+    out = np.empty((B, H, N, d), storage_dtype(cfg.dtype))
 
     def fill(bh):
         b, h = divmod(bh, H)
@@ -221,7 +276,7 @@ def make_packed(cfg: Config, name: str, lengths, seed: int = 0, H: int | None = 
     H = cfg.H if H is None else H
     d = cfg.d if d is None else d
     lengths = [int(n) for n in lengths]
-    out = np.empty((H, sum(lengths), d), np.uint16 if cfg.dtype in HALF_DTYPES else np.float32)
+    out = np.empty((H, sum(lengths), d), storage_dtype(cfg.dtype))
     start = 0
     for b, n in enumerate(lengths):
         for h in range(H):

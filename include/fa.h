@@ -66,6 +66,7 @@
  *            (fp32 on the fp32 MFMA: fp32 inputs, arithmetic and outputs)
  *  decode and merge: FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in
  *  {64, 128, 256}
+ *  fa_forward_fp8: E4M3 inputs, bf16 output, d = 128
  * The 16-bit formats and head dimensions up to 256 are those the pages list
  * for fused kernels ("What is FlashAttention?", "Trade-offs and edge cases");
  * both 16-bit formats run the same kernels, on the MFMA of their format, with
@@ -133,6 +134,33 @@ fa_status fa_forward(fa_dtype dtype, int B, int H, int Nq, int Nk, int d,
                      const void* q, const void* k, const void* v,
                      const int32_t* seqlens_k, float scale, int causal,
                      void* o, float* lse, hipStream_t stream);
+
+/*
+ * Forward pass on FP8 inputs: q, k and v hold OCP FP8 E4M3 codes (one byte
+ * per element: sign, 4 exponent bits with bias 7, 3 mantissa bits, largest
+ * finite value 448) and each tensor has one fp32 descale factor, so the real
+ * inputs are code * descale.  The pages name an FP8 forward among the newest
+ * kernels ("What is FlashAttention?", sections "Trade-offs and edge cases"
+ * and "What is FlashAttention 3?") without its scaling rules; this call computes the attention of the real inputs, exactly as
+ * fa_forward defines it, with the products on the FP8 MFMA:
+ *   s_ij = scale * q_descale * k_descale * (q_i . k_j over the codes),
+ *   O = v_descale * softmax(s) V_codes, LSE as for fa_forward.
+ * The probabilities of each key tile are rounded to E4M3 (after scaling by
+ * 2^8 into its normal range) for the second product; the row sums use them
+ * before rounding.
+ *
+ *   B, H, Nq, Nk, seqlens_k, scale, causal   as for fa_forward
+ *   d                  128
+ *   q                  [B][H][Nq][d] E4M3 codes; k, v [B][H][Nk][d]
+ *   q_descale, k_descale, v_descale   finite and > 0
+ *   o                  [B][H][Nq][d] bf16 output (round to nearest even)
+ *   lse                [B][H][Nq] fp32 output (natural log)
+ */
+fa_status fa_forward_fp8(int B, int H, int Nq, int Nk, int d,
+                         const void* q, const void* k, const void* v,
+                         const int32_t* seqlens_k, float scale,
+                         float q_descale, float k_descale, float v_descale,
+                         int causal, void* o, float* lse, hipStream_t stream);
 
 /*
  * Bytes of device workspace fa_backward needs for this problem (0 for an

@@ -25,7 +25,7 @@ MIS = 0x10004        # 4-byte aligned, not 16-byte aligned
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declarations_are_exported():
@@ -41,7 +41,7 @@ def test_header_declarations_are_exported():
 
 
 def test_version_and_status_strings():
-    assert fa.fa_abi_version() == 3
+    assert fa.fa_abi_version() == 4
     assert fa.fa_status_string(fa.FA_SUCCESS) == "FA_SUCCESS"
     assert fa.fa_status_string(fa.FA_ERROR_INVALID_VALUE) == "FA_ERROR_INVALID_VALUE"
     assert fa.fa_status_string(fa.FA_ERROR_UNSUPPORTED) == "FA_ERROR_UNSUPPORTED"
@@ -193,6 +193,32 @@ def test_varlen_empty_unsupported_and_limits():
     assert bwd_varlen(tk=0, k=None, v=None, dk=None, dv=None, dq=None) == \
         fa.FA_ERROR_INVALID_VALUE
     assert fwd_varlen(B=1 << 20, H=1 << 10, mq=1 << 16) == fa.FA_ERROR_INVALID_VALUE
+
+
+def fwd_fp8(B=1, H=1, N=16, Nk=16, d=128, q=A, k=A, v=A, lens=None, scale=0.1, qd=0.5, kd=0.5,
+            vd=0.5, causal=0, o=A, lse=A):
+    return fa.fa_forward_fp8(B, H, N, Nk, d, q, k, v, lens, scale, qd, kd, vd, causal, o, lse,
+                             None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(N=-1), dict(Nk=-1), dict(d=0), dict(scale=0.0), dict(scale=math.nan),
+    dict(qd=0.0), dict(kd=-1.0), dict(vd=math.inf), dict(qd=math.nan), dict(causal=2),
+    dict(scale=1e30, qd=1e30, kd=1e30),
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None),
+    dict(q=MIS), dict(k=MIS), dict(o=MIS), dict(lse=MIS), dict(lens=A + 2),
+])
+def test_forward_fp8_rejects_invalid_arguments(kw):
+    assert fwd_fp8(**kw) == fa.FA_ERROR_INVALID_VALUE
+
+
+def test_forward_fp8_unsupported_and_empty():
+    for d in (64, 96, 256):
+        assert fwd_fp8(d=d) == fa.FA_ERROR_UNSUPPORTED
+    assert fwd_fp8(N=0, q=None, k=None, v=None, o=None, lse=None) == fa.FA_SUCCESS
+    assert fwd_fp8(B=0, q=None, o=None, lse=None) == fa.FA_SUCCESS
+    assert fwd_fp8(N=8, Nk=0, k=None, v=None, o=None) == fa.FA_ERROR_INVALID_VALUE
+    assert fwd_fp8(B=65535, H=65535, N=1 << 20, Nk=1 << 20) == fa.FA_ERROR_INVALID_VALUE
 
 
 def test_torch_wrappers_validate_before_calling():

@@ -1,5 +1,6 @@
 """Seeded generator, bf16 rounding and work accounting (CPU only)."""
 
+import dataclasses
 import json
 import math
 import os
@@ -198,3 +199,49 @@ def test_packed_generators():
     assert t.shape == (2, 8, 64) and t.dtype == np.uint16
     assert np.array_equal(t[1, 3:8], fi.make_head(cfg, "k", 2, 1, 2, 5, 64))
     assert np.array_equal(t[0, 0:3], fi.make_head(cfg, "k", 0, 0, 2, 3, 64))
+
+
+def test_e4m3_decoding_follows_the_format():
+    """OCP FP8 E4M3: bias 7, 3 mantissa bits, subnormals m * 2^-9, no
+    infinities, S.1111.111 NaN; every code agrees with torch's float8_e4m3fn."""
+    torch = pytest.importorskip("torch")
+    dec = fi.e4m3_bits_to_f64
+    assert dec(0x38) == 1.0 and dec(0x7E) == 448.0 and dec(0xFE) == -448.0
+    assert dec(0x08) == 2.0 ** -6 and dec(0x01) == 2.0 ** -9 and dec(0x07) == 7 * 2.0 ** -9
+    assert dec(0x00) == 0.0 and np.signbit(dec(0x80)) and dec(0x40) == 2.0
+    assert dec(0x3C) == 1.5 and dec(0x77) == 240.0 and dec(0x78) == 256.0
+    assert np.isnan(dec(0x7F)) and np.isnan(dec(0xFF))
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = dec(codes)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.array_equal(mine[~np.isnan(mine)], ref[~np.isnan(ref)])
+
+
+def test_e4m3_encoding_rounds_to_nearest_even():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    codes = np.arange(256, dtype=np.uint8)
+    finite = fi.e4m3_bits_to_f64(codes[(codes & 0x7F) != 0x7F])
+    pos = np.sort(fi.e4m3_bits_to_f64(codes[:127]))
+    x = np.concatenate([rng.standard_normal(20000) * np.exp(rng.uniform(-12, 6, 20000)),
+                        finite, (pos[:-1] + pos[1:]) / 2, -(pos[:-1] + pos[1:]) / 2])
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(fi.f64_to_e4m3_bits(x), ref)
+    assert fi.f64_to_e4m3_bits(1.0 + 2.0 ** -4) == 0x38      # tie to the even mantissa 0
+    assert fi.f64_to_e4m3_bits(1.0 + 3 * 2.0 ** -4) == 0x3A  # tie to the even mantissa 2
+    with pytest.raises(ValueError):
+        fi.f64_to_e4m3_bits(465.0)
+
+
+def test_fp8_generator_codes_dequantise_to_the_draws():
+    cfg = dataclasses.replace(fi.CONFIGS[3], N=64, H=2, dtype="e4m3")
+    for name in ("q", "k", "v"):
+        codes = fi.make_head(cfg, name, 0, 1, seed=3)
+        assert codes.dtype == np.uint8 and codes.shape == (64, 128)
+        x = fi.make_head(dataclasses.replace(cfg, dtype="f32"), name, 0, 1, seed=3)
+        deq = fi.widen(codes, "e4m3") * fi.FP8_DESCALE[name]
+        # nearest E4M3 value: relative error at most 2^-4 (normals)
+        assert np.all(np.abs(deq - x) <= 2.0 ** -4 * np.abs(x) + 2.0 ** -10 * fi.FP8_DESCALE[name])
+        assert np.max(np.abs(fi.widen(codes, "e4m3"))) <= 448
