@@ -182,12 +182,27 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
     __syncthreads();
   }
 
+  // Loop-invariant parts of the LDS addresses.  K fragments: row
+  // 32 sb + key_perm(l32), chunks 4 ks + 2 hi + e; the swizzle only sees row
+  // bits 1..3, which key_perm fixes per lane, so 32 sb enters as an offset.
   const int krow = key_perm(l32);
-  // transposing reads: lane i of a 16-lane group addresses row i / 2 of an
-  // 8-row slab, bytes 8 (i % 2) .. of the 16-byte chunk of its feature half
+  int k_at[KS][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) k_at[ks][e] = fp8_off(krow, 4 * ks + 2 * hi + e);
+  // Transposing reads: lane i of a 16-lane group addresses row i / 2 of an
+  // 8-row slab, bytes 8 (i % 2) .. of the 16-byte chunk of its feature half.
+  // Slab t of a 64-key step starts at row 32 (t / 2) + 16 hi + 8 (t % 2); the
+  // swizzle sees row bits 1..3, i.e. the lane's row in the slab and t % 2.
   const int tr_row = (lane & 15) >> 1;
-  const int tr_half = (lane & 1) * 8;
-  const int tr_chunk = (lane >> 4) & 1;
+  int v_at[2][NDB];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      v_at[par][db] = fp8_off(16 * hi + 8 * par + tr_row, 2 * db + ((lane >> 4) & 1)) +
+                      (lane & 1) * 8;
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
@@ -201,12 +216,10 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
         s[sb] = f32x16{};
-        const int row = 32 * sb + krow;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const int c = 4 * ks + 2 * hi;
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(Kt + fp8_off(row, c));
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(Kt + fp8_off(row, c + 1));
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(Kt + 32 * sb * D + k_at[ks][0]);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(Kt + 32 * sb * D + k_at[ks][1]);
           i32x8 a;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
@@ -217,41 +230,49 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
         }
       }
 
-      // scale to log2 units; mask on absolute positions where the tile
-      // crosses the key length or this wave's causal limit
+      // mask on absolute positions where the tile crosses the key length or
+      // this wave's causal limit: key key0 + 32 sb + 16 hi + v is visible iff
+      // it is at most lim, bit v of a per-lane prefix mask
       const bool need_mask =
           key0 + BC > kv_len || (causal && key0 + BC - 1 > qw0 + off);
-      const int lim = min(kv_len - 1, causal ? query + off : kv_len - 1);
-      float mx = kNegInf;
+      if (need_mask) {
+        const int lim = (causal ? min(kv_len - 1, query + off) : kv_len - 1) - key0 - 16 * hi;
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+          const uint32_t vis = prefix_bits(lim - 32 * sb);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[sb][v] = keep_if_bit(s[sb][v], vis, v, kNegInf);
+        }
+      }
+      // the maximum of the raw scores (qk_log2 > 0), then x = s * qk_log2
+      float mr = kNegInf;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = s[sb][v] * qk_log2;
-          if (need_mask && key0 + 32 * sb + 16 * hi + v > lim) x = kNegInf;
-          s[sb][v] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = halfwave_max(mx);
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      const float base = m_use - 8.f;
+        for (int v = 0; v < 16; ++v) mr = fmaxf(mr, s[sb][v]);
+      const float m_new = fmaxf(m, halfwave_max(mr) * qk_log2);
+      // rescale l and o only when some lane's maximum moved
+      if (__builtin_amdgcn_ballot_w64(m_new != m) != 0) {
+        const float alpha = fast_exp2(m - (m_new == kNegInf ? 0.f : m_new));
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+        m = m_new;
+      }
+      // p = 2^(x - m + 8), one fma and one exp per score
+      const float nb = 8.f - (m == kNegInf ? 0.f : m);
       float rs = 0.f;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float p = fast_exp2(s[sb][v] - base);
+          const float p = fast_exp2(__builtin_fmaf(s[sb][v], qk_log2, nb));
           s[sb][v] = p;
           rs += p;
         }
-      l = l * alpha + rs;
-      m = m_new;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+      l += rs;
 
 #pragma unroll
       for (int u = 0; u < NPV; ++u) {
@@ -265,13 +286,11 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
         }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int chunk = 2 * db + tr_chunk;
           i32x8 a;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             // bytes 8t.. of the operand: keys 64 u + 32 (t / 2) + 16 hi + 8 (t % 2) + 0..7
-            const int row = 64 * u + 32 * (t >> 1) + 16 * hi + 8 * (t & 1) + tr_row;
-            const i32x2 r = read_tr8(Vt + fp8_off(row, chunk) + tr_half);
+            const i32x2 r = read_tr8(Vt + (64 * u + 32 * (t >> 1)) * D + v_at[t & 1][db]);
             a[2 * t] = r[0];
             a[2 * t + 1] = r[1];
           }
