@@ -27,9 +27,13 @@
 //  * V^T fragments come from transposing LDS reads (ds_read_b64_tr_b8: a
 //    16-lane group reads 8 rows x 16 bytes and lane i receives byte i of
 //    each row), four per MFMA, in exactly that key order.
-//  * K and V tiles (128 keys) go HBM -> registers -> LDS one tile ahead in a
-//    two-slot ring; 16-byte chunks are XOR-swizzled by row so that both the
-//    K fragment reads and the transposing V reads are free of bank conflicts.
+//  * K and V tiles (128 keys) go from HBM straight into LDS (buffer loads with
+//    an LDS destination, 16 bytes per lane, 1 KiB per wave instruction), two
+//    tiles ahead in a three-slot ring, so a copy has two tiles of compute to
+//    land; the buffer descriptors end at the sequence's key length, so keys
+//    past it read as zeros.  16-byte chunks are XOR-swizzled by row (each lane
+//    fetches the chunk that belongs at its LDS position) so that both the K
+//    fragment reads and the transposing V reads are free of bank conflicts.
 //  * l is kept per lane over its own keys and combined with the partner lane
 //    once, after the last tile; the running maximum is exchanged per tile.
 
@@ -99,10 +103,12 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
   constexpr int NPV = BC / 64;                    // 64-key steps of O^T = V^T P^T
   constexpr int NDB = D / 32;                     // 32-feature blocks of O^T
   constexpr int TILE = BC * D;                    // bytes per K or V tile
-  constexpr int CPT = TILE / 16 / (NW * 64);      // 16-byte chunks per thread
-  static_assert(CPT * 16 * NW * 64 == TILE, "tile copy covers the tile");
-  __shared__ __attribute__((aligned(16))) uint8_t Ks[2][TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t Vs[2][TILE];
+  constexpr int SLOTS = 3;                        // ring depth: copies run two tiles ahead
+  constexpr int kBlks = TILE / 1024;              // 1 KiB copy blocks per tensor and tile
+  constexpr int kBlksPerWave = 2 * kBlks / NW;
+  static_assert(kBlksPerWave * NW == 2 * kBlks, "whole copy blocks per wave");
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[SLOTS][TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs[SLOTS][TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -149,38 +155,38 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
   float m = kNegInf;   // running maximum of x = score * log2(e), this lane's query
   float l = 0.f;       // this lane's share of the running sum of 2^(x - m + 8)
 
-  u32x4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int kt) FA_INLINE {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int u = tid + i * NW * 64;
-      const int row = u / (D / 16);
-      const int c = u % (D / 16);
-      const int key = kt * BC + row;
-      // keys at or past the length are never visible; zeros keep whatever
-      // lies there out of 0 * x products
-      const bool ok = key < kv_len;
-      const size_t at = (size_t)key * D + c * 16;
-      kreg[i] = ok ? *reinterpret_cast<const u32x4*>(Kh + at) : u32x4{};
-      vreg[i] = ok ? *reinterpret_cast<const u32x4*>(Vh + at) : u32x4{};
-    }
-  };
-  auto store_tile = [&](int buf) FA_INLINE {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int u = tid + i * NW * 64;
-      const int row = u / (D / 16);
-      const int c = u % (D / 16);
-      *reinterpret_cast<u32x4*>(&Ks[buf][fp8_off(row, c)]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&Vs[buf][fp8_off(row, c)]) = vreg[i];
-    }
-  };
+  // The Q fragments must have landed before the loop: the tile copies are
+  // issued outside the compiler's counter tracking, so a wait it placed for Q
+  // inside the loop would also wait for copies in flight.
+  wait_vmem();
 
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+  // Copies: wave w fills 1 KiB blocks w * kBlksPerWave + j (K blocks first,
+  // then V) of each tile; lane l writes bytes [16 l, 16 l + 16) of a block,
+  // row 8 b + l / 8, LDS chunk l % 8, so it fetches global chunk
+  // (l % 8) ^ swz(row).  Keys at or past the key length read as zeros (the
+  // descriptors end there), which also keeps whatever lies past it out of
+  // 0 * x products.
+  const u32x4 k_rsrc = buffer_rsrc_words(Kh, (uint32_t)(kv_len * D));
+  const u32x4 v_rsrc = buffer_rsrc_words(Vh, (uint32_t)(kv_len * D));
+  int voff[kBlksPerWave];
+#pragma unroll
+  for (int j = 0; j < kBlksPerWave; ++j) {
+    const int rb = (wave * kBlksPerWave + j) % kBlks;
+    const int row = rb * 8 + lane / 8;
+    voff[j] = row * D + ((lane % 8) ^ fp8_swz(row)) * 16;
   }
+  auto issue_tile = [&](int kt) FA_INLINE {
+    const int slot = kt % SLOTS;
+#pragma unroll
+    for (int j = 0; j < kBlksPerWave; ++j) {
+      const int blk = wave * kBlksPerWave + j;
+      const bool is_k = blk < kBlks;
+      uint8_t* dst = (is_k ? Ks[slot] : Vs[slot]) + (blk % kBlks) * 1024;
+      lds_dma16(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D);
+    }
+  };
+  if (n_kt > 0) issue_tile(0);
+  if (n_kt > 1) issue_tile(1);
 
   // Loop-invariant parts of the LDS addresses.  K fragments: row
   // 32 sb + key_perm(l32), chunks 4 ks + 2 hi + e; the swizzle only sees row
@@ -205,8 +211,18 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
                       (lane & 1) * 8;
 
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    const int buf = kt % SLOTS;
+    // this wave's copies of tile kt have landed once at most those of tile
+    // kt + 1 are outstanding (loads complete in order); after the barrier
+    // every wave's have, and every wave has finished reading the slot that
+    // tile kt + 2 goes to (tile kt - 1's)
+    if (kt + 1 < n_kt)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kBlksPerWave);   // vmcnt(kBlksPerWave)
+    else
+      wait_vmem();
+    asm volatile("" ::: "memory");
+    lds_barrier();
+    if (kt + 2 < n_kt) issue_tile(kt + 2);
     const int key0 = kt * BC;
     const bool active = qw0 < N && (!causal || key0 <= qw0 + 31 + off);
     if (active) {
@@ -297,10 +313,6 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
           o[db] = mfma_fp8(a, pb, o[db]);
         }
       }
-    }
-    if (kt + 1 < n_kt) {
-      store_tile(buf ^ 1);
-      __syncthreads();
     }
   }
 
