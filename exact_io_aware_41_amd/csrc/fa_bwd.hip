@@ -169,7 +169,7 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
   elt8 kf[C::KS], vf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    if (my_key < Nk) {
+    if (my_key < kv_len) {   // keys past the length never enter a product
       kf[ks] = *reinterpret_cast<const elt8*>(Kh + (size_t)my_key * D + ks * 16 + hi * 8);
       vf[ks] = *reinterpret_cast<const elt8*>(Vh + (size_t)my_key * D + ks * 16 + hi * 8);
     } else {
@@ -432,17 +432,17 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
   // Staging.  Row-major K and V tiles are copied straight from global memory
   // into LDS (lane l of a wave fills bytes [16 l, 16 l + 16) of a 1 KiB
   // block; each lane fetches the global chunk that the tile's XOR swizzle
-  // places there), one tile ahead.  The buffer descriptors cover exactly one
-  // head, so keys at or past N read as zeros; keys in [L_b, N) are masked.
+  // places there), one tile ahead.  The buffer descriptors end at the key
+  // length L_b, so keys at or past it read as zeros.
   // K is read both as 16-row fragments (S^T = K Q^T) and by transposing
   // reads (the A operand of dQ^T = K^T dS^T), so no transposed copy exists.
   constexpr int kRowsPerBlk = 1024 / (D * 2);
   constexpr int kBlksPerTensor = BC / kRowsPerBlk;
   constexpr int kBlksPerWave = 2 * kBlksPerTensor / NW;
   static_assert(2 * kBlksPerTensor % NW == 0 && kBlksPerWave >= 1, "whole 1 KiB blocks per wave");
-  const int head_bytes = Nk * D * 2;
-  const u32x4 k_rsrc = buffer_rsrc_words(Kh, (uint32_t)head_bytes);
-  const u32x4 v_rsrc = buffer_rsrc_words(Vh, (uint32_t)head_bytes);
+  const int key_bytes = kv_len * D * 2;
+  const u32x4 k_rsrc = buffer_rsrc_words(Kh, (uint32_t)key_bytes);
+  const u32x4 v_rsrc = buffer_rsrc_words(Vh, (uint32_t)key_bytes);
   // per-lane byte offsets inside a tile, computed once; the tile's position
   // goes in the scalar offset (see fa_fwd.hip: copies issued through the
   // builtin made the next transposing read wait for the whole copy)

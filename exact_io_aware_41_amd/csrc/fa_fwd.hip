@@ -186,16 +186,17 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
   // ---- staging: K and V tiles go straight from global memory into LDS
   // (buffer loads with an LDS destination: lane l of a wave fills bytes
   // [16 l, 16 l + 16) of a 1 KiB block), one tile ahead, with no registers.
-  // The buffer descriptors cover exactly one head, so keys at or past N read
-  // as zeros; keys in [L_b, N) are masked.  Each lane fetches the global chunk
+  // The buffer descriptors end at the sequence's key length L_b, so keys at
+  // or past it read as zeros (masked anyway, and whatever lies there never
+  // enters a 0 * x product).  Each lane fetches the global chunk
   // that the tile's swizzle places at its LDS position.
   constexpr int kRowsPerBlk = 1024 / (D * 2);
   constexpr int kBlksPerTensor = BC / kRowsPerBlk;
   constexpr int kBlksPerWave = 2 * kBlksPerTensor / NW;
   static_assert(2 * kBlksPerTensor % NW == 0 && kBlksPerWave >= 1, "whole 1 KiB blocks per wave");
-  const int head_bytes = Nk * D * 2;
-  const u32x4 k_rsrc = buffer_rsrc_words(Kh, (uint32_t)head_bytes);
-  const u32x4 v_rsrc = buffer_rsrc_words(Vh, (uint32_t)head_bytes);
+  const int key_bytes = kv_len * D * 2;
+  const u32x4 k_rsrc = buffer_rsrc_words(Kh, (uint32_t)key_bytes);
+  const u32x4 v_rsrc = buffer_rsrc_words(Vh, (uint32_t)key_bytes);
   // per-lane byte offsets inside a tile, computed once: the loads' address
   // registers then stay untouched for the whole loop (the compiler treats
   // them as pending load results and would otherwise wait for the copy

@@ -42,7 +42,9 @@
  *    enqueues work on `stream` (calls return without synchronising).  Calls
  *    are re-entrant.  Outputs must not alias inputs.
  *  - Data pointers must be 16-byte aligned.
- *  - Inputs must be finite; NaN or infinite inputs propagate unchecked.
+ *  - Inputs must be finite; NaN or infinite inputs propagate unchecked.  Key
+ *    and value rows at or past a sequence's key length are never read, so
+ *    they may hold anything.
  *  - B, H or N equal to 0 is an empty problem: FA_SUCCESS, nothing is
  *    launched and pointers are not inspected.
  *
