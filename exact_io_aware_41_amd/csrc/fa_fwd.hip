@@ -280,24 +280,36 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
 #endif
   };
 
+  // A fragment of V^T for keys {16g + 4hi + 0..3, 16g + 8 + 4hi + 0..3}
+  // (the order of the P^T fragment) and features 32 db + l32: two
+  // transposing reads of the row-major V tile.  The segment swizzle sees only
+  // row bits 0..1, which the lane fixes (rows 4hi + ts/4, + 8, + 16g), so the
+  // lane's element offset for g = 0 is computed once per feature block and the
+  // key group and the second read enter as immediate offsets.
+  int v_at[C::NDB];
+  {
+    const int ts = lane & 15;
+    const int tcol = ((lane >> 4) & 1) * 16 + 4 * (ts & 3);
+    const int r0 = 4 * hi + (ts >> 2);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int col = db * 32 + tcol;
+      v_at[db] = r0 * D + (((col >> 5) ^ seg_swizzle<D>(r0)) << 5) + (col & 31);
+    }
+  }
+
   // O^T += V^T(t) P^T(t), V^T fragments prefetched the same way
   auto stage_PV = [&](int vbuf, auto&& dma) FA_INLINE {
     constexpr int NF = C::NG * C::NDB;   // fragments per tile, ordered (g, db)
-    // A fragment of V^T for keys {16g + 4hi + 0..3, 16g + 8 + 4hi + 0..3}
-    // (the order of the P^T fragment) and features 32 db + l32: two
-    // transposing reads of the row-major V tile
-    const int ts = lane & 15;
-    const int tcol = ((lane >> 4) & 1) * 16 + 4 * (ts & 3);
+    // the slot index is made opaque: otherwise the compiler folds the ring's
+    // modulo into the addresses as negative constants, which the reads'
+    // unsigned offset field cannot hold, and adds them per read instead
+    asm volatile("" : "+s"(vbuf));
     auto vfrag = [&](int f) FA_INLINE {
       const int g = f / C::NDB, db = f % C::NDB;
-      const int r0 = 16 * g + 4 * hi + (ts >> 2);
-      const int r1 = r0 + 8;
-      const int col = db * 32 + tcol;
-      const elt* vb = Vs[vbuf];
-      const s16x4 lo =
-          read_tr16(vb + r0 * D + (((col >> 5) ^ seg_swizzle<D>(r0)) << 5) + (col & 31));
-      const s16x4 up =
-          read_tr16(vb + r1 * D + (((col >> 5) ^ seg_swizzle<D>(r1)) << 5) + (col & 31));
+      const elt* vb = Vs[vbuf] + v_at[db] + 16 * g * D;
+      const s16x4 lo = read_tr16(vb);
+      const s16x4 up = read_tr16(vb + 8 * D);
       return __builtin_bit_cast(elt8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     constexpr int kReadsPerFrag = 2;
