@@ -154,11 +154,20 @@ __device__ __forceinline__ void lds_dma16_tracked(__amdgpu_buffer_rsrc_t rsrc, v
 // accesses against it, so the caller must wait_vmem() and pass a barrier
 // before anything reads the destination.  (Issued through the builtin, the
 // compiler makes the next LDS read wait for the whole copy.)
-__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, const void* lds, int voff, int soff) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)lds));
+__device__ __forceinline__ void lds_dma16_at(const u32x4& rsrc, uint32_t lds, int voff, int soff) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(base), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+// 32-bit LDS address of a __shared__ object.  Taken once from the object
+// itself, it lets callers form slot addresses with integer arithmetic instead
+// of casting generic pointers back to LDS (each such cast carries a null test).
+template <class T>
+__device__ __forceinline__ uint32_t lds_address(const T* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
+}
+__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, const void* lds, int voff, int soff) {
+  lds_dma16_at(rsrc, lds_address(static_cast<const char*>(lds)), voff, soff);
 }
 
 // Wait until every vector-memory load issued by this wave has completed,

@@ -213,24 +213,23 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
                            : ((((cpos >> 2) ^ seg_swizzle<D>(row)) << 2) | (cpos & 3));
     voff[j] = row * (D * 2) + chunk * 16;
   }
-  auto issue_tile = [&](int kt, int kbuf, int vslot) FA_INLINE {
-#pragma unroll
-    for (int j = 0; j < kBlksPerWave; ++j) {
-      const int blk = wave * kBlksPerWave + j;
-      const bool is_k = blk < kBlksPerTensor;
-      const int rb = is_k ? blk : blk - kBlksPerTensor;
-      elt* dst = (is_k ? Ks[kbuf] : Vs[vslot]) + rb * kRowsPerBlk * D;
-      lds_dma16(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D * 2);
-    }
-  };
-
-  // one of this wave's copies of tile kt (block j of its share)
+  // one of this wave's copies of tile kt (block j of its share); slot
+  // addresses are formed as 32-bit LDS offsets from the rings' bases
+  const uint32_t ks_lds = lds_address(&Ks[0][0]);
+  const uint32_t vs_lds = lds_address(&Vs[0][0]);
+  constexpr uint32_t kSlotBytes = BC * D * 2;
   auto issue_block = [&](int kt, int kbuf, int vslot, int j) FA_INLINE {
     const int blk = wave * kBlksPerWave + j;
     const bool is_k = blk < kBlksPerTensor;
     const int rb = is_k ? blk : blk - kBlksPerTensor;
-    elt* dst = (is_k ? Ks[kbuf] : Vs[vslot]) + rb * kRowsPerBlk * D;
-    lds_dma16(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D * 2);
+    const uint32_t dst = (is_k ? ks_lds + (uint32_t)kbuf * kSlotBytes
+                               : vs_lds + (uint32_t)vslot * kSlotBytes) +
+                         (uint32_t)(rb * kRowsPerBlk * D * 2);
+    lds_dma16_at(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D * 2);
+  };
+  auto issue_tile = [&](int kt, int kbuf, int vslot) FA_INLINE {
+#pragma unroll
+    for (int j = 0; j < kBlksPerWave; ++j) issue_block(kt, kbuf, vslot, j);
   };
   auto no_dma = [](int) FA_INLINE {};
 
