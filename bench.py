@@ -143,6 +143,17 @@ def cpu_baseline(cfg, inputs, budget_s):
             "seconds": round(elapsed, 2)}
 
 
+def forward_bytes(cfg, Nk=None):
+    """Algorithmic HBM bytes of one forward launch: Q, K and V read once, O
+    and the fp32 LSE written once (K and V rows past a key length still
+    counted: the padded tensors are the call's inputs)."""
+    es = {"e4m3": 1, "f32": 4}.get(cfg.dtype, 2)
+    out_es = 2 if cfg.dtype == "e4m3" else es
+    nk = cfg.N if Nk is None else Nk
+    rows_q, rows_k = cfg.B * cfg.H * cfg.N, cfg.B * cfg.H * nk
+    return rows_q * cfg.d * es + 2 * rows_k * cfg.d * es + rows_q * cfg.d * out_es + rows_q * 4
+
+
 def step_flops(cfg, lengths=None, heads=None, Nk=None):
     """Credited FLOPs of one step (all heads, or `heads` heads).  With Nk keys
     (Nk != N) every visible pair is counted."""
@@ -293,12 +304,26 @@ def main():
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": None if variant or KV_LEN else measured_traffic(dominant, args.config)}
+    # the forward's HBM rate on its algorithmic bytes (Q, K, V read once, O and
+    # the LSE written once); the single-head fp32 workload (16.8 MFLOP against
+    # 263 KB) is bound by latency and bytes, not by the MFMA, so its roofline
+    # is the HBM one
+    fwd_bytes = forward_bytes(cfg, Nk=KV_LEN)
+    fwd_gbs = fwd_bytes / (per_kernel["fwd"] * 1e-3) / 1e9
+    fwd_hbm = {"bytes_per_launch": fwd_bytes, "achieved_gbs": round(fwd_gbs, 1),
+               "peak_gbs": PEAK_HBM_GBS, "frac": round(fwd_gbs / PEAK_HBM_GBS, 4),
+               "latency_us": round(per_kernel["fwd"] * 1e3, 2)}
+    if cfg.cid == 1 and not variant and KV_LEN is None:
+        roofline = {"bound": "hbm", "kernel": "fwd", "achieved": fwd_hbm["achieved_gbs"],
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": fwd_hbm["frac"],
+                    "traffic": measured_traffic("fwd", args.config)}
 
     extra = {
         "per_launch_ms": {n: round(t, 4) for n, t in per_kernel.items()},
         "kernel_tflops": {n: round(kernel_flops[n] / (per_kernel[n] * 1e-3) / 1e12, 1)
                           for n in kernel_flops},
         "pct_of_peak": round(100.0 * value / peak, 2),
+        "fwd_hbm": fwd_hbm,
     }
     if cfg.backward:
         fwd_ms = per_kernel["fwd"]
