@@ -479,34 +479,41 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
 // disjoint LDS banks.
 // ---------------------------------------------------------------------------
 
-template <int D, int NW, int BC>
+template <int D, int NW, int BC, int KSPLIT = 1>
 struct FwdF32Cfg {
   static constexpr int BR = NW * 32;
-  static constexpr int NT = NW * 64;
+  static constexpr int NT = NW * KSPLIT * 64;
+  static constexpr int BCR = BC * KSPLIT;     // keys staged per round
   static constexpr int KS = D / 2;
   static constexpr int NCB = BC / 32;
   static constexpr int NDB = D / 32;
   static constexpr int KPITCH = D + 2;   // floats per K row (halves on odd/even banks)
   static constexpr int VPITCH = D + 8;   // floats per V row (key+4 rows 32 banks apart)
-  static constexpr int KU = BC * D / 4 / NT;  // 16-byte chunks per thread
-  static_assert(KU * NT * 4 == BC * D, "tile must split evenly over threads");
+  static constexpr int KU = BCR * D / 4 / NT;  // 16-byte chunks per thread
+  static_assert(KU * NT * 4 == BCR * D, "tile must split evenly over threads");
 };
 
-template <int D, int NW, int BC>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+// KSPLIT > 1 (small grids): KSPLIT waves share each 32-row block, wave
+// split j taking key tiles j, j + KSPLIT, ... of a round of KSPLIT tiles, and
+// the partial states (m, l, o) of a row block are merged through LDS at the
+// end with the same rescale, so a grid too small to fill the chip still runs
+// KSPLIT times fewer dependent tiles per wave.
+template <int D, int NW, int BC, int KSPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * KSPLIT * 64, NW * KSPLIT * 64)))
 void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, const int32_t* __restrict__ seqlens_k,
                        float scale_log2, int causal, float* __restrict__ O,
                        float* __restrict__ LSE, int B, int H, int n_q, int n_k,
                        int n_qtiles, const int32_t* __restrict__ cu_q,
                        const int32_t* __restrict__ cu_k, int total_q, int total_k) {
-  using C = FwdF32Cfg<D, NW, BC>;
-  __shared__ __attribute__((aligned(16))) float Ks[2][BC * C::KPITCH];
-  __shared__ __attribute__((aligned(16))) float Vs[2][BC * C::VPITCH];
+  using C = FwdF32Cfg<D, NW, BC, KSPLIT>;
+  __shared__ __attribute__((aligned(16))) float Ks[2][C::BCR * C::KPITCH];
+  __shared__ __attribute__((aligned(16))) float Vs[2][C::BCR * C::VPITCH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = (tid >> 6) % NW;     // row block
+  const int split = (tid >> 6) / NW;    // key split of the row block
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -526,7 +533,7 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   const int qw0 = q0 + wave * 32;
   int kv_end = kv_len;
   if (causal) kv_end = min(kv_end, max(0, min(q0 + C::BR + off, Nk)));
-  const int n_kt = (kv_end + BC - 1) / BC;
+  const int n_kt = (kv_end + C::BCR - 1) / C::BCR;   // rounds of KSPLIT tiles
 
   const int qrow = qw0 + l32;
   float qf[C::KS];
@@ -544,7 +551,7 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   // after the compute instead
   constexpr bool kStage = D <= 128;
   auto load_tile = [&](int kt) FA_INLINE {
-    const int key0 = kt * BC;
+    const int key0 = kt * C::BCR;
 #pragma unroll
     for (int i = 0; i < C::KU; ++i) {
       const int u = tid + i * C::NT;
@@ -574,7 +581,7 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   // unstaged copy (d = 256): each 16-byte chunk goes to LDS as soon as it
   // arrives, so only a few registers are live
   auto copy_tile = [&](int kt, int buf) FA_INLINE {
-    const int key0 = kt * BC;
+    const int key0 = kt * C::BCR;
 #pragma unroll 4
     for (int i = 0; i < C::KU; ++i) {
       const int u = tid + i * C::NT;
@@ -603,8 +610,11 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
     if (kStage && kt + 1 < n_kt) load_tile(kt + 1);
-    const int key0 = kt * BC;
-    const bool wave_active = (qw0 < N) && (!causal || key0 <= qw0 + 31 + off);
+    const int key0 = kt * C::BCR + split * BC;   // this wave's tile of the round
+    const float* Kt = &Ks[buf][split * BC * C::KPITCH];
+    const float* Vt = &Vs[buf][split * BC * C::VPITCH];
+    const bool wave_active =
+        (qw0 < N) && key0 < kv_end && (!causal || key0 <= qw0 + 31 + off);
     if (wave_active) {
       f32x16 sacc[C::NCB];
 #pragma unroll
@@ -613,7 +623,7 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
         for (int c = 0; c < C::NCB; ++c)
-          sacc[c] = mfma_f32(Ks[buf][(c * 32 + l32) * C::KPITCH + 2 * ks + hi], qf[ks], sacc[c]);
+          sacc[c] = mfma_f32(Kt[(c * 32 + l32) * C::KPITCH + 2 * ks + hi], qf[ks], sacc[c]);
 
       const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0 + off);
       if (need_mask) {
@@ -658,7 +668,7 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
           const int key = c * 32 + c_row(v, lane);
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db)
-            oacc[db] = mfma_f32(Vs[buf][key * C::VPITCH + db * 32 + l32], sacc[c][v], oacc[db]);
+            oacc[db] = mfma_f32(Vt[key * C::VPITCH + db * 32 + l32], sacc[c][v], oacc[db]);
         }
     }
     if (kt + 1 < n_kt) {
@@ -668,6 +678,50 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         copy_tile(kt + 1, buf ^ 1);
     }
     __syncthreads();
+  }
+
+  if constexpr (KSPLIT > 1) {
+    // merge the row block's partial states: splits 1.. leave (m, l, o) in
+    // LDS (the tile buffers are free after the loop's last barrier), split
+    // 0 combines them, each weighed by 2^(m_j - M) with M the largest m
+    constexpr int kSlot = C::NDB * 16 + 2;   // floats per lane
+    static_assert(NW * (KSPLIT - 1) * 64 * kSlot <= 2 * C::BCR * C::KPITCH,
+                  "partial states fit the K tile buffers");
+    float* part = &Ks[0][0];
+    if (split > 0) {
+      float* dst = part + ((wave * (KSPLIT - 1) + split - 1) * 64 + lane) * kSlot;
+      dst[0] = m;
+      dst[1] = l;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[2 + db * 16 + v] = oacc[db][v];
+    }
+    __syncthreads();
+    if (split > 0) return;
+    float mj[KSPLIT];
+    mj[0] = m;
+#pragma unroll
+    for (int j = 1; j < KSPLIT; ++j)
+      mj[j] = part[((wave * (KSPLIT - 1) + j - 1) * 64 + lane) * kSlot];
+    float M = mj[0];
+#pragma unroll
+    for (int j = 1; j < KSPLIT; ++j) M = fmaxf(M, mj[j]);
+    const float w0 = (m == kNegInf) ? 0.f : fast_exp2(m - M);
+    l *= w0;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) oacc[db] *= w0;
+#pragma unroll
+    for (int j = 1; j < KSPLIT; ++j) {
+      const float* src = part + ((wave * (KSPLIT - 1) + j - 1) * 64 + lane) * kSlot;
+      const float w = (mj[j] == kNegInf) ? 0.f : fast_exp2(mj[j] - M);
+      l = __builtin_fmaf(src[1], w, l);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] = __builtin_fmaf(src[2 + db * 16 + v], w, oacc[db][v]);
+    }
+    m = M;
   }
 
   const float lt = halfwave_sum(l);
@@ -725,17 +779,30 @@ hipError_t launch_half_e(const FwdArgs& a) {
   }
 }
 
-template <int D>
-hipError_t launch_f32_d(const FwdArgs& a) {
-  using C = FwdF32Cfg<D, kF32NW, kF32BC>;
+template <int D, int KSPLIT>
+hipError_t launch_f32_split(const FwdArgs& a) {
+  using C = FwdF32Cfg<D, kF32NW, kF32BC, KSPLIT>;
   const int n_qtiles = (a.N + C::BR - 1) / C::BR;
   const dim3 grid((unsigned)((long long)n_qtiles * a.B * a.H));
-  hipLaunchKernelGGL((fa_fwd_f32_kernel<D, kF32NW, kF32BC>), grid, dim3(C::NT), 0, a.stream,
-                     static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+  hipLaunchKernelGGL((fa_fwd_f32_kernel<D, kF32NW, kF32BC, KSPLIT>), grid, dim3(C::NT), 0,
+                     a.stream, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), a.seqlens_k, a.scale * kLog2e, a.causal,
                      static_cast<float*>(a.o), a.lse, a.B, a.H, a.N, a.Nk, n_qtiles,
                      a.cu_q, a.cu_k, a.total_q, a.total_k);
   return hipGetLastError();
+}
+
+// Grids with fewer work-groups than the chip has CUs split each row block's
+// keys over four waves (d = 64, where four tiles of a round fit in LDS).
+constexpr long long kF32SplitBelow = 256;
+
+template <int D>
+hipError_t launch_f32_d(const FwdArgs& a) {
+  if constexpr (D == 64) {
+    const long long grid = (long long)((a.N + kF32NW * 32 - 1) / (kF32NW * 32)) * a.B * a.H;
+    if (grid < kF32SplitBelow) return launch_f32_split<D, 4>(a);
+  }
+  return launch_f32_split<D, 1>(a);
 }
 
 }  // namespace

@@ -90,6 +90,31 @@ def test_small_shapes_all_rows(d, causal, dtype):
             assert_forward_close(cfg, o, lse, ref_o, ref_l)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_d64_small_and_large_grids(causal):
+    """fp32 at d = 64 takes two paths by grid size: below the CU count each
+    64-row block's keys are split over four waves whose partial states are
+    merged at the end; above it one wave per 32-row block walks every key.
+    A 288-work-group batch (ragged lengths, an empty sequence) runs the
+    second path; each of two of its heads alone runs the first; all match
+    the oracle on every row."""
+    torch = torch_cuda()
+    cfg = custom(2, B=2, H=16, N=520, d=64, dtype="f32", causal=causal)
+    log_case(test="f32_d64_grids", shape=cfg.shape, causal=causal)
+    inputs = fi.make_inputs(cfg, seed=11)
+    inputs["lengths"] = np.array([0, 389], np.int32)
+    o, lse = run_forward(torch, cfg, inputs)
+    q, k, v = widen_all(cfg, inputs)
+    ref_o, ref_l = oracle.attention_materialised(q, k, v, cfg.scale, causal, inputs["lengths"])
+    assert_forward_close(cfg, o, lse, ref_o, ref_l)
+    for b, h in ((1, 0), (1, 15)):
+        one = custom(2, B=1, H=1, N=520, d=64, dtype="f32", causal=causal)
+        sub = {n: np.ascontiguousarray(inputs[n][b:b + 1, h:h + 1]) for n in ("q", "k", "v")}
+        sub["lengths"] = inputs["lengths"][b:b + 1].copy()
+        o1, l1 = run_forward(torch, one, sub)
+        assert_forward_close(one, o1, l1, ref_o[b:b + 1, h:h + 1], ref_l[b:b + 1, h:h + 1])
+
+
 def test_lengths_clamped_to_range():
     torch = torch_cuda()
     cfg = custom(2, B=3, H=2, N=130, causal=True)
