@@ -479,6 +479,9 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
 // disjoint LDS banks.
 // ---------------------------------------------------------------------------
 
+// LDS operand reads issued this many MFMAs ahead in the fp32 kernel
+constexpr int kF32Pre = 8;
+
 template <int D, int NW, int BC, int KSPLIT = 1>
 struct FwdF32Cfg {
   static constexpr int BR = NW * 32;
@@ -619,11 +622,31 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       f32x16 sacc[C::NCB];
 #pragma unroll
       for (int c = 0; c < C::NCB; ++c) sacc[c] = f32x16{};
+      // operands are read from LDS kF32Pre MFMAs ahead of their use, so the
+      // MFMAs do not each wait for their own read
+      {
+        constexpr int NF = C::KS * C::NCB;   // (ks, c)
+        auto kval = [&](int f) FA_INLINE {
+          const int ks = f / C::NCB, c = f % C::NCB;
+          return Kt[(c * 32 + l32) * C::KPITCH + 2 * ks + hi];
+        };
+        float ring[kF32Pre];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
+        for (int f = 0; f < kF32Pre; ++f) ring[f] = kval(f);
 #pragma unroll
-        for (int c = 0; c < C::NCB; ++c)
-          sacc[c] = mfma_f32(Kt[(c * 32 + l32) * C::KPITCH + 2 * ks + hi], qf[ks], sacc[c]);
+        for (int f = 0; f < NF; ++f) {
+          const float x = ring[f % kF32Pre];
+          if (f + kF32Pre < NF) ring[f % kF32Pre] = kval(f + kF32Pre);
+          sacc[f % C::NCB] = mfma_f32(x, qf[f / C::NCB], sacc[f % C::NCB]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, kF32Pre, 0);
+#pragma unroll
+        for (int f = 0; f < NF - kF32Pre; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kF32Pre, 0);
+      }
 
       const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0 + off);
       if (need_mask) {
@@ -661,15 +684,30 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha;
 
       // O^T += V^T P^T: one MFMA per key pair (lane halves supply keys k and k+4)
+      {
+        constexpr int NF = C::NCB * 16 * C::NDB;   // (c, v, db)
+        auto vval = [&](int f) FA_INLINE {
+          const int c = f / (16 * C::NDB), v = (f / C::NDB) % 16, db = f % C::NDB;
+          return Vt[(c * 32 + c_row(v, lane)) * C::VPITCH + db * 32 + l32];
+        };
+        float ring[kF32Pre];
 #pragma unroll
-      for (int c = 0; c < C::NCB; ++c)
+        for (int f = 0; f < kF32Pre; ++f) ring[f] = vval(f);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = c * 32 + c_row(v, lane);
-#pragma unroll
-          for (int db = 0; db < C::NDB; ++db)
-            oacc[db] = mfma_f32(Vt[key * C::VPITCH + db * 32 + l32], sacc[c][v], oacc[db]);
+        for (int f = 0; f < NF; ++f) {
+          const int c = f / (16 * C::NDB), v = (f / C::NDB) % 16, db = f % C::NDB;
+          const float x = ring[f % kF32Pre];
+          if (f + kF32Pre < NF) ring[f % kF32Pre] = vval(f + kF32Pre);
+          oacc[db] = mfma_f32(x, sacc[c][v], oacc[db]);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, kF32Pre, 0);
+#pragma unroll
+        for (int f = 0; f < NF - kF32Pre; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kF32Pre, 0);
+      }
     }
     if (kt + 1 < n_kt) {
       if (kStage)
