@@ -115,7 +115,9 @@ def cpu_baseline(cfg, inputs, budget_s):
                        if i.get("user_api") == "blas"), default=1)
     except Exception:  # noqa: BLE001 - report what we can
         threads = 1
-    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    # batch index fastest, so that a short sample spans the batch's sequences
+    # (with key lengths, not only the first sequence's heads)
+    heads = [(b, h) for h in range(cfg.H) for b in range(cfg.B)]
     lengths = inputs.get("lengths")
     flops = 0
     elapsed = 0.0
