@@ -72,8 +72,8 @@ def measured_traffic(kernel: str, config_id: int):
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
     p.add_argument("--workload", default="attention", choices=["attention", "decode"],
                    help="attention: the --config workload (default, the headline metric); "
@@ -93,12 +93,105 @@ def parse_args():
                         "padding, and time the packed entry points")
     p.add_argument("--decode-lengths", default=None, choices=[None, "zero_then_uniform"],
                    help="cached lengths of the decode workload (default: all full)")
+    p.add_argument("--causal-forward-side", type=int, default=1, choices=[0, 1],
+                   help="with the default training-step workload, also time the causal "
+                        "B=1, H=32, N=8192 forward on its own (1, default) or not (0)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time for the oracle baseline sample (0 disables it)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="after timing, run one device-to-device copy of MIB MiB so that HBM "
                         "byte counters can be scaled against a kernel of known traffic")
     return p.parse_args()
+
+
+def host_cpu():
+    """(cores this process may run on, CPU model string)."""
+    cores = len(os.sched_getaffinity(0))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+def blas_threads(n):
+    """Context that sets the BLAS / OpenMP pools to n threads (a no-op
+    context when threadpoolctl is missing)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=n)
+    except ImportError:
+        import contextlib
+        return contextlib.nullcontext()
+
+
+class SclkSampler:
+    """Samples the GPU's graphics clock (MHz, via torch.cuda.clock_rate) on a
+    background thread while a timed region runs; median of the samples, or
+    None where the query is unavailable."""
+
+    def __init__(self, torch, dev, period_s=0.002):
+        import threading
+        self.torch, self.dev, self.period = torch, dev, period_s
+        self.samples = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self.stop.is_set():
+            try:
+                mhz = self.torch.cuda.clock_rate(self.dev)
+            except Exception:  # noqa: BLE001 - clock query unavailable
+                return
+            if mhz:
+                self.samples.append(float(mhz))
+            self.stop.wait(self.period)
+
+    def __enter__(self):
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.thread.join()
+
+    def result(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"median_mhz": xs[len(xs) // 2], "max_mhz": xs[-1], "samples": len(xs)}
+
+
+def timing_stats(ms):
+    """Median and min of per-step (or per-launch) times in ms."""
+    xs = sorted(ms)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"median": round(med, 4), "min": round(xs[0], 4), "mean": round(sum(xs) / n, 4)}
+
+
+def measured_mfma(kernel: str, config_id: int):
+    """MFMA utilisation of a kernel from the committed rocprofv3 counter runs
+    (busy fraction of the MFMA units and executed MFMA TFLOP/s), or None when
+    missing or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    entry = data.get("kernels", {}).get(f"{kernel}@config{config_id}") or {}
+    if "mfma_busy_frac" not in entry:
+        return None
+    return {"mfma_busy_frac": entry["mfma_busy_frac"],
+            "mfma_executed_tflops": entry.get("mfma_executed_tflops"),
+            "effective_sclk_mhz": entry.get("effective_sclk_mhz")}
 
 
 def cpu_baseline(cfg, inputs, budget_s):
@@ -109,12 +202,7 @@ def cpu_baseline(cfg, inputs, budget_s):
     import fa_inputs as fi
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"), default=1)
-    except Exception:  # noqa: BLE001 - report what we can
-        threads = 1
+    cores, model = host_cpu()
     # batch index fastest, so that a short sample spans the batch's sequences
     # (with key lengths, not only the first sequence's heads)
     heads = [(b, h) for h in range(cfg.H) for b in range(cfg.B)]
@@ -128,21 +216,31 @@ def cpu_baseline(cfg, inputs, budget_s):
              for n in ("q", "k", "v", "do") if n in inputs}
         lb = None if lengths is None else np.asarray(lengths)[b:b + 1]
         t0 = time.perf_counter()
-        o, lse = oracle.attention_materialised(w["q"], w["k"], w["v"], cfg.scale, cfg.causal, lb)
-        if cfg.backward:
-            oracle.attention_backward(w["q"], w["k"], w["v"], o, w["do"], lse, cfg.scale,
-                                      cfg.causal, lb)
+        with blas_threads(cores):
+            o, lse = oracle.attention_materialised(w["q"], w["k"], w["v"], cfg.scale, cfg.causal,
+                                                   lb)
+            if cfg.backward:
+                oracle.attention_backward(w["q"], w["k"], w["v"], o, w["do"], lse, cfg.scale,
+                                          cfg.causal, lb)
         elapsed += time.perf_counter() - t0
         flops += step_flops(cfg, lb, heads=1, Nk=KV_LEN)
         done += 1
         if elapsed >= budget_s:
             break
     what = "forward+backward" if cfg.backward else "forward"
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{done} of {len(heads)} heads ({what}, fp64 materialised route), "
-                      f"{elapsed:.1f} s",
-            "seconds": round(elapsed, 2)}
+    res = {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+           "kind": "oracle", "cpu_model": model,
+           "sample": f"{done} of {len(heads)} heads ({what}, fp64 materialised route, BLAS "
+                     f"threads = {cores} cores of sched_getaffinity), {elapsed:.1f} s",
+           "seconds": round(elapsed, 2)}
+    if cfg.cid == 1 and cfg.H * cfg.B == 1:
+        # the single-head workload once more on one thread
+        t0 = time.perf_counter()
+        with blas_threads(1):
+            o, lse = oracle.attention_materialised(w["q"], w["k"], w["v"], cfg.scale, cfg.causal)
+        one = time.perf_counter() - t0
+        res["one_thread_value"] = flops / done / one / 1e12
+    return res
 
 
 def forward_bytes(cfg, Nk=None):
@@ -268,19 +366,23 @@ def main():
     events = [mk() for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        step(events[i])
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    with SclkSampler(torch, dev) as sclk:
+        wall0 = time.perf_counter()
+        start.record()
+        for i in range(args.steps):
+            step(events[i])
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
+    step_ms = timing_stats([e[0].elapsed_time(e[-1]) for e in events])
 
     names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"][:n_ev - 1]
     per_kernel = {n: sum(e[i].elapsed_time(e[i + 1]) for e in events) / args.steps
                   for i, n in enumerate(names)}
+    launch_ms = {n: timing_stats([e[i].elapsed_time(e[i + 1]) for e in events])
+                 for i, n in enumerate(names)}
     log("per-launch ms: " + ", ".join(f"{n}={t:.4f}" for n, t in per_kernel.items())
         + f"; wall {wall * 1e3 / args.steps:.4f} ms/step")
 
@@ -305,7 +407,8 @@ def main():
     achieved = kernel_flops[dominant] / (per_kernel[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": None if variant or KV_LEN else measured_traffic(dominant, args.config)}
+                "traffic": None if variant or KV_LEN else measured_traffic(dominant, args.config),
+                "counters": None if variant or KV_LEN else measured_mfma(dominant, args.config)}
     # the forward's HBM rate on its algorithmic bytes (Q, K, V read once, O and
     # the LSE written once); the single-head fp32 workload (16.8 MFLOP against
     # 263 KB) is bound by latency and bytes, not by the MFMA, so its roofline
@@ -321,7 +424,10 @@ def main():
                     "traffic": measured_traffic("fwd", args.config)}
 
     extra = {
+        "step_ms": step_ms,
+        "sclk": sclk.result(),
         "per_launch_ms": {n: round(t, 4) for n, t in per_kernel.items()},
+        "per_launch_stats_ms": launch_ms,
         "kernel_tflops": {n: round(kernel_flops[n] / (per_kernel[n] * 1e-3) / 1e12, 1)
                           for n in kernel_flops},
         "pct_of_peak": round(100.0 * value / peak, 2),
@@ -336,9 +442,18 @@ def main():
     if args.calibrate_copy > 0:
         calibration_copy(torch, dev, args.calibrate_copy)
 
+    if (args.config == 5 and not variant and KV_LEN is None and args.calibrate_copy == 0
+            and args.causal_forward_side):
+        # the causal N=8192 forward on its own (B=1, H=32): its own inputs and
+        # timed region, reported beside the training step
+        del inputs
+        extra["causal_forward_N8192"] = causal_forward_side(args, torch, dev)
+
     cpu = None
     if args.cpu_seconds > 0:
         log("timing the fp64 CPU oracle on a sample ...")
+        if "causal_forward_N8192" in extra:
+            inputs = fi.make_inputs(cfg)
         cpu = cpu_baseline(cfg, inputs, args.cpu_seconds)
 
     workload = {1: "single-head non-causal forward", 2: "non-causal forward",
@@ -367,6 +482,51 @@ def main():
         **extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def causal_forward_side(args, torch, dev):
+    """Time fa_forward on the causal B=1, H=32, N=8192, d=128 bf16 workload
+    with resident inputs: args.warmup untimed launches, then args.steps
+    launches each bracketed by HIP events on the current stream."""
+    import numpy as np
+
+    import exact_io_aware_41_amd as fa
+    import fa_inputs as fi
+
+    cfg = fi.CONFIGS[3]
+    inputs = fi.make_inputs(cfg)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    q, k, v = up(inputs["q"]), up(inputs["k"]), up(inputs["v"])
+    del inputs
+    o = torch.empty_like(q)
+    lse = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev)
+
+    def launch():
+        fa.forward(q, k, v, scale=cfg.scale, causal=True, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        launch()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        launch()
+        b.record()
+    torch.cuda.synchronize()
+    st = timing_stats([a.elapsed_time(b) for a, b in ev])
+    flops = fi.credited_flops(cfg.B, cfg.H, cfg.N, cfg.d, True)
+    tf = flops / (st["median"] * 1e-3) / 1e12
+    target_ms = flops / (0.5 * PEAK_BF16_TFLOPS * 1e12) * 1e3
+    log(f"causal N=8192 forward: median {st['median']:.4f} ms, min {st['min']:.4f} ms, "
+        f"{tf:.1f} TFLOP/s")
+    return {"config": {"B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d, "causal": True,
+                       "dtype": "bf16"},
+            "credited_flops": flops, "launches": args.steps, "ms": st,
+            "tflops_at_median": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "target_ms_at_half_peak": round(target_ms, 4),
+            "counters": measured_mfma("fwd", 3)}
 
 
 def packed_main(args, cfg, dev):
@@ -462,11 +622,12 @@ def packed_main(args, cfg, dev):
                 sl = slice(int(cu[b]), int(cu[b + 1]))
                 w = {x: fi.widen(host[x][h:h + 1, sl][None], cfg.dtype) for x in names}
                 c0 = time.perf_counter()
-                ro, rl = oracle.attention_materialised(w["q"], w["k"], w["v"], cfg.scale,
-                                                       cfg.causal)
-                if cfg.backward:
-                    oracle.attention_backward(w["q"], w["k"], w["v"], ro, w["do"], rl, cfg.scale,
-                                              cfg.causal)
+                with blas_threads(len(os.sched_getaffinity(0))):
+                    ro, rl = oracle.attention_materialised(w["q"], w["k"], w["v"], cfg.scale,
+                                                           cfg.causal)
+                    if cfg.backward:
+                        oracle.attention_backward(w["q"], w["k"], w["v"], ro, w["do"], rl,
+                                                  cfg.scale, cfg.causal)
                 elapsed += time.perf_counter() - c0
                 done_f += fi.useful_flops(1, 1, int(n), cfg.d, cfg.causal)
                 if cfg.backward:
@@ -476,14 +637,9 @@ def packed_main(args, cfg, dev):
                     break
             if elapsed >= args.cpu_seconds:
                 break
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max((i.get("num_threads", 1) for i in threadpool_info()
-                           if i.get("user_api") == "blas"), default=1)
-        except Exception:  # noqa: BLE001 - report what we can
-            threads = 1
+        threads, model = host_cpu()
         cpu = {"value": done_f / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": model,
                "sample": f"{done} (sequence, head) pairs of {len(lens) * cfg.H}, "
                          f"{elapsed:.1f} s", "seconds": round(elapsed, 2)}
 
@@ -581,20 +737,16 @@ def decode_main(args):
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max((i.get("num_threads", 1) for i in threadpool_info()
-                           if i.get("user_api") == "blas"), default=1)
-        except ImportError:
-            threads = 1
+        threads, model = host_cpu()
         qw, kw, vw = (fi.widen(inputs[n], "bf16") for n in ("q", "k", "v"))
         done_bytes, t_cpu, heads = 0, 0.0, 0
         for b in range(B):
             for h in range(H):
                 sub = None if lengths is None else lengths[b:b + 1]
                 t1 = time.perf_counter()
-                oracle.attention_decode(qw[b:b + 1, h:h + 1], kw[b:b + 1, h:h + 1],
-                                        vw[b:b + 1, h:h + 1], cfg.scale, sub)
+                with blas_threads(len(os.sched_getaffinity(0))):
+                    oracle.attention_decode(qw[b:b + 1, h:h + 1], kw[b:b + 1, h:h + 1],
+                                            vw[b:b + 1, h:h + 1], cfg.scale, sub)
                 t_cpu += time.perf_counter() - t1
                 done_bytes += fi.decode_bytes(1, 1, N, d, 2, sub)
                 heads += 1
@@ -603,7 +755,7 @@ def decode_main(args):
             if t_cpu >= args.cpu_seconds:
                 break
         cpu = {"value": round(done_bytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": model,
                "sample": f"{heads} of {B * H} heads (fp64 decode, one score row each), "
                          f"{t_cpu:.1f} s", "seconds": round(t_cpu, 2)}
 

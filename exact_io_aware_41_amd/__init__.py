@@ -227,6 +227,14 @@ def _check_keys(name, t, k, q):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_q_k(q, k):
+    """q [B, H, Nq, d] and k [B, H, Nk, d], q dense: the kernels index q as a
+    contiguous row-major tensor, so a strided view must be rejected here."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d] and k [B, H, Nk, d]")
+    _check_like("q", q, q)
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -255,9 +263,7 @@ def forward(q, k, v, scale=None, causal=False, seqlens_k=None, out=None, lse=Non
     Returns (o, lse) with o like q and lse fp32 [B, H, Nq].
     """
     import torch
-    if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("q must be [B, H, Nq, d] and k [B, H, Nk, d]")
-    _check_like("q", q, q)
+    _check_q_k(q, k)
     for name, t in (("k", k), ("v", v)):
         _check_keys(name, t, k, q)
     B, H, N, d = q.shape
@@ -284,6 +290,7 @@ def backward(q, k, v, o, do, lse, scale=None, causal=False, seqlens_k=None,
     """dQ, dK, dV of <dO, O> for the tensors of a previous ``forward`` call
     (q, o, do, dq [B, H, Nq, d]; k, v, dk, dv [B, H, Nk, d])."""
     import torch
+    _check_q_k(q, k)
     for name, t in (("o", o), ("do", do)):
         _check_like(name, t, q)
     for name, t in (("k", k), ("v", v)):
@@ -443,6 +450,7 @@ def backward_phases(q, k, v, o, do, lse, scale=None, causal=False, seqlens_k=Non
     launch can be timed on the stream it runs on.
     """
     import torch
+    _check_q_k(q, k)
     for name, t in (("o", o), ("do", do)):
         _check_like(name, t, q)
     for name, t in (("k", k), ("v", v)):
@@ -458,8 +466,13 @@ def backward_phases(q, k, v, o, do, lse, scale=None, causal=False, seqlens_k=Non
     _check_like("dq", dq, q)
     for name, t in (("dk", dk), ("dv", dv)):
         _check_keys(name, t, k, q)
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
     if delta is None:
         delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if (delta.shape != (B, H, N) or delta.dtype != torch.float32 or delta.device != q.device
+            or not delta.is_contiguous()):
+        raise ValueError("delta must be a contiguous fp32 [B, H, N] tensor on q's device")
     code = _dtype_code(q)
     stream = _stream(q.device)
     rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)

@@ -103,6 +103,14 @@ struct EltBf16 {
     lo = __uint_as_float(w << 16);
     hi = __uint_as_float(w & 0xffff0000u);
   }
+  // acc + x[j] + x[j + 1] in fp32 (v_dot2c_f32_bf16 against (1, 1): the
+  // products are exact, the sum is an fp32 accumulation)
+  static __device__ __forceinline__ float sum2(V8 x, int j, float acc) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 v2;
+    const v2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    const v2 pair = {x[j], x[j + 1]};
+    return __builtin_amdgcn_fdot2_f32_bf16(pair, one, acc, false);
+  }
 };
 struct EltF16 {
   using T = _Float16;
@@ -115,6 +123,13 @@ struct EltF16 {
   static __device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi) {
     lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
     hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+  // acc + x[j] + x[j + 1] in fp32 (v_dot2c_f32_f16 against (1, 1))
+  static __device__ __forceinline__ float sum2(V8 x, int j, float acc) {
+    typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 v2;
+    const v2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    const v2 pair = {x[j], x[j + 1]};
+    return __builtin_amdgcn_fdot2(pair, one, acc, false);
   }
 };
 

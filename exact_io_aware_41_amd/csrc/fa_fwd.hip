@@ -370,22 +370,24 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
       scale_o |= upd && (m[qb] != kNegInf);
       m[qb] = m_new;
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      // the row sum accumulates the fp32 weights (the LSE the backward relies
-      // on stays exact to fp32 rounding); P^T is rounded to bf16 for the MFMA
-      float rs0 = 0.f, rs1 = 0.f;
+      // P^T is rounded to the 16-bit format for the MFMA, and the row sum
+      // adds exactly those rounded weights (in fp32, two per instruction), so
+      // O = o / l is a combination of the values whose weights sum to one: a
+      // weight's rounding then moves O only through its difference from the
+      // other values, never by a common factor
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int g = 0; g < C::NG; ++g) {
         elt8 pk;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p =
-              fast_exp2(__builtin_fmaf(sacc[g >> 1][qb][8 * (g & 1) + i], scale_log2, -m_use));
-          if (i & 1) rs1 += p; else rs0 += p;
-          pk[i] = E::cvt(p);
-        }
+        for (int i = 0; i < 8; ++i)
+          pk[i] = E::cvt(
+              fast_exp2(__builtin_fmaf(sacc[g >> 1][qb][8 * (g & 1) + i], scale_log2, -m_use)));
         pf[g][qb] = pk;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) rs[j / 2] = E::sum2(pk, j, rs[j / 2]);
       }
-      l[qb] = l[qb] * alpha[qb] + (rs0 + rs1);
+      l[qb] = l[qb] * alpha[qb] + ((rs[0] + rs[1]) + (rs[2] + rs[3]));
     }
     // the O accumulators move only when some lane's maximum jumped
     if (__builtin_amdgcn_ballot_w64(scale_o) != 0) {

@@ -31,10 +31,12 @@
  *  - lse is fp32 [B][H][N]: the natural-log log-sum-exp of the visible scaled
  *    scores of each query row, LSE_i = m_i + ln(l_i).
  *  - Scores are s_ij = scale * q_i . k_j.  A pair (i, j) of sequence b is
- *    visible iff j < L_b and (causal == 0 or j <= i), with absolute positions
- *    i, j in [0, N).  L_b = seqlens_k[b] clamped to [0, N], or N when
- *    seqlens_k is NULL.  Query rows are never masked: row i >= L_b still
- *    attends to keys 0..L_b-1.
+ *    visible iff j < L_b and (causal == 0 or j <= i + Nk - Nq), with absolute
+ *    positions i in [0, Nq) and j in [0, Nk): the pages state the causal mask
+ *    j <= i for Nq = Nk, and with Nq != Nk the queries are the last Nq
+ *    positions of the sequence.  L_b = seqlens_k[b] clamped to [0, Nk], or
+ *    Nk when seqlens_k is NULL.  Query rows are never masked: row i still
+ *    attends to the keys below L_b that the causal mask allows.
  *  - A row with no visible key gets O = 0 and LSE = -inf (explicit empty-row
  *    policy); its gradients are 0.
  *  - Every pointer is a device pointer owned by the caller.  The library

@@ -159,25 +159,59 @@ def attention_rows(q_head, k_head, v_head, rows, scale, causal=False, length=Non
 # Route B: the online recurrence
 # ---------------------------------------------------------------------------
 
+def _fold_chunk(m, l, o, s, v, *, subtract_max=True, rescale=True):
+    """Fold one chunk of keys into the running state of a set of rows.
+
+    The state update of [infra] "Keep only the state needed for the final
+    weighted average" (and [deep] "Why it is allowed to be exact"), for R
+    rows at once: m (R,) running maxima, l (R,) running sums of exponentials
+    relative to m, o (R, dv) value sums on the same scale; s (R, c) the
+    chunk's scaled scores with -inf at keys a row does not see, v (c, dv)
+    the chunk's value rows.  A row that sees no key of the chunk keeps its
+    state (its factor is 1 and nothing is added), so -inf - (-inf) is never
+    formed ([infra] "Executable recurrence, with an empty-state policy").
+
+    `subtract_max` / `rescale` = False plant the two classic mistakes for the
+    negative tests: the reference stays 0 instead of the running maximum, or
+    the old sums are not multiplied by exp(m_old - m_new).
+
+    Returns (m, l, o, factor, seen): the new state, the factor the old sums
+    were multiplied by, and which rows saw a key in this chunk.
+    """
+    dt = l.dtype.type
+    seen = np.any(~np.isneginf(s), axis=1)
+    if subtract_max:
+        ref = np.maximum(m, np.max(s, axis=1, initial=-np.inf))
+    else:
+        ref = np.zeros_like(m)
+    ref = np.where(seen, ref, m)
+    was_empty = np.isneginf(m)
+    safe_gap = np.where(seen & ~was_empty, m - ref, dt(0.0))
+    if rescale:
+        factor = np.where(was_empty, dt(0.0), np.exp(safe_gap))
+    else:
+        factor = np.ones_like(l)
+    factor = np.where(seen, factor, dt(1.0))
+    safe_ref = np.where(seen, ref, dt(0.0))
+    w = np.where(np.isneginf(s), dt(0.0), np.exp(s - safe_ref[:, None]))
+    o_new = factor[:, None] * o + (w @ v).astype(o.dtype)
+    l_new = factor * l + w.sum(axis=1, dtype=l.dtype)
+    return ref.astype(m.dtype), l_new, o_new, factor, seen
+
+
 def online_row(scores, values, tile=2, *, dtype=np.float64,
                subtract_max=True, rescale=True, return_state=False):
     """Online softmax-weighted average of value rows for ONE query.
 
-    Re-written from the description of the recurrence in [infra] "Keep only
-    the state needed for the final weighted average" and the policy of
-    [infra] "Executable recurrence, with an empty-state policy":
-      * the state is (m, l, o): running maximum, running sum of exponentials
-        relative to m, and the value sum on the same scale;
-      * for each chunk of `tile` scores: m_new = max(m, max(chunk));
-        alpha = exp(m - m_new) (0 while the state is empty);
-        l = alpha*l + sum(exp(chunk - m_new)); o = alpha*o + exp(chunk - m_new) @ V;
-      * a chunk whose scores are all -inf (fully masked) is skipped, so
-        -inf - (-inf) is never evaluated;
-      * the result is o / l, or zeros when nothing was visible.
+    The single-row case of the state update `_fold_chunk` (the same update
+    `attention_online` applies to every row of a head), run over consecutive
+    chunks of `tile` scores; the result is o / l, or zeros when no score was
+    visible ([infra] "Executable recurrence, with an empty-state policy").
 
-    `scores` are already scaled and masked (-inf for masked keys).  Inputs
-    are validated as the page's reference does: one score per value row,
-    a positive integer tile, no NaN or +inf scores, finite values.
+    `scores` are already scaled and masked (-inf for masked keys).  The
+    inputs must be well formed as that page requires: a positive integer
+    tile, a 1-D score vector with one entry per row of a 2-D value matrix,
+    scores finite or -inf, values finite.
 
     `subtract_max` and `rescale` exist ONLY so that negative tests can plant
     the two classic mistakes ([deep] "Why it is allowed to be exact": drop
@@ -186,45 +220,38 @@ def online_row(scores, values, tile=2, *, dtype=np.float64,
     (float64 by default; float32 for the overflow demonstration).
 
     Returns the output vector, or (output, trace) with return_state=True,
-    where trace lists (m, alpha, l, o) after every processed chunk.
+    where trace lists (m, factor, l, o) after every chunk that held a visible
+    score.
     """
-    scores = np.asarray(scores, dtype=np.float64)
-    values = np.asarray(values, dtype=np.float64)
-    if scores.ndim != 1 or values.ndim != 2 or scores.shape[0] != values.shape[0]:
-        raise ValueError("need exactly one score per value row")
-    if not isinstance(tile, int) or isinstance(tile, bool) or tile <= 0:
+    if type(tile) is not int or tile < 1:
         raise ValueError("tile must be a positive int")
-    if np.any(np.isnan(scores)) or np.any(np.isposinf(scores)):
+    s_row = np.asarray(scores, dtype=np.float64)
+    vals = np.asarray(values, dtype=np.float64)
+    if vals.ndim != 2 or s_row.shape != (vals.shape[0],):
+        raise ValueError("need exactly one score per value row")
+    if np.isnan(s_row).any() or (s_row == np.inf).any():
         raise ValueError("scores must be finite or -inf")
-    if not np.all(np.isfinite(values)):
+    if not np.isfinite(vals).all():
         raise ValueError("values must be finite")
 
-    f = np.dtype(dtype).type
-    s_all = scores.astype(dtype)
-    v_all = values.astype(dtype)
-    m = f(-np.inf)
-    l = f(0.0)
-    o = np.zeros(values.shape[1], dtype)
+    dt = np.dtype(dtype).type
+    s_row = s_row.astype(dtype)
+    vals = vals.astype(dtype)
+    m = np.full(1, -np.inf, dtype)
+    l = np.zeros(1, dtype)
+    o = np.zeros((1, vals.shape[1]), dtype)
     trace = []
+    n = s_row.shape[0]
     with np.errstate(over="ignore", invalid="ignore"):
-        for start in range(0, s_all.shape[0], tile):
-            s = s_all[start:start + tile]
-            chunk_max = s.max()
-            if np.isneginf(chunk_max):
-                continue                      # fully masked chunk: state unchanged
-            m_new = max(m, chunk_max) if subtract_max else f(0.0)
-            if not rescale:
-                alpha = f(1.0)
-            elif np.isneginf(m):
-                alpha = f(0.0)                # empty state: nothing to rescale
-            else:
-                alpha = np.exp(m - m_new, dtype=dtype)
-            w = np.exp(s - m_new, dtype=dtype)
-            o = alpha * o + (w @ v_all[start:start + tile]).astype(dtype)
-            l = alpha * l + w.sum(dtype=dtype)
-            m = m_new
-            trace.append((float(m), float(alpha), float(l), o.astype(np.float64).copy()))
-        out = o / l if l != 0 else np.zeros_like(o)
+        for c0 in range(0, n, tile):
+            c1 = min(n, c0 + tile)
+            m, l, o, factor, seen = _fold_chunk(
+                m, l, o, s_row[None, c0:c1], vals[c0:c1],
+                subtract_max=subtract_max, rescale=rescale)
+            if seen[0]:
+                trace.append((float(m[0]), float(factor[0]), float(l[0]),
+                              o[0].astype(np.float64).copy()))
+        out = o[0] / l[0] if l[0] != dt(0.0) else np.zeros_like(o[0])
     if return_state:
         return out.astype(np.float64), trace
     return out.astype(np.float64)
@@ -234,17 +261,17 @@ def attention_online(q, k, v, scale, causal=False, lengths=None, tile=64,
                      return_state=False):
     """Route B: the online recurrence over key chunks of width `tile`.
 
-    Vectorised over all query rows of a head; for each row the state (m, l, o)
-    follows [infra] "Keep only the state needed for the final weighted
-    average" and [deep] "Why it is allowed to be exact" (rescale both sums by
-    exp(m_old - m_new), divide by l after the last chunk).  Rows for which a
-    chunk is fully masked keep their state ([infra] "Executable recurrence,
-    with an empty-state policy").  Shares no code with route A beyond the
-    mask and score helpers.
+    Vectorised over all query rows of a head; each chunk is folded into the
+    per-row state (m, l, o) by `_fold_chunk` ([infra] "Keep only the state
+    needed for the final weighted average"; [deep] "Why it is allowed to be
+    exact": rescale both sums by exp(m_old - m_new), divide by l after the
+    last chunk).  Rows for which a chunk is fully masked keep their state
+    ([infra] "Executable recurrence, with an empty-state policy").  Shares
+    no code with route A beyond the mask and score helpers.
 
     Returns (o, lse) or, with return_state=True, (o, lse, m, l).
     """
-    if not isinstance(tile, int) or isinstance(tile, bool) or tile <= 0:
+    if type(tile) is not int or tile < 1:
         raise ValueError("tile must be a positive int")
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -263,22 +290,15 @@ def attention_online(q, k, v, scale, causal=False, lengths=None, tile=64,
             l = np.zeros(N)
             o = np.zeros((N, v.shape[3]))
             for j0 in range(0, Nk, tile):
-                cols = slice(j0, min(Nk, j0 + tile))
-                vis = visible_mask(rows, Nk, causal, length,
-                                   keys=np.arange(j0, min(Nk, j0 + tile)), offset=Nk - N)
+                keys = np.arange(j0, min(Nk, j0 + tile))
+                vis = visible_mask(rows, Nk, causal, length, keys=keys, offset=Nk - N)
                 live = vis.any(axis=1)            # rows with something visible here
                 if not live.any():
                     continue
-                s = scaled_scores(q[b, h, live], k[b, h, cols], scale)
-                s = np.where(vis[live], s, -np.inf)
-                m_old = m[live]
-                m_new = np.maximum(m_old, s.max(axis=1))
-                alpha = np.where(np.isneginf(m_old), 0.0,
-                                 np.exp(np.where(np.isneginf(m_old), 0.0, m_old - m_new)))
-                w = np.where(vis[live], np.exp(s - m_new[:, None]), 0.0)
-                o[live] = alpha[:, None] * o[live] + w @ v[b, h, cols]
-                l[live] = alpha * l[live] + w.sum(axis=1)
-                m[live] = m_new
+                s = np.where(vis[live], scaled_scores(q[b, h, live], k[b, h, keys], scale),
+                             -np.inf)
+                m[live], l[live], o[live], _, _ = _fold_chunk(m[live], l[live], o[live], s,
+                                                             v[b, h, keys])
             done = l > 0
             O[b, h, done] = o[done] / l[done, None]
             LSE[b, h] = np.where(done, m + np.log(np.where(done, l, 1.0)), -np.inf)

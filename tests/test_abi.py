@@ -234,6 +234,26 @@ def test_torch_wrappers_validate_before_calling():
         fa.forward(b, b.float(), b)
 
 
+def test_backward_wrappers_reject_strided_q():
+    """A q view that is not dense (here sliced along N from a larger buffer)
+    must be refused before any launch, even when every other tensor and dq
+    are dense: the kernels index q as a contiguous [B][H][N][d] tensor."""
+    torch = pytest.importorskip("torch")
+    big = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16)
+    q = big[:, :, ::2]
+    dense = torch.zeros(1, 1, 4, 128, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 4, dtype=torch.float32)
+    assert not q.is_contiguous() and q.shape == dense.shape
+    for fn in (fa.backward, fa.backward_phases):
+        with pytest.raises(ValueError, match="q must be contiguous"):
+            fn(q, dense, dense, dense, dense, lse, dq=dense.clone(), dk=dense.clone(),
+               dv=dense.clone())
+        with pytest.raises(ValueError):
+            fn(dense[0], dense[0], dense[0], dense[0], dense[0], lse)
+    with pytest.raises(ValueError, match="delta"):
+        fa.backward_phases(dense, dense, dense, dense, dense, lse, delta=lse[0])
+
+
 def test_backward_phase_entry_points_validate():
     pre = lambda o=A, do=A, delta=A, **kw: fa.fa_backward_preprocess(
         kw.get("dtype", BF16), kw.get("B", 1), kw.get("H", 1), kw.get("N", 16), kw.get("d", 128),

@@ -17,15 +17,12 @@ import pytest
 
 import fa_inputs as fi
 import oracle
-from tests.gpu_helpers import (check_lse, from_device, lib, log_case, max_abs, to_device,
-                               torch_cuda)
+from tests.gpu_helpers import (LSE_TOL, check_lse, from_device, grad_bound, lib, log_case,
+                               max_abs, to_device, torch_cuda)
 
 pytestmark = pytest.mark.gpu
 
 O_TOL = {"bf16": 2e-2, "f16": 5e-3, "f32": 1e-5}
-G_TOL = {"bf16": 5e-2, "f16": 2e-2, "f32": 1e-4}
-ULP = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -20}
-LSE_TOL = {"bf16": (1e-3, 1e-5), "f16": (1e-3, 1e-5), "f32": (1e-5, 0.0)}
 
 SHAPES = [(1, 300), (7, 129), (65, 300), (200, 64), (300, 65), (129, 1), (64, 256)]
 
@@ -76,7 +73,7 @@ def test_rectangular_forward_and_backward(dtype, d, causal):
             for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
                 g = from_device(got, dtype)
                 assert not np.any(np.isnan(g)), name
-                bound = G_TOL[dtype] + ULP[dtype] * np.abs(ref)
+                bound = grad_bound(ref, dtype)
                 assert np.all(np.abs(g - ref) <= bound), \
                     f"{name} Nq={Nq} Nk={Nk} err {max_abs(g, ref):.3e}"
 
@@ -94,7 +91,7 @@ def test_rectangular_d256_backward(dtype):
                                                cfg.scale, True)
         for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
             g = from_device(got, dtype)
-            assert np.all(np.abs(g - ref) <= G_TOL[dtype] + ULP[dtype] * np.abs(ref))
+            assert np.all(np.abs(g - ref) <= grad_bound(ref, dtype))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
