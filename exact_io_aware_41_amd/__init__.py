@@ -22,6 +22,8 @@ import os
 
 __all__ = [
     "FA_SUCCESS", "FA_ERROR_INVALID_VALUE", "FA_ERROR_UNSUPPORTED", "FA_ERROR_LAUNCH",
+    "FA_ERROR_SCRATCH_LIMIT", "FA_NOALLOC_SCRATCH_BYTES", "fa_backward_noalloc",
+    "backward_noalloc",
     "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "EXPORTED_SYMBOLS",
     "FAError", "FALibraryMissing", "LIB_PATH", "load_library",
     "fa_abi_version", "fa_status_string", "fa_forward", "fa_backward",
@@ -35,6 +37,7 @@ FA_SUCCESS = 0
 FA_ERROR_INVALID_VALUE = 1
 FA_ERROR_UNSUPPORTED = 2
 FA_ERROR_LAUNCH = 3
+FA_ERROR_SCRATCH_LIMIT = 4
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
 FA_DTYPE_F16 = 2
@@ -43,7 +46,11 @@ EXPORTED_SYMBOLS = ("fa_abi_version", "fa_status_string", "fa_forward",
                     "fa_backward_workspace_size", "fa_backward", "fa_backward_preprocess",
                     "fa_backward_dkdv", "fa_backward_dq", "fa_forward_fp8", "fa_forward_varlen",
                     "fa_backward_varlen", "fa_decode_workspace_size", "fa_decode",
-                    "fa_merge_states")
+                    "fa_merge_states", "fa_backward_noalloc")
+
+# bytes of the static workspace fa_backward_noalloc uses on each GPU (one
+# fp32 per query row of the batch)
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_mi355x.so")
 
@@ -84,6 +91,9 @@ def load_library():
     lib.fa_backward.restype = i32
     lib.fa_backward.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32,
                                 i32, vp, vp, vp, vp, sz, vp]
+    lib.fa_backward_noalloc.restype = i32
+    lib.fa_backward_noalloc.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                        f32, i32, vp, vp, vp, vp]
     lib.fa_backward_preprocess.restype = i32
     lib.fa_backward_preprocess.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.fa_backward_dkdv.restype = i32
@@ -138,6 +148,12 @@ def fa_backward(dtype, B, H, Nq, Nk, d, q, k, v, o, dout, lse, seqlens_k, scale,
     return load_library().fa_backward(dtype, B, H, Nq, Nk, d, q, k, v, o, dout, lse, seqlens_k,
                                       scale, causal, dq, dk, dv, workspace, workspace_bytes,
                                       stream)
+
+
+def fa_backward_noalloc(dtype, B, H, Nq, Nk, d, q, k, v, o, dout, lse, seqlens_k, scale, causal,
+                        dq, dk, dv, stream=0) -> int:
+    return load_library().fa_backward_noalloc(dtype, B, H, Nq, Nk, d, q, k, v, o, dout, lse,
+                                              seqlens_k, scale, causal, dq, dk, dv, stream)
 
 
 def fa_backward_preprocess(dtype, B, H, N, d, o, dout, delta, stream=0) -> int:
@@ -318,6 +334,32 @@ def backward(q, k, v, o, do, lse, scale=None, causal=False, seqlens_k=None,
                      _stream(q.device))
     if st != FA_SUCCESS:
         raise FAError(st, "fa_backward")
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False,
+                     seqlens_k=None):
+    """``backward`` through fa_backward_noalloc: the caller supplies every
+    output, nothing is allocated (the workspace is the library's static
+    per-GPU array); returns (dq, dk, dv)."""
+    import torch
+    _check_q_k(q, k)
+    for name, t in (("o", o), ("do", do), ("dq", dq)):
+        _check_like(name, t, q)
+    for name, t in (("k", k), ("v", v), ("dk", dk), ("dv", dv)):
+        _check_keys(name, t, k, q)
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    seqlens_k = _lengths(seqlens_k, q)
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    st = fa_backward_noalloc(_dtype_code(q), B, H, N, Nk, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                             _ptr(do), _ptr(lse), _ptr(seqlens_k), float(scale),
+                             int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), _stream(q.device))
+    if st != FA_SUCCESS:
+        raise FAError(st, "fa_backward_noalloc")
     return dq, dk, dv
 
 

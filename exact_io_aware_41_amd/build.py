@@ -24,7 +24,7 @@ LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_f32.hip", "fa_decode.hip",
-           "fa_fwd_fp8.hip"]
+           "fa_fwd_fp8.hip", "fa_noalloc.hip"]
 # per-source code-generation options (none at present)
 EXTRA_FLAGS: dict[str, list[str]] = {}
 ARCH = "gfx950"

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr long long kMaxGrid = 0x7fffffffLL;
 // one head's rows of one sequence must be addressable with 32-bit byte
 // offsets (the kernels' buffer descriptors)
@@ -93,6 +93,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERROR_INVALID_VALUE: return "FA_ERROR_INVALID_VALUE";
     case FA_ERROR_UNSUPPORTED: return "FA_ERROR_UNSUPPORTED";
     case FA_ERROR_LAUNCH: return "FA_ERROR_LAUNCH";
+    case FA_ERROR_SCRATCH_LIMIT: return "FA_ERROR_SCRATCH_LIMIT";
   }
   return "FA_ERROR_UNKNOWN";
 }

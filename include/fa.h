@@ -42,7 +42,9 @@
  *  - Every pointer is a device pointer owned by the caller.  The library
  *    allocates and frees nothing, keeps no state between calls, and only
  *    enqueues work on `stream` (calls return without synchronising).  Calls
- *    are re-entrant.  Outputs must not alias inputs.
+ *    are re-entrant.  Outputs must not alias inputs.  The one exception is
+ *    fa_backward_noalloc, whose workspace is a static device array of the
+ *    library shared by every call on a GPU (see there).
  *  - Data pointers must be 16-byte aligned.
  *  - Inputs must be finite; NaN or infinite inputs propagate unchecked.  Key
  *    and value rows at or past a sequence's key length are never read, so
@@ -63,6 +65,8 @@
  *  FA_ERROR_LAUNCH         the HIP runtime reported an error when the kernel
  *                          was enqueued (hipGetLastError).  Faults inside a
  *                          kernel surface at the caller's next synchronise.
+ *  FA_ERROR_SCRATCH_LIMIT  fa_backward_noalloc only: the problem needs more
+ *                          workspace than the library's static array holds.
  *
  * Compiled (dtype, d) set:
  *  forward : FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128, 256}
@@ -91,7 +95,9 @@ typedef enum {
   FA_SUCCESS = 0,
   FA_ERROR_INVALID_VALUE = 1,
   FA_ERROR_UNSUPPORTED = 2,
-  FA_ERROR_LAUNCH = 3
+  FA_ERROR_LAUNCH = 3,
+  FA_ERROR_SCRATCH_LIMIT = 4 /* fa_backward_noalloc: the problem needs more
+                                than FA_NOALLOC_SCRATCH_BYTES of scratch  */
 } fa_status;
 
 typedef enum {
@@ -229,6 +235,32 @@ fa_status fa_backward_dq(fa_dtype dtype, int B, int H, int Nq, int Nk, int d,
                          const void* dout, const float* lse, const float* delta,
                          const int32_t* seqlens_k, float scale, int causal,
                          void* dq, hipStream_t stream);
+
+/*
+ * fa_backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * must not call hipMalloc, harnesses that forbid allocation).  The workspace
+ * fa_backward takes (one fp32 per query row, fa_backward_workspace_size
+ * bytes) lives instead in a static device array of the library,
+ * FA_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held from the library's first
+ * use of that GPU until the process ends.  This call allocates nothing and
+ * calls no allocating routine; it uses the copy of the array on the calling
+ * thread's current device, so `stream` must belong to that device.
+ *
+ * Arguments, layouts, results and the other errors are those of fa_backward
+ * (same kernels, bit-identical outputs).  Limit: B * H * Nq <= 8,388,608
+ * query rows; a larger problem returns FA_ERROR_SCRATCH_LIMIT before any HIP
+ * call.  Every call on one GPU shares that GPU's array and it keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that overlap
+ * on one GPU, on different streams or host threads, race on it and must be
+ * serialised by the caller.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+fa_status fa_backward_noalloc(fa_dtype dtype, int B, int H, int Nq, int Nk, int d,
+                              const void* q, const void* k, const void* v,
+                              const void* o, const void* dout, const float* lse,
+                              const int32_t* seqlens_k, float scale, int causal,
+                              void* dq, void* dk, void* dv, hipStream_t stream);
 
 /*
  * Packed batches: B sequences of different lengths stored back to back

@@ -41,12 +41,43 @@ def test_header_declarations_are_exported():
 
 
 def test_version_and_status_strings():
-    assert fa.fa_abi_version() == 4
+    assert fa.fa_abi_version() == 5
     assert fa.fa_status_string(fa.FA_SUCCESS) == "FA_SUCCESS"
     assert fa.fa_status_string(fa.FA_ERROR_INVALID_VALUE) == "FA_ERROR_INVALID_VALUE"
     assert fa.fa_status_string(fa.FA_ERROR_UNSUPPORTED) == "FA_ERROR_UNSUPPORTED"
     assert fa.fa_status_string(fa.FA_ERROR_LAUNCH) == "FA_ERROR_LAUNCH"
+    assert fa.fa_status_string(fa.FA_ERROR_SCRATCH_LIMIT) == "FA_ERROR_SCRATCH_LIMIT"
     assert fa.fa_status_string(99) == "FA_ERROR_UNKNOWN"
+
+
+def test_library_imports_no_allocation_routine():
+    """No entry point can allocate device or host memory: the library does
+    not even import the HIP allocation routines."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", fa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    names = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    alloc = {n for n in names if re.match(r"hip(Ext)?(Host)?(Malloc|Free|MemAlloc|HostAlloc|"
+                                          r"MallocManaged|MallocAsync|FreeAsync|HostRegister)", n)}
+    assert not alloc, alloc
+    assert "hipGetSymbolAddress" in names
+
+
+def noalloc(dtype=BF16, B=1, H=1, N=16, d=128, Nk=None, scale=0.1, causal=0, p=A):
+    Nk = N if Nk is None else Nk
+    return fa.fa_backward_noalloc(dtype, B, H, N, Nk, d, p, p, p, p, p, p, None, scale, causal,
+                                  p, p, p, None)
+
+
+def test_backward_noalloc_limits_without_a_gpu():
+    """Checks that run before any HIP call: a problem whose row statistics
+    exceed the static workspace is refused, an empty one succeeds."""
+    rows = fa.FA_NOALLOC_SCRATCH_BYTES // 4
+    assert rows == 8 * 32 * 32768
+    assert noalloc(B=1, H=1, N=rows + 1) == fa.FA_ERROR_SCRATCH_LIMIT
+    assert noalloc(B=8, H=32, N=32768 + 1) == fa.FA_ERROR_SCRATCH_LIMIT
+    assert noalloc(B=0) == fa.FA_SUCCESS
+    assert noalloc(H=0) == fa.FA_SUCCESS
+    assert noalloc(N=0, Nk=0) == fa.FA_SUCCESS
 
 
 def fwd(dtype=BF16, B=1, H=1, N=16, d=128, q=A, k=A, v=A, lens=None, scale=0.1, causal=0, o=A,
