@@ -16,6 +16,7 @@ raises ``FALibraryMissing``; build it with ``python -m exact_io_aware_41_amd.bui
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -25,7 +26,8 @@ __all__ = [
     "FA_ERROR_SCRATCH_LIMIT", "FA_NOALLOC_SCRATCH_BYTES", "fa_backward_noalloc",
     "backward_noalloc",
     "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "EXPORTED_SYMBOLS",
-    "FAError", "FALibraryMissing", "LIB_PATH", "load_library",
+    "FAError", "FALibraryMissing", "LIB_PATH", "DEBUG_LIB_PATH", "load_library",
+    "load_debug_library", "library",
     "fa_abi_version", "fa_status_string", "fa_forward", "fa_backward",
     "fa_backward_workspace_size", "fa_backward_preprocess", "fa_backward_dkdv",
     "fa_backward_dq", "fa_forward_fp8", "fa_forward_varlen", "fa_backward_varlen", "fa_decode_workspace_size",
@@ -53,6 +55,9 @@ EXPORTED_SYMBOLS = ("fa_abi_version", "fa_status_string", "fa_forward",
 FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_mi355x.so")
+# the same library built with the race-check switches (NaN-poisoned LDS copy
+# destinations, scrambled work-group order); for tests only
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_mi355x_debug.so")
 
 _lib = None
 
@@ -74,10 +79,33 @@ def load_library():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    _lib = _open(LIB_PATH)
+    return _lib
+
+
+def load_debug_library():
+    """The race-check build of the library (a separate handle; the torch
+    wrappers use it inside ``with library(handle):``)."""
+    return _open(DEBUG_LIB_PATH)
+
+
+@contextlib.contextmanager
+def library(handle):
+    """Route every call of this module to `handle` inside the block."""
+    global _lib
+    old = load_library()
+    _lib = handle
+    try:
+        yield handle
+    finally:
+        _lib = old
+
+
+def _open(path):
+    if not os.path.exists(path):
         raise FALibraryMissing(
-            f"{LIB_PATH} is not built; run `python -m exact_io_aware_41_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+            f"{path} is not built; run `python -m exact_io_aware_41_amd.build`")
+    lib = ctypes.CDLL(path)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_abi_version.restype = i32
     lib.fa_abi_version.argtypes = []
@@ -117,7 +145,6 @@ def load_library():
     lib.fa_decode.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
     lib.fa_merge_states.restype = i32
     lib.fa_merge_states.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
-    _lib = lib
     return lib
 
 

@@ -22,6 +22,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# the same sources built with the race-check switches: LDS copy destinations
+# poisoned with NaN before every copy, work-group ids visited in a scrambled
+# order (tests compare it bit for bit with the default library)
+DEBUG_LIB_NAME = "libfa_mi355x_debug.so"
+DEBUG_LIB_PATH = os.path.join(PKG, DEBUG_LIB_NAME)
+DEBUG_FLAGS = ["-DFA_LDS_POISON=1", "-DFA_WG_PERMUTE=1"]
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_f32.hip", "fa_decode.hip",
            "fa_fwd_fp8.hip", "fa_noalloc.hip"]
@@ -59,28 +65,33 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link the shared library.
+    """Compile every source for gfx950 and link the library, and the same
+    sources with the race-check switches into the debug library.
 
-    Always recompiles.  The library is written to a temporary name and moved
+    Always recompiles.  Each library is written to a temporary name and moved
     into place, so a concurrent reader never sees a partial file.
     """
     cc = hipcc()
+    variants = [(LIB_NAME, LIB_PATH, []), (DEBUG_LIB_NAME, DEBUG_LIB_PATH, DEBUG_FLAGS)]
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
-        objs = []
         cmds = []
-        for src in SOURCES:
-            obj = os.path.join(tmp, src + ".o")
-            lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmds.append([cc, *common_flags(), *EXTRA_FLAGS.get(src, []), *lang, "-c",
-                         os.path.join(CSRC, src), "-o", obj])
-            objs.append(obj)
-        with ThreadPoolExecutor(len(cmds)) as ex:
+        objs = {name: [] for name, _, _ in variants}
+        for name, _, flags in variants:
+            for src in SOURCES:
+                obj = os.path.join(tmp, f"{name}.{src}.o")
+                lang = ["-x", "hip"] if src.endswith(".hip") else []
+                cmds.append([cc, *common_flags(), *flags, *EXTRA_FLAGS.get(src, []), *lang, "-c",
+                             os.path.join(CSRC, src), "-o", obj])
+                objs[name].append(obj)
+        with ThreadPoolExecutor(min(len(cmds), os.cpu_count() or 4)) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))
-        tmp_lib = os.path.join(tmp, LIB_NAME)
-        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], verbose)
-        staged = LIB_PATH + ".tmp"
-        shutil.copyfile(tmp_lib, staged)
-        os.replace(staged, LIB_PATH)
+        for name, path, _ in variants:
+            tmp_lib = os.path.join(tmp, name)
+            _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs[name], "-o", tmp_lib],
+                 verbose)
+            staged = path + ".tmp"
+            shutil.copyfile(tmp_lib, staged)
+            os.replace(staged, path)
     return LIB_PATH
 
 

@@ -139,9 +139,10 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
   const int pr = wave % C::NP;   // key block of the pair
   const int half = wave / C::NP; // query half for S/dP, feature half for dK/dV
 
-  const int bh_count = B * H;
-  const int kt = blockIdx.x / bh_count;
-  const int bh = blockIdx.x - kt * bh_count;
+  // key tiles longest first: the first key tile is seen by the most queries
+  const WgOrder wo = wg_order(blockIdx.x, B * H, n_ktiles);
+  const int kt = wo.rank;
+  const int bh = wo.bh;
   const int b = bh / H;
   const int h = bh - b * H;
   const SeqSpan sp = seq_span(b, h, H, n_q, n_k, cu_q, cu_k, total_q, total_k);

@@ -121,9 +121,9 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
   const int hi = lane >> 5;
 
   // key blocks in order: under a causal mask block 0 sees every query tile
-  const int bh_count = B * H;
-  const int kb = blockIdx.x / bh_count;
-  const int bh = blockIdx.x - kb * bh_count;
+  const WgOrder wo = wg_order(blockIdx.x, B * H, (int)(gridDim.x / (unsigned)(B * H)));
+  const int kb = wo.rank;
+  const int bh = wo.bh;
   const int b = bh / H;
   const SeqSpan sp = seq_span(b, bh - b * H, H, n_q, n_k, cu_q, cu_k, total_q, total_k);
   const int N = sp.nq, Nk = sp.nk;   // this sequence's query and key rows

@@ -156,8 +156,30 @@ __device__ __forceinline__ u32x4 buffer_rsrc_words(const void* base, uint32_t by
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferRsrcWord3);
 }
+// Debug builds (FA_LDS_POISON) fill the 16 bytes a lane's copy is about to
+// write with all-ones (NaN in every element format of the library) just
+// before issuing it, i.e. after the slot's last reader passed the barrier
+// that frees it.  A reader that runs ahead of the copy's wait and barrier, or
+// a copy issued while a slow reader still uses the slot, then sees NaN, which
+// the parity tests reject.
+#ifndef FA_LDS_POISON
+#define FA_LDS_POISON 0
+#endif
+__device__ __forceinline__ void poison_lds16(uint32_t lds_base) {
+#if FA_LDS_POISON
+  auto* p = (__attribute__((address_space(3))) u32x4*)(uintptr_t)(lds_base + 16u * (threadIdx.x & 63));
+  *p = u32x4{~0u, ~0u, ~0u, ~0u};
+  // the poison must land before the copy's data
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+#else
+  (void)lds_base;
+#endif
+}
+
 __device__ __forceinline__ void lds_dma16_tracked(__amdgpu_buffer_rsrc_t rsrc, void* lds_dst,
                                                   int voff) {
+  poison_lds16(__builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) void*)lds_dst)));
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       rsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, 0, 0, 0);
 }
@@ -171,6 +193,7 @@ __device__ __forceinline__ void lds_dma16_tracked(__amdgpu_buffer_rsrc_t rsrc, v
 // compiler makes the next LDS read wait for the whole copy.)
 __device__ __forceinline__ void lds_dma16_at(const u32x4& rsrc, uint32_t lds, int voff, int soff) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
+  poison_lds16(base);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(base), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
@@ -277,25 +300,84 @@ __device__ __forceinline__ int key_length(const int32_t* seqlens_k, int b, int N
   return L < 0 ? 0 : (L > N ? N : L);
 }
 
-// Work-group schedule.  Work-groups are numbered so that consecutive ids
-// cover all (batch, head) pairs of one query tile; query tiles are issued
-// from the last (the longest under a causal mask) to the first, so the
+// Work-group schedule.  A launch has n_tiles work-groups per (batch, head)
+// pair, and a tile's rank orders them longest first (the last query tile
+// under a causal mask, the first key tile in the dK/dV kernel), so that the
 // dispatcher starts the long tiles first and fills the tail with short ones.
-// Consecutive ids are dispatched round-robin over the 8 XCDs, so when B*H is
-// a multiple of 8 every query tile of one head runs on the same XCD and the
-// head's K/V tiles are shared through that XCD's L2.
+// Ids are dispatched round-robin over the 8 XCDs (id % 8), each with its own
+// L2.  When B*H is a multiple of 8, XCD x takes heads x, x + 8, x + 16, ...
+// in groups of FA_XCD_GROUP heads, one group after the other, and runs a
+// group's tiles rank by rank: the XCD's CUs then work on few heads at a time,
+// stream the same K and V rows at about the same time and share them
+// through the XCD's L2, while each group still runs longest first.
+// Otherwise consecutive ids cover every head at one rank before the next.
+#ifndef FA_XCD_GROUP
+#define FA_XCD_GROUP 4
+#endif
+struct WgOrder {
+  int bh, rank;
+};
+
+// Debug builds (FA_WG_PERMUTE) visit the work-group ids in a scrambled
+// order, id -> id * P mod n for a prime P (n the grid size; the reversed order
+// when P divides n).  Every kernel computes each tile independently of the
+// others, so results must not change by a single bit.
+#ifndef FA_WG_PERMUTE
+#define FA_WG_PERMUTE 0
+#endif
+constexpr bool is_prime(unsigned n) {
+  if (n < 2) return false;
+  for (unsigned p = 2; p * p <= n; ++p)
+    if (n % p == 0) return false;
+  return true;
+}
+__device__ __forceinline__ int scheduled_wg(int wg) {
+#if FA_WG_PERMUTE
+  const unsigned n = gridDim.x;
+  constexpr unsigned kP = 40009u;
+  static_assert(is_prime(kP), "id -> id * P mod n is a permutation only for P coprime with n");
+  if (n % kP != 0) return (int)(((unsigned long long)(unsigned)wg * kP) % n);
+  return (int)(n - 1u - (unsigned)wg);
+#else
+  return wg;
+#endif
+}
+
+__device__ __forceinline__ WgOrder wg_order(int wg_id, int bh_count, int n_tiles) {
+  const int wg = scheduled_wg(wg_id);
+  WgOrder o;
+  if (FA_XCD_GROUP > 0 && (bh_count & 7) == 0) {
+    const int x = wg & 7, k = wg >> 3;
+    const int heads = bh_count >> 3;                  // heads of this XCD
+    const int span = FA_XCD_GROUP * n_tiles;          // ids of a full group
+    const int full = heads / FA_XCD_GROUP;            // full groups
+    int g = k / span;
+    int size = FA_XCD_GROUP;
+    if (g >= full) {                                  // the last, smaller group
+      g = full;
+      size = heads - full * FA_XCD_GROUP;
+    }
+    const int j = k - g * span;
+    o.rank = j / size;
+    o.bh = x + 8 * (g * FA_XCD_GROUP + (j - o.rank * size));
+  } else {
+    o.rank = wg / bh_count;
+    o.bh = wg - o.rank * bh_count;
+  }
+  return o;
+}
+
 struct TileCoord {
   int b, h, qt;
 };
 
+// Query-tile work-groups: the longest is the last query tile.
 __device__ __forceinline__ TileCoord tile_coord(int wg, int B, int H, int n_qtiles) {
-  const int bh_count = B * H;
-  const int qt_rev = wg / bh_count;
-  const int bh = wg - qt_rev * bh_count;
+  const WgOrder o = wg_order(wg, B * H, n_qtiles);
   TileCoord t;
-  t.qt = n_qtiles - 1 - qt_rev;
-  t.b = bh / H;
-  t.h = bh - t.b * H;
+  t.qt = n_qtiles - 1 - o.rank;
+  t.b = o.bh / H;
+  t.h = o.bh - t.b * H;
   return t;
 }
 

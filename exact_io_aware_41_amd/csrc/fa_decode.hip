@@ -120,8 +120,9 @@ void fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   __shared__ float red[KPS * D];
   __shared__ float scratch[4];
 
-  const int part = blockIdx.x % n_parts;
-  const int bh = blockIdx.x / n_parts;
+  const int wg = scheduled_wg(blockIdx.x);
+  const int part = wg % n_parts;
+  const int bh = wg / n_parts;
   const int b = bh / H;
   const int L = key_length(seqlens_k, b, N);
   const int k0 = part * chunk;

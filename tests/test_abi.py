@@ -40,6 +40,21 @@ def test_header_declarations_are_exported():
     assert set(names) <= exported
 
 
+def test_race_check_library_exports_the_same_calls():
+    """The race-check build (NaN-poisoned copy destinations, scrambled
+    work-group order) is the same C ABI, so the binding can drive it."""
+    names = declared_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.DEBUG_LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert set(names) <= set(re.findall(r"\bT (fa_\w+)", out))
+    dbg = fa.load_debug_library()
+    assert dbg.fa_abi_version() == fa.fa_abi_version()
+    with fa.library(dbg):
+        assert fa.fa_abi_version() == 5
+        assert fa.load_library() is dbg
+    assert fa.load_library() is not dbg
+
+
 def test_version_and_status_strings():
     assert fa.fa_abi_version() == 5
     assert fa.fa_status_string(fa.FA_SUCCESS) == "FA_SUCCESS"
