@@ -130,43 +130,6 @@ def blas_threads(n):
         return contextlib.nullcontext()
 
 
-class SclkSampler:
-    """Samples the GPU's graphics clock (MHz, via torch.cuda.clock_rate) on a
-    background thread while a timed region runs; median of the samples, or
-    None where the query is unavailable."""
-
-    def __init__(self, torch, dev, period_s=0.002):
-        import threading
-        self.torch, self.dev, self.period = torch, dev, period_s
-        self.samples = []
-        self.stop = threading.Event()
-        self.thread = threading.Thread(target=self._run, daemon=True)
-
-    def _run(self):
-        while not self.stop.is_set():
-            try:
-                mhz = self.torch.cuda.clock_rate(self.dev)
-            except Exception:  # noqa: BLE001 - clock query unavailable
-                return
-            if mhz:
-                self.samples.append(float(mhz))
-            self.stop.wait(self.period)
-
-    def __enter__(self):
-        self.thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self.stop.set()
-        self.thread.join()
-
-    def result(self):
-        if not self.samples:
-            return None
-        xs = sorted(self.samples)
-        return {"median_mhz": xs[len(xs) // 2], "max_mhz": xs[-1], "samples": len(xs)}
-
-
 def timing_stats(ms):
     """Median and min of per-step (or per-launch) times in ms."""
     xs = sorted(ms)
@@ -366,14 +329,13 @@ def main():
     events = [mk() for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    with SclkSampler(torch, dev) as sclk:
-        wall0 = time.perf_counter()
-        start.record()
-        for i in range(args.steps):
-            step(events[i])
-        end.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(events[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     step_ms = timing_stats([e[0].elapsed_time(e[-1]) for e in events])
@@ -423,9 +385,14 @@ def main():
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": fwd_hbm["frac"],
                     "traffic": measured_traffic("fwd", args.config)}
 
+    counters = roofline.get("counters")
     extra = {
         "step_ms": step_ms,
-        "sclk": sclk.result(),
+        # the clock the dominant kernel ran at: GRBM_GUI_ACTIVE cycles per XCD
+        # over the dispatch's duration in the committed counter run (the
+        # runtime's clock query reports no live engine clock on this chip)
+        "sclk": None if not counters else {"effective_mhz": counters.get("effective_sclk_mhz"),
+                                           "kernel": dominant, "source": "rocprofv3 counters"},
         "per_launch_ms": {n: round(t, 4) for n, t in per_kernel.items()},
         "per_launch_stats_ms": launch_ms,
         "kernel_tflops": {n: round(kernel_flops[n] / (per_kernel[n] * 1e-3) / 1e12, 1)

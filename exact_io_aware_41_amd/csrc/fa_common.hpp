@@ -312,7 +312,7 @@ __device__ __forceinline__ int key_length(const int32_t* seqlens_k, int b, int N
 // through the XCD's L2, while each group still runs longest first.
 // Otherwise consecutive ids cover every head at one rank before the next.
 #ifndef FA_XCD_GROUP
-#define FA_XCD_GROUP 4
+#define FA_XCD_GROUP 2
 #endif
 struct WgOrder {
   int bh, rank;
