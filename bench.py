@@ -82,7 +82,7 @@ def parse_args():
                    help="run the --config workload in another element format (default: its "
                         "own); e4m3: FP8 inputs with per-tensor descale factors and a bf16 "
                         "output, forward workloads only")
-    p.add_argument("--head-dim", type=int, default=None, choices=[64, 128, 256],
+    p.add_argument("--head-dim", type=int, default=None, choices=[64, 96, 128, 192, 256],
                    help="run the --config workload with another head dimension")
     p.add_argument("--kv-len", type=int, default=None, metavar="NK",
                    help="give keys and values NK rows instead of the queries' N (causal: query "

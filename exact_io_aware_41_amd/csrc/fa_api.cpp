@@ -26,12 +26,16 @@ fa::Elt elt_of(fa_dtype dtype) {
                                 : dtype == FA_DTYPE_F16 ? fa::Elt::kF16 : fa::Elt::kF32;
 }
 
+// head dimensions of the kernels: multiples of 32 from 64 to 256 that the
+// tile shapes and swizzles are built for
+bool head_dim_supported(int d) { return d == 64 || d == 96 || d == 128 || d == 192 || d == 256; }
+
 bool fwd_supported(fa_dtype dtype, int d) {
-  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128 || d == 256);
+  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && head_dim_supported(d);
 }
 
 bool bwd_supported(fa_dtype dtype, int d) {
-  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128 || d == 256);
+  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && head_dim_supported(d);
 }
 
 long long bwd_grid(fa_dtype dtype, int B, int H, int N, int d) {
@@ -54,7 +58,7 @@ hipError_t bwd_dq(fa_dtype t, const fa::BwdArgs& a) {
 }
 
 bool decode_supported(fa_dtype dtype, int d) {
-  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && (d == 64 || d == 128 || d == 256);
+  return (dtype == FA_DTYPE_F32 || is_half(dtype)) && head_dim_supported(d);
 }
 
 

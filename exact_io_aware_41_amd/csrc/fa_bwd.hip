@@ -46,8 +46,15 @@ namespace fa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// 1. D_i = sum_t dO_it O_it (fp32), one row per D/8 threads
+// 1. D_i = sum_t dO_it O_it (fp32): a row's D/8 16-byte chunks on the next
+//    power of two of threads (the spare ones of d = 96 and 192 add zero), so
+//    the row sum is a butterfly
 // ---------------------------------------------------------------------------
+template <int D>
+struct RowdotThreads {
+  static constexpr int value = D / 8 <= 8 ? 8 : D / 8 <= 16 ? 16 : 32;
+  static_assert(D / 8 <= 32, "head dimension");
+};
 template <class E, int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void fa_bwd_rowdot_kernel(const typename E::T* __restrict__ O, const typename E::T* __restrict__ dO,
@@ -55,12 +62,12 @@ void fa_bwd_rowdot_kernel(const typename E::T* __restrict__ O, const typename E:
   using elt = typename E::T;
   using elt8 = typename E::V8;
   using elt4 = typename E::V4;
-  constexpr int TPR = D / 8;  // threads per row
+  constexpr int TPR = RowdotThreads<D>::value;  // threads per row
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = gid / TPR;
   const int part = (int)(gid % TPR);
   float acc = 0.f;
-  if (row < rows) {
+  if (row < rows && part < D / 8) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(O + row * D + part * 8);
     const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * D + part * 8);
 #pragma unroll
@@ -101,9 +108,10 @@ struct DkdvPairCfg {
   static constexpr int KS = D / 16;
   static constexpr int NG = BQ / 16;       // 16-query groups per tile
   static constexpr int NDB = D / 32;
-  static constexpr int HDB = NDB / 2;      // 32-feature blocks per wave (its half)
+  // 32-feature blocks per wave (its half; at d = 96 the first wave of a pair
+  // takes two blocks and the second one)
+  static constexpr int HDB = (NDB + 1) / 2;
   static_assert(BQ == 64, "two 32-row halves per tile");
-  static_assert(NDB % 2 == 0, "head dimension splits in two halves of 32-feature blocks");
 };
 
 template <class E, int D, int BQ, int NW>
@@ -206,15 +214,16 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
     const s16x4 up = read_tr16(tile + r1 * D + ((col >> 3) ^ tile_swizzle<D>(r1)) * 8 + (col & 7));
     return __builtin_bit_cast(elt8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  constexpr int kRowsPerBlk = 1024 / (D * 2);
-  constexpr int kBlksPerTensor = BQ / kRowsPerBlk;
+  // 1 KiB block rb of a tile holds its 16-byte chunk positions 64 rb .. 64 rb
+  // + 63 (rows straddle blocks at d = 96 and 192)
+  constexpr int kChunksPerRow = D / 8;
+  constexpr int kBlksPerTensor = BQ * D * 2 / 1024;
   constexpr int kBlksPerWave = 2 * kBlksPerTensor / C::NW;
-  static_assert(2 * kBlksPerTensor % C::NW == 0, "whole 1 KiB blocks per wave");
+  static_assert(BQ * D * 2 % 1024 == 0 && 2 * kBlksPerTensor % C::NW == 0,
+                "whole 1 KiB blocks per wave");
   const int head_bytes = N * D * 2;
   const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(Qh, head_bytes);
   const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(dOh, head_bytes);
-  const int blk_row = lane / (D / 8);
-  const int blk_cpos = lane % (D / 8);
   float lreg = 0.f, dreg = 0.f;
   auto issue_tile = [&](int qi, int buf) FA_INLINE {
     const int qt0 = q_begin + qi * BQ;
@@ -230,10 +239,11 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
       const int blk = wave * kBlksPerWave + j;
       const bool is_q = blk < kBlksPerTensor;
       const int rb = is_q ? blk : blk - kBlksPerTensor;
-      const int row = rb * kRowsPerBlk + blk_row;
-      const int chunk = blk_cpos ^ kSwz(row);
+      const int pos = rb * 64 + lane;
+      const int row = pos / kChunksPerRow;
+      const int chunk = (pos % kChunksPerRow) ^ kSwz(row);
       const int voff = (qt0 + row) * (D * 2) + chunk * 16;
-      elt* dst = (is_q ? Qs[buf] : dOs[buf]) + rb * kRowsPerBlk * D;
+      elt* dst = (is_q ? Qs[buf] : dOs[buf]) + rb * 512;
       lds_dma16_tracked(is_q ? q_rsrc : o_rsrc, dst, voff);
     }
   };
@@ -316,20 +326,47 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
       po[1] = Xs[partner][1][lane];
       dso[0] = Xs[partner][2][lane];
       dso[1] = Xs[partner][3][lane];
+      // NB feature blocks from db0 (a compile-time count, so that at d = 96,
+      // where the pair's waves take two blocks and one, each wave still runs
+      // one straight-line schedule)
+      auto accumulate = [&](auto nb_tag, int db0) FA_INLINE {
+        constexpr int NB = decltype(nb_tag)::value;
 #pragma unroll
-      for (int g = 0; g < C::NG; ++g) {
-        // groups 2*half, 2*half+1 are this wave's rows; the others the partner's
-        const bool own = (g >> 1) == half;
-        const elt8 pfrag = own ? pa[g & 1] : po[g & 1];
-        const elt8 dsfrag = own ? dsa[g & 1] : dso[g & 1];
+        for (int g = 0; g < C::NG; ++g) {
+          // groups 2*half, 2*half+1 are this wave's rows; the others the partner's
+          const bool own = (g >> 1) == half;
+          const elt8 pfrag = own ? pa[g & 1] : po[g & 1];
+          const elt8 dsfrag = own ? dsa[g & 1] : dso[g & 1];
 #pragma unroll
-        for (int j = 0; j < C::HDB; ++j) {
-          const int db = half * C::HDB + j;
-          const elt8 ob = colfrag(dOs[buf], g, db);
-          const elt8 qbv = colfrag(Qs[buf], g, db);
-          dvacc[j] = E::mfma(pfrag, ob, dvacc[j]);
-          dkacc[j] = E::mfma(dsfrag, qbv, dkacc[j]);
+          for (int j = 0; j < NB; ++j) {
+            const int db = db0 + j;
+            const elt8 ob = colfrag(dOs[buf], g, db);
+            const elt8 qbv = colfrag(Qs[buf], g, db);
+            dvacc[j] = E::mfma(pfrag, ob, dvacc[j]);
+            dkacc[j] = E::mfma(dsfrag, qbv, dkacc[j]);
+          }
         }
+      };
+      if constexpr (C::NDB % 2 == 0) {
+#pragma unroll
+        for (int g = 0; g < C::NG; ++g) {
+          // groups 2*half, 2*half+1 are this wave's rows; the others the partner's
+          const bool own = (g >> 1) == half;
+          const elt8 pfrag = own ? pa[g & 1] : po[g & 1];
+          const elt8 dsfrag = own ? dsa[g & 1] : dso[g & 1];
+#pragma unroll
+          for (int j = 0; j < C::HDB; ++j) {
+            const int db = half * C::HDB + j;
+            const elt8 ob = colfrag(dOs[buf], g, db);
+            const elt8 qbv = colfrag(Qs[buf], g, db);
+            dvacc[j] = E::mfma(pfrag, ob, dvacc[j]);
+            dkacc[j] = E::mfma(dsfrag, qbv, dkacc[j]);
+          }
+        }
+      } else if (half == 0) {
+        accumulate(std::integral_constant<int, C::HDB>{}, 0);
+      } else {
+        accumulate(std::integral_constant<int, C::NDB - C::HDB>{}, C::HDB);
       }
     }
     // the next tile's row-major copy has landed once every wave passes here
@@ -341,6 +378,7 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
 #pragma unroll
   for (int j = 0; j < C::HDB; ++j) {
     const int db = half * C::HDB + j;
+    if (C::NDB % 2 != 0 && db >= C::NDB) break;   // the second wave's single block at d = 96
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int key = kw0 + c_row(v, lane);
@@ -437,9 +475,10 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
   // length L_b, so keys at or past it read as zeros.
   // K is read both as 16-row fragments (S^T = K Q^T) and by transposing
   // reads (the A operand of dQ^T = K^T dS^T), so no transposed copy exists.
-  constexpr int kRowsPerBlk = 1024 / (D * 2);
-  constexpr int kBlksPerTensor = BC / kRowsPerBlk;
+  constexpr int kChunksPerRow = D / 8;
+  constexpr int kBlksPerTensor = BC * D * 2 / 1024;
   constexpr int kBlksPerWave = 2 * kBlksPerTensor / NW;
+  static_assert(BC * D * 2 % 1024 == 0, "whole 1 KiB blocks per tile");
   static_assert(2 * kBlksPerTensor % NW == 0 && kBlksPerWave >= 1, "whole 1 KiB blocks per wave");
   const int key_bytes = kv_len * D * 2;
   const u32x4 k_rsrc = buffer_rsrc_words(Kh, (uint32_t)key_bytes);
@@ -452,8 +491,9 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
   for (int j = 0; j < kBlksPerWave; ++j) {
     const int blk = wave * kBlksPerWave + j;
     const int rb = blk < kBlksPerTensor ? blk : blk - kBlksPerTensor;
-    const int row = rb * kRowsPerBlk + lane / (D / 8);
-    voff[j] = row * (D * 2) + ((lane % (D / 8)) ^ tile_swizzle<D>(row)) * 16;
+    const int pos = rb * 64 + lane;
+    const int row = pos / kChunksPerRow;
+    voff[j] = row * (D * 2) + ((pos % kChunksPerRow) ^ tile_swizzle<D>(row)) * 16;
   }
   auto issue_tile = [&](int kt, int slot) FA_INLINE {
 #pragma unroll
@@ -461,7 +501,7 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
       const int blk = wave * kBlksPerWave + j;
       const bool is_k = blk < kBlksPerTensor;
       const int rb = is_k ? blk : blk - kBlksPerTensor;
-      elt* dst = (is_k ? Ks[slot] : Vs[slot]) + rb * kRowsPerBlk * D;
+      elt* dst = (is_k ? Ks[slot] : Vs[slot]) + rb * 512;
       lds_dma16(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D * 2);
     }
   };
@@ -572,7 +612,7 @@ hipError_t launch_preprocess_d(const BwdArgs& a) {
   using T = typename E::T;
   const long long rows = a.cu_q ? (long long)a.H * a.total_q : (long long)a.B * a.H * a.N;
   if (rows == 0) return hipSuccess;
-  const long long threads = rows * (D / 8);
+  const long long threads = rows * RowdotThreads<D>::value;
   hipLaunchKernelGGL((fa_bwd_rowdot_kernel<E, D>), dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, a.stream, static_cast<const T*>(a.o),
                      static_cast<const T*>(a.dout), a.delta, rows);
@@ -611,6 +651,8 @@ hipError_t launch_dq_d(const BwdArgs& a) {
   return hipGetLastError();
 }
 
+bool bwd_head_dim(int d) { return d == 64 || d == 96 || d == 128 || d == 192 || d == 256; }
+
 }  // namespace
 
 long long bwd_half_grid(int B, int H, int N, int d) {
@@ -619,7 +661,8 @@ long long bwd_half_grid(int B, int H, int N, int d) {
   const int br = 32 * (d <= 128 ? BwdWaves<128>::DQ : BwdWaves<256>::DQ);
   const long long kt = (N + bk - 1) / bk;
   const long long qt = (N + br - 1) / br;
-  const long long rows_wg = ((long long)B * H * N * 16 + 255) / 256;
+  const int tpr = d / 8 <= 8 ? 8 : d / 8 <= 16 ? 16 : 32;   // RowdotThreads
+  const long long rows_wg = ((long long)B * H * N * tpr + 255) / 256;
   long long m = kt * B * H;
   if (qt * B * H > m) m = qt * B * H;
   if (rows_wg > m) m = rows_wg;
@@ -627,40 +670,52 @@ long long bwd_half_grid(int B, int H, int N, int d) {
 }
 
 hipError_t launch_bwd_preprocess_half(const BwdArgs& a, Elt e) {
-  if (a.d != 64 && a.d != 128 && a.d != 256) return hipErrorInvalidValue;
+  if (!bwd_head_dim(a.d)) return hipErrorInvalidValue;
   if (e == Elt::kBf16)
     return a.d == 64    ? launch_preprocess_d<EltBf16, 64>(a)
+           : a.d == 96  ? launch_preprocess_d<EltBf16, 96>(a)
            : a.d == 128 ? launch_preprocess_d<EltBf16, 128>(a)
+           : a.d == 192 ? launch_preprocess_d<EltBf16, 192>(a)
                         : launch_preprocess_d<EltBf16, 256>(a);
   if (e == Elt::kF16)
     return a.d == 64    ? launch_preprocess_d<EltF16, 64>(a)
+           : a.d == 96  ? launch_preprocess_d<EltF16, 96>(a)
            : a.d == 128 ? launch_preprocess_d<EltF16, 128>(a)
+           : a.d == 192 ? launch_preprocess_d<EltF16, 192>(a)
                         : launch_preprocess_d<EltF16, 256>(a);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dkdv_half(const BwdArgs& a, Elt e) {
-  if (a.d != 64 && a.d != 128 && a.d != 256) return hipErrorInvalidValue;
+  if (!bwd_head_dim(a.d)) return hipErrorInvalidValue;
   if (e == Elt::kBf16)
     return a.d == 64    ? launch_dkdv_d<EltBf16, 64>(a)
+           : a.d == 96  ? launch_dkdv_d<EltBf16, 96>(a)
            : a.d == 128 ? launch_dkdv_d<EltBf16, 128>(a)
+           : a.d == 192 ? launch_dkdv_d<EltBf16, 192>(a)
                         : launch_dkdv_d<EltBf16, 256>(a);
   if (e == Elt::kF16)
     return a.d == 64    ? launch_dkdv_d<EltF16, 64>(a)
+           : a.d == 96  ? launch_dkdv_d<EltF16, 96>(a)
            : a.d == 128 ? launch_dkdv_d<EltF16, 128>(a)
+           : a.d == 192 ? launch_dkdv_d<EltF16, 192>(a)
                         : launch_dkdv_d<EltF16, 256>(a);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq_half(const BwdArgs& a, Elt e) {
-  if (a.d != 64 && a.d != 128 && a.d != 256) return hipErrorInvalidValue;
+  if (!bwd_head_dim(a.d)) return hipErrorInvalidValue;
   if (e == Elt::kBf16)
     return a.d == 64    ? launch_dq_d<EltBf16, 64>(a)
+           : a.d == 96  ? launch_dq_d<EltBf16, 96>(a)
            : a.d == 128 ? launch_dq_d<EltBf16, 128>(a)
+           : a.d == 192 ? launch_dq_d<EltBf16, 192>(a)
                         : launch_dq_d<EltBf16, 256>(a);
   if (e == Elt::kF16)
     return a.d == 64    ? launch_dq_d<EltF16, 64>(a)
+           : a.d == 96  ? launch_dq_d<EltF16, 96>(a)
            : a.d == 128 ? launch_dq_d<EltF16, 128>(a)
+           : a.d == 192 ? launch_dq_d<EltF16, 192>(a)
                         : launch_dq_d<EltF16, 256>(a);
   return hipErrorInvalidValue;
 }

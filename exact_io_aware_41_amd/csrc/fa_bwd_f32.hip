@@ -54,16 +54,24 @@ struct F32BwdCfg {
   static_assert(D % 32 == 0, "head dimension");
 };
 
+// threads per row of the row dot products: the row's D/4 16-byte chunks on
+// the next power of two of threads (the spare ones of d = 96 and 192 add zero)
+template <int D>
+struct RowdotF32Threads {
+  static constexpr int value = D / 4 <= 16 ? 16 : D / 4 <= 32 ? 32 : 64;
+  static_assert(D / 4 <= 64, "head dimension");
+};
+
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void fa_bwd_rowdot_f32_kernel(const float* __restrict__ O, const float* __restrict__ dO,
                               float* __restrict__ Dout, long long rows) {
-  constexpr int TPR = D / 4;   // threads per row
+  constexpr int TPR = RowdotF32Threads<D>::value;   // threads per row
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = gid / TPR;
   const int part = (int)(gid % TPR);
   float acc = 0.f;
-  if (row < rows) {
+  if (row < rows && part < D / 4) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(O + row * D + part * 4);
     const f32x4 b = *reinterpret_cast<const f32x4*>(dO + row * D + part * 4);
 #pragma unroll
@@ -344,7 +352,7 @@ template <int D>
 hipError_t launch_preprocess_f32_d(const BwdArgs& a) {
   const long long rows = a.cu_q ? (long long)a.H * a.total_q : (long long)a.B * a.H * a.N;
   if (rows == 0) return hipSuccess;
-  const long long threads = rows * (D / 4);
+  const long long threads = rows * RowdotF32Threads<D>::value;
   hipLaunchKernelGGL((fa_bwd_rowdot_f32_kernel<D>), dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, a.stream, static_cast<const float*>(a.o),
                      static_cast<const float*>(a.dout), a.delta, rows);
@@ -387,28 +395,35 @@ hipError_t launch_dq_f32_d(const BwdArgs& a) {
 long long bwd_f32_grid(int B, int H, int N, int d) {
   (void)d;
   const long long tiles = (N + 31) / 32;   // the smallest row block of either kernel
-  const long long rows_wg = ((long long)B * H * N * (d / 4) + 255) / 256;
+  const int tpr = d / 4 <= 16 ? 16 : d / 4 <= 32 ? 32 : 64;   // RowdotF32Threads
+  const long long rows_wg = ((long long)B * H * N * tpr + 255) / 256;
   const long long m = tiles * B * H;
   return rows_wg > m ? rows_wg : m;
 }
 
 hipError_t launch_bwd_preprocess_f32(const BwdArgs& a) {
   if (a.d == 64) return launch_preprocess_f32_d<64>(a);
+  if (a.d == 96) return launch_preprocess_f32_d<96>(a);
   if (a.d == 128) return launch_preprocess_f32_d<128>(a);
+  if (a.d == 192) return launch_preprocess_f32_d<192>(a);
   if (a.d == 256) return launch_preprocess_f32_d<256>(a);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dkdv_f32(const BwdArgs& a) {
   if (a.d == 64) return launch_dkdv_f32_d<64>(a);
+  if (a.d == 96) return launch_dkdv_f32_d<96>(a);
   if (a.d == 128) return launch_dkdv_f32_d<128>(a);
+  if (a.d == 192) return launch_dkdv_f32_d<192>(a);
   if (a.d == 256) return launch_dkdv_f32_d<256>(a);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq_f32(const BwdArgs& a) {
   if (a.d == 64) return launch_dq_f32_d<64>(a);
+  if (a.d == 96) return launch_dq_f32_d<96>(a);
   if (a.d == 128) return launch_dq_f32_d<128>(a);
+  if (a.d == 192) return launch_dq_f32_d<192>(a);
   if (a.d == 256) return launch_dq_f32_d<256>(a);
   return hipErrorInvalidValue;
 }

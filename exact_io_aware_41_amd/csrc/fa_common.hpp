@@ -228,6 +228,28 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Row-major tiles read both ways - 16-row fragments by ds_read_b128 and
+// column fragments by transposing reads (16 lanes: 4 consecutive rows x 32
+// bytes; a wave half: 4 rows x 64 bytes, served as 32 lanes per cycle) -
+// XOR their 16-byte chunk index with a linear map of the row bits that is
+// one-to-one on every lane group of both access kinds (searched exhaustively
+// under the measured grouping rules).  Rows of d = 96 and 192 (192 and 384
+// bytes) are not whole bank periods; their maps change only the low 2 or 3
+// bits of the chunk index, so a chunk stays inside its aligned group of 4 or
+// 8 of the row's 12 or 24 chunks.
+template <int D>
+__device__ __forceinline__ int tile_swizzle(int row) {
+  static_assert(D == 64 || D == 96 || D == 128 || D == 192 || D == 256, "head dimension");
+  if constexpr (D == 128 || D == 256)
+    return ((row & 3) << 2) ^ ((row >> 2) & 3) ^ (((row >> 4) & 1) * 3);
+  else if constexpr (D == 192)
+    return (((row >> 1) & 1) << 2) | ((row >> 3) & 3);
+  else if constexpr (D == 96)
+    return (row >> 3) & 3;
+  else
+    return (((row >> 1) & 1) << 2) ^ ((row >> 3) & 1) ^ (((row >> 4) & 1) << 1);
+}
+
 // Row-major tiles are stored unpadded with their 16-byte chunks XOR-swizzled
 // by a function of the row.  On gfx950 a ds_read_b128 serves lanes 0-31 and
 // 32-63 in different cycles, and within a half two groups of 16 lanes
@@ -243,26 +265,17 @@ __device__ __forceinline__ void lds_barrier() {
 // a bank period, leaving 8 slots for 16 lanes).
 template <int D>
 __device__ __forceinline__ int row_swizzle(int row) {
+  static_assert(D == 64 || D == 96 || D == 128 || D == 192 || D == 256, "head dimension");
   // d = 256: rows of 512 bytes repeat the 256-byte bank pattern, so the
   // d = 128 XOR of the low four chunk bits serves unchanged
-  if constexpr (D >= 128)
+  if constexpr (D == 128 || D == 256)
     return (row & 15) ^ (((row >> 4) & 1) * 12) ^ (((row >> 5) & 1) * 2);
+  // d = 96 and 192: the map that also serves transposing reads (below) is
+  // conflict-free for these fragment reads as well
+  else if constexpr (D == 96 || D == 192)
+    return tile_swizzle<D>(row);
   else
     return (row ^ (row >> 2)) & (D / 8 - 1);
-}
-
-// Row-major tiles read both ways - 16-row fragments by ds_read_b128 and
-// column fragments by transposing reads (16 lanes: 4 consecutive rows x 32
-// bytes; a wave half: 4 rows x 64 bytes, served as 32 lanes per cycle) -
-// XOR their 16-byte chunk index with a linear map of the row bits that is
-// one-to-one on every lane group of both access kinds (searched exhaustively
-// under the measured grouping rules).
-template <int D>
-__device__ __forceinline__ int tile_swizzle(int row) {
-  if constexpr (D >= 128)
-    return ((row & 3) << 2) ^ ((row >> 2) & 3) ^ (((row >> 4) & 1) * 3);
-  else
-    return (((row >> 1) & 1) << 2) ^ ((row >> 3) & 1) ^ (((row >> 4) & 1) << 1);
 }
 
 // Row-major tiles read only by transposing reads (ds_read_b64_tr_b16) swizzle
@@ -273,8 +286,13 @@ __device__ __forceinline__ int tile_swizzle(int row) {
 // 4 x 64 bytes on 4 distinct 64-byte bank ranges (measured conflict-free).
 template <int D>
 __device__ __forceinline__ int seg_swizzle(int row) {
-  if constexpr (D >= 128)
+  static_assert(D == 64 || D == 96 || D == 128 || D == 192 || D == 256, "head dimension");
+  if constexpr (D == 128 || D == 256)
     return row & 3;
+  else if constexpr (D == 192)   // 384-byte rows: row bit 0 already alternates bank halves
+    return (row >> 1) & 1;
+  else if constexpr (D == 96)    // 192-byte rows: four rows already fall on four 64-byte ranges
+    return 0;
   else
     return (row >> 1) & 1;
 }

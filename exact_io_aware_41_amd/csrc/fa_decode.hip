@@ -113,9 +113,12 @@ void fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                             float scale_log2, int H, int N, int chunk, int n_parts,
                             float* __restrict__ o_parts, float* __restrict__ lse_parts) {
   constexpr int E = ElemsPer16<T>::value;
-  constexpr int LPK = D / E;              // lanes per key row
+  constexpr int CPR = D / E;              // 16-byte chunks per key row
+  // lanes per key row: the next power of two (d = 96 and 192 leave the last
+  // lanes of each row group idle), so the row's dot product is a butterfly
+  constexpr int LPK = CPR <= 1 ? 1 : 1 << (32 - __builtin_clz(CPR - 1));
   constexpr int KPS = kDecThreads / LPK;  // keys per step of the work-group
-  static_assert(LPK <= 64 && (LPK & (LPK - 1)) == 0, "a key row spans whole lanes of one wave");
+  static_assert(CPR * E == D && LPK <= 64, "a key row spans whole lanes of one wave");
   __shared__ float sc[kDecMaxChunk];
   __shared__ float red[KPS * D];
   __shared__ float scratch[4];
@@ -137,12 +140,18 @@ void fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   const int n = k1 - k0;
   const int kg = tid / LPK;
   const int lp = tid % LPK;
+  const bool live = lp < CPR;   // this lane holds a chunk of the row
   const T* Kp = K + ((size_t)bh * N + k0) * D + lp * E;
   const T* Vp = V + ((size_t)bh * N + k0) * D + lp * E;
 
   // the query chunk of this lane, in log2 units of the scaled score
   float qv[E];
-  load16(Q + (size_t)bh * D + lp * E, qv);
+  if (live) {
+    load16(Q + (size_t)bh * D + lp * E, qv);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) qv[e] = 0.f;
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e) qv[e] *= scale_log2;
 
@@ -152,7 +161,7 @@ void fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
       const int j = j0 + u * KPS + kg;
-      if (j < n) {
+      if (j < n && live) {
         load16(Kp + (size_t)j * D, kr[u]);
       } else {
 #pragma unroll
@@ -193,7 +202,7 @@ void fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
       const int j = j0 + u * KPS + kg;
-      if (j < n) {
+      if (j < n && live) {
         load16(Vp + (size_t)j * D, vr[u]);
       } else {
 #pragma unroll
@@ -208,8 +217,10 @@ void fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(p, vr[u][e], acc[e]);
     }
   }
+  if (live) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) red[kg * D + lp * E + e] = acc[e];
+    for (int e = 0; e < E; ++e) red[kg * D + lp * E + e] = acc[e];
+  }
   __syncthreads();
   const float inv = 1.f / l;
   for (int f = tid; f < D; f += kDecThreads) {
@@ -313,9 +324,14 @@ DecodePlan decode_plan(int B, int H, int N) {
 template <typename T>
 hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, float* o_parts,
                            float* lse_parts) {
-  if (a.d == 64) return launch_decode_split<T, 64>(a, p, o_parts, lse_parts);
-  if (a.d == 128) return launch_decode_split<T, 128>(a, p, o_parts, lse_parts);
-  return launch_decode_split<T, 256>(a, p, o_parts, lse_parts);
+  switch (a.d) {
+    case 64: return launch_decode_split<T, 64>(a, p, o_parts, lse_parts);
+    case 96: return launch_decode_split<T, 96>(a, p, o_parts, lse_parts);
+    case 128: return launch_decode_split<T, 128>(a, p, o_parts, lse_parts);
+    case 192: return launch_decode_split<T, 192>(a, p, o_parts, lse_parts);
+    case 256: return launch_decode_split<T, 256>(a, p, o_parts, lse_parts);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_decode(const DecodeArgs& a, Elt elt) {

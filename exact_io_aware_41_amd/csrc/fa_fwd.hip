@@ -190,9 +190,13 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
   // or past it read as zeros (masked anyway, and whatever lies there never
   // enters a 0 * x product).  Each lane fetches the global chunk
   // that the tile's swizzle places at its LDS position.
-  constexpr int kRowsPerBlk = 1024 / (D * 2);
-  constexpr int kBlksPerTensor = BC / kRowsPerBlk;
+  // A tile is BC rows of D/8 16-byte chunks stored contiguously; 1 KiB block
+  // rb holds chunk positions 64 rb .. 64 rb + 63 (whole rows when D/8
+  // divides 64, rows straddling blocks at d = 96 and 192).
+  constexpr int kChunksPerRow = D / 8;
+  constexpr int kBlksPerTensor = BC * D * 2 / 1024;
   constexpr int kBlksPerWave = 2 * kBlksPerTensor / NW;
+  static_assert(BC * D * 2 % 1024 == 0, "whole 1 KiB blocks per tile");
   static_assert(2 * kBlksPerTensor % NW == 0 && kBlksPerWave >= 1, "whole 1 KiB blocks per wave");
   const int key_bytes = kv_len * D * 2;
   const u32x4 k_rsrc = buffer_rsrc_words(Kh, (uint32_t)key_bytes);
@@ -207,8 +211,9 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
     const int blk = wave * kBlksPerWave + j;
     const bool is_k = blk < kBlksPerTensor;
     const int rb = is_k ? blk : blk - kBlksPerTensor;
-    const int row = rb * kRowsPerBlk + lane / (D / 8);
-    const int cpos = lane % (D / 8);
+    const int pos = rb * 64 + lane;
+    const int row = pos / kChunksPerRow;
+    const int cpos = pos % kChunksPerRow;
     const int chunk = is_k ? (cpos ^ row_swizzle<D>(row))
                            : ((((cpos >> 2) ^ seg_swizzle<D>(row)) << 2) | (cpos & 3));
     voff[j] = row * (D * 2) + chunk * 16;
@@ -224,7 +229,7 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
     const int rb = is_k ? blk : blk - kBlksPerTensor;
     const uint32_t dst = (is_k ? ks_lds + (uint32_t)kbuf * kSlotBytes
                                : vs_lds + (uint32_t)vslot * kSlotBytes) +
-                         (uint32_t)(rb * kRowsPerBlk * D * 2);
+                         (uint32_t)(rb * 1024);
     lds_dma16_at(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D * 2);
   };
   auto issue_tile = [&](int kt, int kbuf, int vslot) FA_INLINE {
@@ -813,7 +818,9 @@ template <class E>
 hipError_t launch_half_e(const FwdArgs& a) {
   switch (a.d) {
     case 64: return launch_half_d<E, 64>(a);
+    case 96: return launch_half_d<E, 96>(a);
     case 128: return launch_half_d<E, 128>(a);
+    case 192: return launch_half_d<E, 192>(a);
     case 256: return launch_half_d<E, 256>(a);
     default: return hipErrorInvalidValue;
   }
@@ -867,7 +874,9 @@ hipError_t launch_fwd_half(const FwdArgs& a, Elt e) {
 hipError_t launch_fwd_f32(const FwdArgs& a) {
   switch (a.d) {
     case 64: return launch_f32_d<64>(a);
+    case 96: return launch_f32_d<96>(a);
     case 128: return launch_f32_d<128>(a);
+    case 192: return launch_f32_d<192>(a);
     case 256: return launch_f32_d<256>(a);
     default: return hipErrorInvalidValue;
   }

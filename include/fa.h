@@ -69,11 +69,13 @@
  *                          workspace than the library's static array holds.
  *
  * Compiled (dtype, d) set:
- *  forward : FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128, 256}
- *  backward: FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in {64, 128, 256}
+ *  forward : FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in
+ *            {64, 96, 128, 192, 256}
+ *  backward: FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in
+ *            {64, 96, 128, 192, 256}
  *            (fp32 on the fp32 MFMA: fp32 inputs, arithmetic and outputs)
  *  decode and merge: FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16 with d in
- *  {64, 128, 256}
+ *  {64, 96, 128, 192, 256}
  *  fa_forward_fp8: E4M3 inputs, bf16 output, d = 128
  * The 16-bit formats and head dimensions up to 256 are those the pages list
  * for fused kernels ("What is FlashAttention?", "Trade-offs and edge cases");

@@ -122,8 +122,8 @@ def test_forward_rejects_invalid_arguments(kw):
     assert fwd(**kw) == fa.FA_ERROR_INVALID_VALUE
 
 
-@pytest.mark.parametrize("dtype,d", [(BF16, 96), (BF16, 512), (BF16, 32), (F32, 96), (F32, 16),
-                                     (F32, 192), (F16, 96), (F16, 512)])
+@pytest.mark.parametrize("dtype,d", [(BF16, 80), (BF16, 512), (BF16, 32), (F32, 160), (F32, 16),
+                                     (F32, 224), (F16, 160), (F16, 512), (BF16, 100)])
 def test_forward_unsupported_shapes_fail_loudly(dtype, d):
     assert fwd(dtype=dtype, d=d) == fa.FA_ERROR_UNSUPPORTED
 
@@ -132,7 +132,7 @@ def test_forward_empty_problems_succeed_without_pointers():
     for B, H, N in ((0, 4, 16), (2, 0, 16), (2, 4, 0)):
         assert fwd(B=B, H=H, N=N, q=None, k=None, v=None, o=None, lse=None) == fa.FA_SUCCESS
     # an empty problem with an unsupported head dim still reports it
-    assert fwd(N=0, d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert fwd(N=0, d=160) == fa.FA_ERROR_UNSUPPORTED
     # f16 is a known format; an unknown code is an invalid value
     assert fwd(dtype=F16, N=0, q=None, k=None, v=None, o=None, lse=None) == fa.FA_SUCCESS
     assert fwd(dtype=3) == fa.FA_ERROR_INVALID_VALUE
@@ -165,11 +165,11 @@ def test_backward_rejects_invalid_arguments(kw):
 
 
 def test_backward_unsupported_and_workspace_size():
-    assert bwd(dtype=F32, d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(dtype=F32, d=160) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(dtype=F32, d=512) == fa.FA_ERROR_UNSUPPORTED
-    assert bwd(d=192) == fa.FA_ERROR_UNSUPPORTED
-    assert bwd(d=96) == fa.FA_ERROR_UNSUPPORTED
-    assert bwd(dtype=F16, d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(d=224) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(d=80) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd(dtype=F16, d=160) == fa.FA_ERROR_UNSUPPORTED
     assert bwd(dtype=F16, B=0, q=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
     assert bwd(dtype=3) == fa.FA_ERROR_INVALID_VALUE
     assert fa.fa_backward_workspace_size(BF16, 2, 32, 8192, 128) == 2 * 32 * 8192 * 4
@@ -223,9 +223,9 @@ def test_varlen_empty_unsupported_and_limits():
     assert fwd_varlen(tq=0, cq=None) == fa.FA_ERROR_INVALID_VALUE
     # queries without keys still write empty rows, so o and lse are required
     assert fwd_varlen(tk=0, k=None, v=None, lse=None) == fa.FA_ERROR_INVALID_VALUE
-    assert fwd_varlen(d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert fwd_varlen(d=160) == fa.FA_ERROR_UNSUPPORTED
     assert fwd_varlen(dtype=F32, d=512) == fa.FA_ERROR_UNSUPPORTED
-    assert bwd_varlen(d=192) == fa.FA_ERROR_UNSUPPORTED
+    assert bwd_varlen(d=224) == fa.FA_ERROR_UNSUPPORTED
     # one sequence's head must stay under 2^31 bytes
     assert fwd_varlen(mq=1 << 23, tq=1 << 23) == fa.FA_ERROR_UNSUPPORTED
     assert fwd(N=1 << 23) == fa.FA_ERROR_UNSUPPORTED
@@ -306,8 +306,8 @@ def test_backward_phase_entry_points_validate():
         o, do, delta, None)
     assert pre(o=None) == fa.FA_ERROR_INVALID_VALUE
     assert pre(delta=MIS) == fa.FA_ERROR_INVALID_VALUE
-    assert pre(d=96) == fa.FA_ERROR_UNSUPPORTED
-    assert pre(dtype=F32, d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert pre(d=160) == fa.FA_ERROR_UNSUPPORTED
+    assert pre(dtype=F32, d=224) == fa.FA_ERROR_UNSUPPORTED
     assert pre(N=0, o=None, do=None, delta=None) == fa.FA_SUCCESS
 
     def dkdv(q=A, dk=A, dv=A, delta=A, scale=0.1, causal=0, d=128, N=16, Nk=None):
@@ -355,11 +355,11 @@ def test_decode_rejects_invalid_arguments(kw):
 
 
 def test_decode_unsupported_and_empty():
-    assert dec(d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert dec(d=160) == fa.FA_ERROR_UNSUPPORTED
     assert dec(dtype=F32, d=512) == fa.FA_ERROR_UNSUPPORTED
     assert dec(B=0, q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
     assert dec(N=0, q=None, ws=None, ws_bytes=0) == fa.FA_SUCCESS
-    assert dec(dtype=F16, d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert dec(dtype=F16, d=224) == fa.FA_ERROR_UNSUPPORTED
     assert dec(dtype=F16, B=0, q=None, k=None, v=None, o=None, lse=None, ws=None,
                ws_bytes=0) == fa.FA_SUCCESS
 
@@ -389,7 +389,7 @@ def test_merge_states_validates():
     assert m(parts=0) == fa.FA_ERROR_INVALID_VALUE
     assert m(parts=4097) == fa.FA_ERROR_INVALID_VALUE
     assert m(rows=-1) == fa.FA_ERROR_INVALID_VALUE
-    assert m(d=96) == fa.FA_ERROR_UNSUPPORTED
+    assert m(d=160) == fa.FA_ERROR_UNSUPPORTED
     assert m(rows=0, op=None, lp=None, o=None) == fa.FA_SUCCESS
 
 

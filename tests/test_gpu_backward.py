@@ -76,7 +76,7 @@ def compare_heads(cfg, inputs, o, dq, dk, dv, heads, strict=False):
     return worst
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 192])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_small_shapes_all_heads(d, causal, dtype):

@@ -60,7 +60,7 @@ def oracle_decode(cfg, inputs, heads=None):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
 @pytest.mark.parametrize("N,lengths", [
     (1, None), (63, None), (300, "zero_then_uniform"), (300, [300, 1, 0]), (5000, None),
     (5000, [4097, 4096, 64]), (9000, "zero_then_uniform"),
@@ -108,7 +108,7 @@ def test_decode_one_long_row_many_parts():
 
 
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("parts,d", [(1, 128), (7, 64), (300, 128), (4096, 64)])
+@pytest.mark.parametrize("parts,d", [(1, 128), (7, 64), (300, 128), (4096, 64), (5, 96), (33, 192)])
 def test_merge_states_against_oracle(out_dtype, parts, d):
     torch = torch_cuda()
     fa = lib()

@@ -66,7 +66,7 @@ def test_config1_fp32_full_against_both_routes():
 SMALL_N = [1, 2, 63, 65, 127, 129, 256, 300, 513]
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_small_shapes_all_rows(d, causal, dtype):
