@@ -47,6 +47,11 @@ def common_flags() -> list[str]:
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators and operands in VGPRs: kernels with more than 256
+        # live registers (one wave per SIMD: d = 192 and 256, the fp32 paths)
+        # otherwise had the compiler park values in AGPRs and copy them back
+        # and forth, several hundred v_accvgpr moves per loop iteration
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-I", INCLUDE, "-I", CSRC,
         "-Wall", "-Wno-unused-function",
     ]
