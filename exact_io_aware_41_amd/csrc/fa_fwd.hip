@@ -27,9 +27,9 @@
 //  * the waves of a SIMD run out of phase: waves 4..7 take the softmax of
 //    tile t-1 and multiply P(t-1) V(t-1) before computing S(t), while waves
 //    0..3 compute S(t) first, so one wave's MFMAs overlap the other's softmax.
-//    Waves 0..3 issue their copies of the next tile between their S(t)
-//    MFMAs, so the copies of all eight waves do not queue up at once after
-//    the barrier.
+//    Waves 0..3 issue all the copies of the next tile (16 each), one every
+//    two MFMAs of their S(t) stage: waves 4..7 run the longer iteration, and
+//    copies issued at the start of it cost them about 560 cycles.
 //  * scores are handled in the log2 domain: x = s * scale * log2(e), so the
 //    exponentials are single v_exp_f32 instructions.  The reference maximum
 //    only moves when a tile's maximum exceeds it by more than 2^8, so the O
@@ -66,6 +66,11 @@
 #endif
 #ifndef FA_FWD_SCHED
 #define FA_FWD_SCHED 2
+#endif
+// 1: with two wave groups, only the first group issues the tile copies (the
+// second group's iteration is the longer one; 8 copies cost it about 560 cycles)
+#ifndef FA_FWD_DMA_LEAD
+#define FA_FWD_DMA_LEAD 1
 #endif
 
 
@@ -195,9 +200,16 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
   // divides 64, rows straddling blocks at d = 96 and 192).
   constexpr int kChunksPerRow = D / 8;
   constexpr int kBlksPerTensor = BC * D * 2 / 1024;
-  constexpr int kBlksPerWave = 2 * kBlksPerTensor / NW;
+  // with two groups, only the first group's waves copy (FA_FWD_DMA_LEAD):
+  // the second group's iteration is the longer one
+  constexpr bool kLeadCopies = FA_FWD_DMA_LEAD && kPingPong;
+  constexpr int kCopyWaves = kLeadCopies ? NW / 2 : NW;
+  constexpr int kBlksPerWave = 2 * kBlksPerTensor / kCopyWaves;
+  const bool copier = !kLeadCopies || !lagging;
+  const int cwave = copier ? wave : 0;   // keeps a non-copying wave's offsets in range
   static_assert(BC * D * 2 % 1024 == 0, "whole 1 KiB blocks per tile");
-  static_assert(2 * kBlksPerTensor % NW == 0 && kBlksPerWave >= 1, "whole 1 KiB blocks per wave");
+  static_assert(2 * kBlksPerTensor % kCopyWaves == 0 && kBlksPerWave >= 1,
+                "whole 1 KiB blocks per wave");
   const int key_bytes = kv_len * D * 2;
   const u32x4 k_rsrc = buffer_rsrc_words(Kh, (uint32_t)key_bytes);
   const u32x4 v_rsrc = buffer_rsrc_words(Vh, (uint32_t)key_bytes);
@@ -208,7 +220,7 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
   int voff[kBlksPerWave];
 #pragma unroll
   for (int j = 0; j < kBlksPerWave; ++j) {
-    const int blk = wave * kBlksPerWave + j;
+    const int blk = cwave * kBlksPerWave + j;
     const bool is_k = blk < kBlksPerTensor;
     const int rb = is_k ? blk : blk - kBlksPerTensor;
     const int pos = rb * 64 + lane;
@@ -224,7 +236,7 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
   const uint32_t vs_lds = lds_address(&Vs[0][0]);
   constexpr uint32_t kSlotBytes = BC * D * 2;
   auto issue_block = [&](int kt, int kbuf, int vslot, int j) FA_INLINE {
-    const int blk = wave * kBlksPerWave + j;
+    const int blk = cwave * kBlksPerWave + j;
     const bool is_k = blk < kBlksPerTensor;
     const int rb = is_k ? blk : blk - kBlksPerTensor;
     const uint32_t dst = (is_k ? ks_lds + (uint32_t)kbuf * kSlotBytes
@@ -233,8 +245,10 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
     lds_dma16_at(is_k ? k_rsrc : v_rsrc, dst, voff[j], kt * BC * D * 2);
   };
   auto issue_tile = [&](int kt, int kbuf, int vslot) FA_INLINE {
+    if (copier) {
 #pragma unroll
-    for (int j = 0; j < kBlksPerWave; ++j) issue_block(kt, kbuf, vslot, j);
+      for (int j = 0; j < kBlksPerWave; ++j) issue_block(kt, kbuf, vslot, j);
+    }
   };
   auto no_dma = [](int) FA_INLINE {};
 
@@ -428,7 +442,7 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
       if (kLag) {
         // second group: softmax(t-1) and P(t-1) V(t-1), then S(t); its
         // softmax runs while the first group computes S(t)
-        dma_all();
+        if constexpr (!kLeadCopies) dma_all();
         if (kt >= 1 && kt - 1 < n_act) {
           stage_softmax(kt - 1);
           stage_PV((kt - 1) % kVSlots, no_dma);
