@@ -17,7 +17,9 @@
 //     transposing reads (ds_read_b64_tr_b16) of the same tile give the B
 //     operands of dV and dK with the rows in the order of the P fragment.  S
 //     and dP come out with one key per lane, so P and dS feed the next MFMA
-//     straight from registers;
+//     straight from registers.  Up to d = 128 the two waves of a pair run
+//     half a tile apart (one computes exponentials while the other issues
+//     MFMAs, section 2b); at d = 192 and 256 four waves run in step;
 //  3. dQ: a work-group owns query rows (like the forward) and loops over key
 //     tiles; S^T and dP^T come out with one query per lane, so LSE_i and D_i
 //     are one register each, and dS^T feeds dQ^T = K^T dS^T from registers,
@@ -39,6 +41,10 @@
 #endif
 #ifndef FA_DQ_BC
 #define FA_DQ_BC 64
+#endif
+// dK/dV with the two waves of each pair half a tile apart (d <= 128)
+#ifndef FA_DKDV_PINGPONG
+#define FA_DKDV_PINGPONG 1
 #endif
 
 namespace fa {
@@ -391,6 +397,383 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
 }
 
 // ---------------------------------------------------------------------------
+// 2b. dK / dV with the pairs' waves out of phase (eight waves, d <= 128)
+//
+// The same pairs, work split and LDS exchange as above, but the second wave
+// of every pair runs half a tile behind the first, so that on each SIMD one
+// wave issues MFMAs while its partner computes exponentials (the in-step
+// schedule leaves the matrix cores idle while both do).  With M1(t) = S and
+// dP of query tile t, V(t) = P and dS, and M2(t) = dV and dK, each stage
+// ends at a work-group barrier:
+//   stage X(t): leading wave  M2(t-1), M1(t)       lagging wave  V(t)
+//   stage Y(t): leading wave  V(t)                 lagging wave  M2(t-1), M1(t+1)
+// A leading wave hands its P and dS over at the end of its V stage, into
+// one of two exchange planes (by tile parity); a lagging wave, at the start
+// of the stage after its V stage, into a single plane, after reading back its
+// own P and dS of the tile before (the 160 KiB of LDS hold a second plane
+// for one group only).  Exchange writes inside an MFMA stage cost that stage
+// several hundred cycles.  Tile t is read from stage Y(t-1) to Y(t+1), so
+// the Q/dO tiles take three LDS slots, and the lagging group copies tile t+1
+// (and stores its statistics) during stage X(t).  Each MFMA stage is one
+// wave's: its operand reads run four MFMAs ahead of their use.
+// ---------------------------------------------------------------------------
+template <class E, int D, int BQ>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
+                           const typename E::T* __restrict__ K,
+                           const typename E::T* __restrict__ V,
+                           const typename E::T* __restrict__ dO,
+                           const float* __restrict__ LSE, const float* __restrict__ Dlt,
+                           const int32_t* __restrict__ seqlens_k, float scale,
+                           float scale_log2, int causal, typename E::T* __restrict__ dK,
+                           typename E::T* __restrict__ dV, int B, int H, int n_q, int n_k,
+                           int n_ktiles,
+                           const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                           int total_q, int total_k) {
+  using elt = typename E::T;
+  using elt8 = typename E::V8;
+  using C = DkdvPairCfg<D, BQ, 8>;
+  __shared__ __attribute__((aligned(16))) elt Qs[3][BQ * D];
+  __shared__ __attribute__((aligned(16))) elt dOs[3][BQ * D];
+  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+  // P and dS fragments handed to the partner wave, [plane][pair][fragment][lane]:
+  // for tile t the leading waves write plane t % 2, the lagging ones plane 2
+  __shared__ __attribute__((aligned(16))) elt8 Xs[3][C::NP][4][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int pr = wave % C::NP;   // key block of the pair
+  const int half = wave / C::NP; // query half for S/dP, feature half for dK/dV
+  const bool lead = half == 0;   // the leading wave of the pair
+
+  const WgOrder wo = wg_order(blockIdx.x, B * H, n_ktiles);
+  const int kt = wo.rank;
+  const int bh = wo.bh;
+  const int b = bh / H;
+  const int h = bh - b * H;
+  const SeqSpan sp = seq_span(b, h, H, n_q, n_k, cu_q, cu_k, total_q, total_k);
+  const int N = sp.nq, Nk = sp.nk;
+  if (kt * C::BK >= Nk) return;
+  const elt* Qh = Q + sp.q_row0 * D;
+  const elt* Kh = K + sp.k_row0 * D;
+  const elt* Vh = V + sp.k_row0 * D;
+  const elt* dOh = dO + sp.q_row0 * D;
+  const float* Lh = LSE + sp.q_row0;
+  const float* Dh = Dlt + sp.q_row0;
+  elt* dKh = dK + sp.k_row0 * D;
+  elt* dVh = dV + sp.k_row0 * D;
+
+  const int kv_len = key_length(seqlens_k, b, Nk);
+  const int off = Nk - N;
+  const int k0 = kt * C::BK;
+  const int kw0 = k0 + pr * 32;
+  const int my_key = kw0 + l32;
+  const int q_begin = causal ? (max(0, k0 - off) / BQ) * BQ : 0;
+  const int n_qt = (k0 < kv_len && q_begin < N) ? (N - q_begin + BQ - 1) / BQ : 0;
+
+  elt8 kf[C::KS], vf[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    if (my_key < kv_len) {
+      kf[ks] = *reinterpret_cast<const elt8*>(Kh + (size_t)my_key * D + ks * 16 + hi * 8);
+      vf[ks] = *reinterpret_cast<const elt8*>(Vh + (size_t)my_key * D + ks * 16 + hi * 8);
+    } else {
+      kf[ks] = elt8{};
+      vf[ks] = elt8{};
+    }
+  }
+  f32x16 dkacc[C::HDB], dvacc[C::HDB];
+#pragma unroll
+  for (int j = 0; j < C::HDB; ++j) {
+    dkacc[j] = f32x16{};
+    dvacc[j] = f32x16{};
+  }
+
+  // Staging as in the kernel above, but only the lagging group copies (its
+  // vector stage is the shorter one), into slot t % 3; its first wave loads
+  // the tile's statistics (one row per lane) ahead of the copies.
+  auto kSwz = [](int row) FA_INLINE { return tile_swizzle<D>(row); };
+  const int ts = lane & 15;
+  const int tcol = ((lane >> 4) & 1) * 16 + 4 * (ts & 3);
+  auto colfrag = [&](const elt* tile, int g, int db) FA_INLINE {
+    const int r0 = 16 * g + 4 * hi + (ts >> 2);
+    const int r1 = r0 + 8;
+    const int col = db * 32 + tcol;
+    const s16x4 lo = read_tr16(tile + r0 * D + ((col >> 3) ^ tile_swizzle<D>(r0)) * 8 + (col & 7));
+    const s16x4 up = read_tr16(tile + r1 * D + ((col >> 3) ^ tile_swizzle<D>(r1)) * 8 + (col & 7));
+    return __builtin_bit_cast(elt8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  constexpr int kChunksPerRow = D / 8;
+  constexpr int kBlksPerTensor = BQ * D * 2 / 1024;
+  constexpr int kCopyWaves = C::NW / 2;
+  constexpr int kBlksPerWave = 2 * kBlksPerTensor / kCopyWaves;
+  static_assert(BQ * D * 2 % 1024 == 0 && 2 * kBlksPerTensor % kCopyWaves == 0,
+                "whole 1 KiB blocks per copying wave");
+  static_assert(BQ == 64, "one statistics row per lane");
+  const int head_bytes = N * D * 2;
+  const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(Qh, head_bytes);
+  const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(dOh, head_bytes);
+  const bool stat_wave = wave == C::NP;
+  float lreg = 0.f, dreg = 0.f;
+  auto issue_tile = [&](int t, int slot) FA_INLINE {
+    const int qt0 = q_begin + t * BQ;
+    if (stat_wave) {
+      const int row = qt0 + lane;
+      lreg = row < N ? Lh[row] : __builtin_huge_valf();
+      dreg = row < N ? Dh[row] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kBlksPerWave; ++j) {
+      const int blk = (wave - C::NP) * kBlksPerWave + j;
+      const bool is_q = blk < kBlksPerTensor;
+      const int rb = is_q ? blk : blk - kBlksPerTensor;
+      const int pos = rb * 64 + lane;
+      const int row = pos / kChunksPerRow;
+      const int chunk = (pos % kChunksPerRow) ^ kSwz(row);
+      const int voff = (qt0 + row) * (D * 2) + chunk * 16;
+      elt* dst = (is_q ? Qs[slot] : dOs[slot]) + rb * 512;
+      lds_dma16_tracked(is_q ? q_rsrc : o_rsrc, dst, voff);
+    }
+  };
+
+  auto store_stats = [&](int t) FA_INLINE {
+    if (stat_wave) {
+      Ls[t & 1][lane] = (lreg == kNegInf) ? __builtin_huge_valf() : lreg * kLog2e;
+      Ds[t & 1][lane] = dreg;
+    }
+  };
+
+  const bool pair_keys_valid = kw0 < kv_len;
+  auto active = [&](int t) FA_INLINE {
+    return pair_keys_valid && (!causal || q_begin + t * BQ + BQ - 1 + off >= kw0);
+  };
+  // The leading waves are the pairs' first halves and the lagging waves the
+  // second, so each loop below passes its half as a compile-time constant.
+  // M1: S and dP for this wave's 32 query rows (one key per lane)
+  constexpr int kM1Pre = 4;
+  auto m1 = [&](auto half_tag, int slot, f32x16& sacc, f32x16& pacc) FA_INLINE {
+    constexpr int HF = decltype(half_tag)::value;
+    sacc = f32x16{};
+    pacc = f32x16{};
+    const int arow = 32 * HF + l32;
+    const int asw = kSwz(arow);
+    // fragments in MFMA order f = (ks, tensor), read kM1Pre MFMAs ahead
+    constexpr int NF = 2 * C::KS;
+    auto frag = [&](int f) FA_INLINE {
+      const int ro = arow * D + ((2 * (f >> 1) + hi) ^ asw) * 8;
+      return *reinterpret_cast<const elt8*>((f & 1) ? &dOs[slot][ro] : &Qs[slot][ro]);
+    };
+    elt8 ring[kM1Pre];
+#pragma unroll
+    for (int f = 0; f < kM1Pre; ++f) ring[f] = frag(f);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const elt8 fr = ring[f % kM1Pre];
+      if (f + kM1Pre < NF) ring[f % kM1Pre] = frag(f + kM1Pre);
+      if (f & 1)
+        pacc = E::mfma(fr, vf[f >> 1], pacc);
+      else
+        sacc = E::mfma(fr, kf[f >> 1], sacc);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kM1Pre, 0);
+#pragma unroll
+    for (int f = 0; f < NF - kM1Pre; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kM1Pre, 0);
+  };
+  // V: P = exp(S - LSE) and dS = P (dP - D), rounded to the element format
+  auto vstage = [&](auto half_tag, int t, const f32x16& sacc, const f32x16& pacc,
+                    elt8 (&pa)[2], elt8 (&dsa)[2]) FA_INLINE {
+    constexpr int HF = decltype(half_tag)::value;
+    const int qt0 = q_begin + t * BQ;
+    const int sb = t & 1;
+    const int first_vis =
+        my_key >= kv_len ? BQ : (causal ? my_key - off - qt0 - 4 * hi : -BQ);
+    auto p_and_ds = [&](auto masked_tag) FA_INLINE {
+      constexpr bool kMasked = decltype(masked_tag)::value;
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int r0 = 32 * HF + 8 * a4 + 4 * hi;
+        const f32x4 lq = *reinterpret_cast<const f32x4*>(&Ls[sb][r0]);
+        const f32x4 dq = *reinterpret_cast<const f32x4*>(&Ds[sb][r0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * a4 + e;
+          float p = fast_exp2(__builtin_fmaf(sacc[v], scale_log2, -lq[e]));
+          if (kMasked) p = (32 * HF + 8 * a4 + e >= first_vis) ? p : 0.f;
+          pa[v >> 3][v & 7] = E::cvt(p);
+          dsa[v >> 3][v & 7] = E::cvt(p * (pacc[v] - dq[e]));
+        }
+      }
+    };
+    if ((kw0 + 31 >= kv_len) || (causal && qt0 + 32 * HF + off < kw0 + 31))
+      p_and_ds(std::true_type{});
+    else
+      p_and_ds(std::false_type{});
+  };
+  auto hand_over = [&](int plane, const elt8 (&pa)[2], const elt8 (&dsa)[2]) FA_INLINE {
+    Xs[plane][pr][0][lane] = pa[0];
+    Xs[plane][pr][1][lane] = pa[1];
+    Xs[plane][pr][2][lane] = dsa[0];
+    Xs[plane][pr][3][lane] = dsa[1];
+  };
+  auto take_back = [&](int plane, elt8 (&pa)[2], elt8 (&dsa)[2]) FA_INLINE {
+    pa[0] = Xs[plane][pr][0][lane];
+    pa[1] = Xs[plane][pr][1][lane];
+    dsa[0] = Xs[plane][pr][2][lane];
+    dsa[1] = Xs[plane][pr][3][lane];
+  };
+  // Element offsets of this lane's two transposing reads (rows r and r + 8,
+  // r = 16 g + 4 hi + ts / 4) for each of its feature blocks, for even and odd
+  // 16-row groups g: the swizzles of d <= 128 see no row bit above 4, so
+  // groups g and g + 2 differ by 32 rows, an immediate offset.
+  int tr_at[C::HDB][2][2];
+#pragma unroll
+  for (int j = 0; j < C::HDB; ++j)
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int row = 16 * par + 4 * hi + (ts >> 2) + 8 * u;
+        const int col = (half * C::HDB + j) * 32 + tcol;
+        tr_at[j][par][u] = row * D + ((col >> 3) ^ tile_swizzle<D>(row)) * 8 + (col & 7);
+      }
+  // M2: dV += P^T dO, dK += dS^T Q over all 64 rows, own feature half.  The
+  // column fragments are read kM2Pre MFMAs ahead of their use: in this stage
+  // the wave's partner runs vector work, so no second wave hides the reads.
+  constexpr int kM2Pre = 4;
+  auto m2 = [&](auto half_tag, int slot, const elt8 (&pa)[2], const elt8 (&dsa)[2],
+                int partner_plane) FA_INLINE {
+    constexpr int HF = decltype(half_tag)::value;
+    // feature blocks of this half (at d = 96 the first half takes two, the second one)
+    constexpr int NB = (C::NDB % 2 == 0 || HF == 0) ? C::HDB : C::NDB - C::HDB;
+    elt8 po[2], dso[2];
+    take_back(partner_plane, po, dso);
+    const elt* qt = Qs[slot];
+    const elt* ot = dOs[slot];
+    // fragments in MFMA order f = (g, j, tensor); tensor 0: dO (for dV), 1: Q (for dK)
+    constexpr int NF = C::NG * NB * 2;
+    auto frag = [&](int f) FA_INLINE {
+      const int g = f / (2 * NB), j = (f / 2) % NB;
+      const elt* base = ((f & 1) ? qt : ot) + (g >> 1) * 32 * D;
+      const s16x4 lo = read_tr16(base + tr_at[j][g & 1][0]);
+      const s16x4 up = read_tr16(base + tr_at[j][g & 1][1]);
+      return __builtin_bit_cast(elt8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    elt8 ring[kM2Pre];
+#pragma unroll
+    for (int f = 0; f < kM2Pre; ++f) ring[f] = frag(f);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int g = f / (2 * NB), j = (f / 2) % NB;
+      const elt8 fr = ring[f % kM2Pre];
+      if (f + kM2Pre < NF) ring[f % kM2Pre] = frag(f + kM2Pre);
+      // row groups 2 HF and 2 HF + 1 are this wave's, the others its partner's
+      const bool own = (g >> 1) == HF;
+      if (f & 1)
+        dkacc[j] = E::mfma(own ? dsa[g & 1] : dso[g & 1], fr, dkacc[j]);
+      else
+        dvacc[j] = E::mfma(own ? pa[g & 1] : po[g & 1], fr, dvacc[j]);
+    }
+    // keep the fragment reads kM2Pre MFMAs ahead of their consumers
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * kM2Pre, 0);
+#pragma unroll
+    for (int f = 0; f < NF - kM2Pre; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kM2Pre, 0);
+  };
+
+  // Each group runs its own loop (2 n + 3 barriers in both).  M1 runs for
+  // every tile, also where the pair sees none of it (its values then go
+  // unused), so S and dP are never carried across the dV/dK stage.
+  constexpr std::integral_constant<int, 0> kLeadHalf{};
+  constexpr std::integral_constant<int, 1> kLagHalf{};
+  if (n_qt > 0) {
+    f32x16 sacc, pacc;
+    elt8 pa[2] = {}, dsa[2] = {};   // this wave's P and dS of its latest V stage
+    if (lead) {
+      lds_barrier();   // tile 0 and its statistics
+      lds_barrier();   // stage P (the lagging group's M1(0))
+      int slot = 0;  // tile t's slot, t % 3
+      for (int t = 0; t < n_qt; ++t) {
+        const int prev = slot == 0 ? 2 : slot - 1;
+        // ---- stage X(t): M2(t - 1), M1(t)
+        if (t >= 1 && active(t - 1)) m2(kLeadHalf, prev, pa, dsa, 2);
+        m1(kLeadHalf, slot, sacc, pacc);
+        lds_barrier();
+        // ---- stage Y(t): V(t), then hand P and dS over
+        if (active(t)) {
+          vstage(kLeadHalf, t, sacc, pacc, pa, dsa);
+          hand_over(t & 1, pa, dsa);
+        }
+        lds_barrier();
+        slot = slot == 2 ? 0 : slot + 1;
+      }
+      // ---- stage X(n): M2(n - 1)
+      if (active(n_qt - 1)) m2(kLeadHalf, slot == 0 ? 2 : slot - 1, pa, dsa, 2);
+      lds_barrier();
+    } else {
+      issue_tile(0, 0);
+      wait_vmem();
+      store_stats(0);
+      lds_barrier();
+      // ---- stage P: M1(0)
+      m1(kLagHalf, 0, sacc, pacc);
+      lds_barrier();
+      int slot = 0;
+      for (int t = 0; t < n_qt; ++t) {
+        const int prev = slot == 0 ? 2 : slot - 1;
+        const int next = slot == 2 ? 0 : slot + 1;
+        // ---- stage X(t): copy tile t + 1, V(t)
+        if (t + 1 < n_qt) issue_tile(t + 1, next);
+        if (active(t)) vstage(kLagHalf, t, sacc, pacc, pa, dsa);
+        // tile t + 1 has landed once every wave passes the barrier
+        wait_vmem();
+        if (t + 1 < n_qt) store_stats(t + 1);
+        lds_barrier();
+        // ---- stage Y(t): M2(t - 1), M1(t + 1) (after the last tile, M1 of a
+        // stale slot, unused).  This wave's own P and dS of tile t - 1 are
+        // read back from its exchange plane before tile t's overwrite them.
+        elt8 pb[2], dsb[2];
+        take_back(2, pb, dsb);
+        if (active(t)) hand_over(2, pa, dsa);
+        if (t >= 1 && active(t - 1)) m2(kLagHalf, prev, pb, dsb, (t - 1) & 1);
+        m1(kLagHalf, next, sacc, pacc);
+        lds_barrier();
+        slot = next;
+      }
+      // ---- stage X(n): nothing; stage Y(n): M2(n - 1)
+      lds_barrier();
+      if (active(n_qt - 1)) m2(kLagHalf, slot == 0 ? 2 : slot - 1, pa, dsa, (n_qt - 1) & 1);
+    }
+  }
+
+  // ---- write dK = scale * acc, dV = acc for this wave's feature half
+#pragma unroll
+  for (int j = 0; j < C::HDB; ++j) {
+    const int db = half * C::HDB + j;
+    if (C::NDB % 2 != 0 && db >= C::NDB) break;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = kw0 + c_row(v, lane);
+      if (key < Nk) {
+        dKh[(size_t)key * D + db * 32 + l32] = E::cvt(dkacc[j][v] * scale);
+        dVh[(size_t)key * D + db * 32 + l32] = E::cvt(dvacc[j][v]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 3. dQ
 // ---------------------------------------------------------------------------
 template <int D, int NW, int BC>
@@ -625,6 +1008,16 @@ hipError_t launch_dkdv_d(const BwdArgs& a) {
   using T = typename E::T;
   const int n_ktiles = (a.Nk + CK::BK - 1) / CK::BK;
   if (n_ktiles == 0) return hipSuccess;   // no keys: dK and dV have no rows
+  if constexpr (FA_DKDV_PINGPONG && BwdWaves<D>::DKDV == 8) {
+    hipLaunchKernelGGL((fa_bwd_dkdv_pp_kernel<E, D, 64>),
+                       dim3((unsigned)((long long)n_ktiles * a.B * a.H)), dim3(CK::NT), 0,
+                       a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
+                       a.seqlens_k, a.scale, a.scale * kLog2e, a.causal, static_cast<T*>(a.dk),
+                       static_cast<T*>(a.dv), a.B, a.H, a.N, a.Nk, n_ktiles,
+                       a.cu_q, a.cu_k, a.total_q, a.total_k);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<E, D, 64, BwdWaves<D>::DKDV>),
                      dim3((unsigned)((long long)n_ktiles * a.B * a.H)), dim3(CK::NT), 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
