@@ -408,11 +408,12 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
 //   stage X(t): leading wave  M2(t-1), M1(t)       lagging wave  V(t)
 //   stage Y(t): leading wave  V(t)                 lagging wave  M2(t-1), M1(t+1)
 // A leading wave hands its P and dS over at the end of its V stage, into
-// one of two exchange planes (by tile parity); a lagging wave, at the start
-// of the stage after its V stage, into a single plane, after reading back its
-// own P and dS of the tile before (the 160 KiB of LDS hold a second plane
-// for one group only).  Exchange writes inside an MFMA stage cost that stage
-// several hundred cycles.  Tile t is read from stage Y(t-1) to Y(t+1), so
+// one of two exchange planes (by tile parity).  A lagging wave writes its dS
+// there too (two planes by parity) but its P at the start of the stage after
+// its V stage, into a single plane, after reading back its own P of the tile
+// before: the 160 KiB of LDS hold the tiles and all but one of the second
+// planes.  Exchange writes inside an MFMA stage cost that stage several
+// hundred cycles.  Tile t is read from stage Y(t-1) to Y(t+1), so
 // the Q/dO tiles take three LDS slots, and the lagging group copies tile t+1
 // (and stores its statistics) during stage X(t).  Each MFMA stage is one
 // wave's: its operand reads run four MFMAs ahead of their use.
@@ -438,9 +439,12 @@ void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
   __shared__ __attribute__((aligned(16))) elt dOs[3][BQ * D];
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
-  // P and dS fragments handed to the partner wave, [plane][pair][fragment][lane]:
-  // for tile t the leading waves write plane t % 2, the lagging ones plane 2
-  __shared__ __attribute__((aligned(16))) elt8 Xs[3][C::NP][4][64];
+  // P and dS fragments handed to the partner wave, [plane][pair][fragment][lane]
+  // (fragments 0-1: P, 2-3: dS): for tile t the leading waves write plane t % 2;
+  // the lagging waves write their P to XP and their dS to XD[t % 2]
+  __shared__ __attribute__((aligned(16))) elt8 Xs[2][C::NP][4][64];
+  __shared__ __attribute__((aligned(16))) elt8 XP[C::NP][2][64];
+  __shared__ __attribute__((aligned(16))) elt8 XD[2][C::NP][2][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -618,17 +622,14 @@ void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
     else
       p_and_ds(std::false_type{});
   };
-  auto hand_over = [&](int plane, const elt8 (&pa)[2], const elt8 (&dsa)[2]) FA_INLINE {
-    Xs[plane][pr][0][lane] = pa[0];
-    Xs[plane][pr][1][lane] = pa[1];
-    Xs[plane][pr][2][lane] = dsa[0];
-    Xs[plane][pr][3][lane] = dsa[1];
+  // two fragments at [2][64] elt8 (fragment-major, one 16-byte piece per lane)
+  auto put2 = [&](elt8* dst, const elt8 (&v)[2]) FA_INLINE {
+    dst[lane] = v[0];
+    dst[64 + lane] = v[1];
   };
-  auto take_back = [&](int plane, elt8 (&pa)[2], elt8 (&dsa)[2]) FA_INLINE {
-    pa[0] = Xs[plane][pr][0][lane];
-    pa[1] = Xs[plane][pr][1][lane];
-    dsa[0] = Xs[plane][pr][2][lane];
-    dsa[1] = Xs[plane][pr][3][lane];
+  auto get2 = [&](const elt8* src, elt8 (&v)[2]) FA_INLINE {
+    v[0] = src[lane];
+    v[1] = src[64 + lane];
   };
   // Element offsets of this lane's two transposing reads (rows r and r + 8,
   // r = 16 g + 4 hi + ts / 4) for each of its feature blocks, for even and odd
@@ -650,12 +651,13 @@ void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
   // the wave's partner runs vector work, so no second wave hides the reads.
   constexpr int kM2Pre = 4;
   auto m2 = [&](auto half_tag, int slot, const elt8 (&pa)[2], const elt8 (&dsa)[2],
-                int partner_plane) FA_INLINE {
+                const elt8* po_src, const elt8* dso_src) FA_INLINE {
     constexpr int HF = decltype(half_tag)::value;
     // feature blocks of this half (at d = 96 the first half takes two, the second one)
     constexpr int NB = (C::NDB % 2 == 0 || HF == 0) ? C::HDB : C::NDB - C::HDB;
     elt8 po[2], dso[2];
-    take_back(partner_plane, po, dso);
+    get2(po_src, po);
+    get2(dso_src, dso);
     const elt* qt = Qs[slot];
     const elt* ot = dOs[slot];
     // fragments in MFMA order f = (g, j, tensor); tensor 0: dO (for dV), 1: Q (for dK)
@@ -707,19 +709,23 @@ void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
       for (int t = 0; t < n_qt; ++t) {
         const int prev = slot == 0 ? 2 : slot - 1;
         // ---- stage X(t): M2(t - 1), M1(t)
-        if (t >= 1 && active(t - 1)) m2(kLeadHalf, prev, pa, dsa, 2);
+        if (t >= 1 && active(t - 1))
+          m2(kLeadHalf, prev, pa, dsa, &XP[pr][0][0], &XD[(t - 1) & 1][pr][0][0]);
         m1(kLeadHalf, slot, sacc, pacc);
         lds_barrier();
         // ---- stage Y(t): V(t), then hand P and dS over
         if (active(t)) {
           vstage(kLeadHalf, t, sacc, pacc, pa, dsa);
-          hand_over(t & 1, pa, dsa);
+          put2(&Xs[t & 1][pr][0][0], pa);
+          put2(&Xs[t & 1][pr][2][0], dsa);
         }
         lds_barrier();
         slot = slot == 2 ? 0 : slot + 1;
       }
       // ---- stage X(n): M2(n - 1)
-      if (active(n_qt - 1)) m2(kLeadHalf, slot == 0 ? 2 : slot - 1, pa, dsa, 2);
+      if (active(n_qt - 1))
+        m2(kLeadHalf, slot == 0 ? 2 : slot - 1, pa, dsa, &XP[pr][0][0],
+           &XD[(n_qt - 1) & 1][pr][0][0]);
       lds_barrier();
     } else {
       issue_tile(0, 0);
@@ -735,7 +741,10 @@ void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
         const int next = slot == 2 ? 0 : slot + 1;
         // ---- stage X(t): copy tile t + 1, V(t)
         if (t + 1 < n_qt) issue_tile(t + 1, next);
-        if (active(t)) vstage(kLagHalf, t, sacc, pacc, pa, dsa);
+        if (active(t)) {
+          vstage(kLagHalf, t, sacc, pacc, pa, dsa);
+          put2(&XD[t & 1][pr][0][0], dsa);
+        }
         // tile t + 1 has landed once every wave passes the barrier
         wait_vmem();
         if (t + 1 < n_qt) store_stats(t + 1);
@@ -744,16 +753,20 @@ void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
         // stale slot, unused).  This wave's own P and dS of tile t - 1 are
         // read back from its exchange plane before tile t's overwrite them.
         elt8 pb[2], dsb[2];
-        take_back(2, pb, dsb);
-        if (active(t)) hand_over(2, pa, dsa);
-        if (t >= 1 && active(t - 1)) m2(kLagHalf, prev, pb, dsb, (t - 1) & 1);
+        get2(&XP[pr][0][0], pb);
+        get2(&XD[(t - 1) & 1][pr][0][0], dsb);
+        if (active(t)) put2(&XP[pr][0][0], pa);
+        if (t >= 1 && active(t - 1))
+          m2(kLagHalf, prev, pb, dsb, &Xs[(t - 1) & 1][pr][0][0], &Xs[(t - 1) & 1][pr][2][0]);
         m1(kLagHalf, next, sacc, pacc);
         lds_barrier();
         slot = next;
       }
       // ---- stage X(n): nothing; stage Y(n): M2(n - 1)
       lds_barrier();
-      if (active(n_qt - 1)) m2(kLagHalf, slot == 0 ? 2 : slot - 1, pa, dsa, (n_qt - 1) & 1);
+      if (active(n_qt - 1))
+        m2(kLagHalf, slot == 0 ? 2 : slot - 1, pa, dsa, &Xs[(n_qt - 1) & 1][pr][0][0],
+           &Xs[(n_qt - 1) & 1][pr][2][0]);
     }
   }
 
