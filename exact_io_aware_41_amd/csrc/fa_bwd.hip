@@ -504,14 +504,6 @@ void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
   auto kSwz = [](int row) FA_INLINE { return tile_swizzle<D>(row); };
   const int ts = lane & 15;
   const int tcol = ((lane >> 4) & 1) * 16 + 4 * (ts & 3);
-  auto colfrag = [&](const elt* tile, int g, int db) FA_INLINE {
-    const int r0 = 16 * g + 4 * hi + (ts >> 2);
-    const int r1 = r0 + 8;
-    const int col = db * 32 + tcol;
-    const s16x4 lo = read_tr16(tile + r0 * D + ((col >> 3) ^ tile_swizzle<D>(r0)) * 8 + (col & 7));
-    const s16x4 up = read_tr16(tile + r1 * D + ((col >> 3) ^ tile_swizzle<D>(r1)) * 8 + (col & 7));
-    return __builtin_bit_cast(elt8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
   constexpr int kChunksPerRow = D / 8;
   constexpr int kBlksPerTensor = BQ * D * 2 / 1024;
   constexpr int kCopyWaves = C::NW / 2;
@@ -750,8 +742,8 @@ void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
         if (t + 1 < n_qt) store_stats(t + 1);
         lds_barrier();
         // ---- stage Y(t): M2(t - 1), M1(t + 1) (after the last tile, M1 of a
-        // stale slot, unused).  This wave's own P and dS of tile t - 1 are
-        // read back from its exchange plane before tile t's overwrite them.
+        // stale slot, unused).  This wave's own P of tile t - 1 is read back
+        // from XP before tile t's overwrites it, its dS from XD[(t - 1) % 2].
         elt8 pb[2], dsb[2];
         get2(&XP[pr][0][0], pb);
         get2(&XD[(t - 1) & 1][pr][0][0], dsb);
