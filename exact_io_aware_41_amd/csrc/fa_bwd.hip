@@ -120,6 +120,13 @@ struct DkdvPairCfg {
   static_assert(BQ == 64, "two 32-row halves per tile");
 };
 
+// LDS operand reads of the in-step dK/dV and the dQ kernels run this many
+// MFMAs ahead of their use
+#ifndef FA_BWD_PREFETCH
+#define FA_BWD_PREFETCH 4
+#endif
+constexpr int kPre = FA_BWD_PREFETCH;
+
 template <class E, int D, int BQ, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1)))
@@ -280,17 +287,37 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
 
     elt8 pa[2], dsa[2];
     if (pair_active) {
-      // ---- phase 1: S and dP for this wave's 32 query rows (one key per lane)
+      // ---- phase 1: S and dP for this wave's 32 query rows (one key per lane);
+      // fragments in MFMA order f = (ks, tensor), read kPre MFMAs ahead (with
+      // one wave per SIMD, d > 128, nothing else hides their latency)
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       const int arow = 32 * half + l32;
       const int asw = kSwz(arow);
+      {
+        constexpr int NF = 2 * C::KS;
+        auto frag = [&](int f) FA_INLINE {
+          const int ro = arow * D + ((2 * (f >> 1) + hi) ^ asw) * 8;
+          return *reinterpret_cast<const elt8*>((f & 1) ? &dOs[buf][ro] : &Qs[buf][ro]);
+        };
+        elt8 ring[kPre];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const int ro = arow * D + ((2 * ks + hi) ^ asw) * 8;
-        const elt8 qa = *reinterpret_cast<const elt8*>(&Qs[buf][ro]);
-        const elt8 oa = *reinterpret_cast<const elt8*>(&dOs[buf][ro]);
-        sacc = E::mfma(qa, kf[ks], sacc);
-        pacc = E::mfma(oa, vf[ks], pacc);
+        for (int f = 0; f < kPre; ++f) ring[f] = frag(f);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const elt8 fr = ring[f % kPre];
+          if (f + kPre < NF) ring[f % kPre] = frag(f + kPre);
+          if (f & 1)
+            pacc = E::mfma(fr, vf[f >> 1], pacc);
+          else
+            sacc = E::mfma(fr, kf[f >> 1], sacc);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+        for (int f = 0; f < NF - kPre; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
       }
       // this lane's key is visible from tile row 32 half + 8 a4 + 4 hi + e iff
       // 32 half + 8 a4 + e >= first_vis
@@ -334,46 +361,44 @@ void fa_bwd_dkdv_pair_kernel(const typename E::T* __restrict__ Q,
       dso[1] = Xs[partner][3][lane];
       // NB feature blocks from db0 (a compile-time count, so that at d = 96,
       // where the pair's waves take two blocks and one, each wave still runs
-      // one straight-line schedule)
+      // one straight-line schedule); column fragments in MFMA order (g, j,
+      // tensor), read kPre MFMAs ahead.  (Splitting this per half, so that the
+      // own/partner choice is static, crashed the compiler at d = 256.)
       auto accumulate = [&](auto nb_tag, int db0) FA_INLINE {
         constexpr int NB = decltype(nb_tag)::value;
+        constexpr int NF = C::NG * NB * 2;
+        auto frag = [&](int f) FA_INLINE {
+          const int g = f / (2 * NB), j = (f / 2) % NB;
+          return colfrag((f & 1) ? Qs[buf] : dOs[buf], g, db0 + j);
+        };
+        elt8 ring[kPre];
 #pragma unroll
-        for (int g = 0; g < C::NG; ++g) {
-          // groups 2*half, 2*half+1 are this wave's rows; the others the partner's
+        for (int f = 0; f < kPre; ++f) ring[f] = frag(f);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int g = f / (2 * NB), j = (f / 2) % NB;
+          const elt8 fr = ring[f % kPre];
+          if (f + kPre < NF) ring[f % kPre] = frag(f + kPre);
           const bool own = (g >> 1) == half;
-          const elt8 pfrag = own ? pa[g & 1] : po[g & 1];
-          const elt8 dsfrag = own ? dsa[g & 1] : dso[g & 1];
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const int db = db0 + j;
-            const elt8 ob = colfrag(dOs[buf], g, db);
-            const elt8 qbv = colfrag(Qs[buf], g, db);
-            dvacc[j] = E::mfma(pfrag, ob, dvacc[j]);
-            dkacc[j] = E::mfma(dsfrag, qbv, dkacc[j]);
-          }
+          if (f & 1)
+            dkacc[j] = E::mfma(own ? dsa[g & 1] : dso[g & 1], fr, dkacc[j]);
+          else
+            dvacc[j] = E::mfma(own ? pa[g & 1] : po[g & 1], fr, dvacc[j]);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
+#pragma unroll
+        for (int f = 0; f < NF - kPre; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
       };
-      if constexpr (C::NDB % 2 == 0) {
-#pragma unroll
-        for (int g = 0; g < C::NG; ++g) {
-          // groups 2*half, 2*half+1 are this wave's rows; the others the partner's
-          const bool own = (g >> 1) == half;
-          const elt8 pfrag = own ? pa[g & 1] : po[g & 1];
-          const elt8 dsfrag = own ? dsa[g & 1] : dso[g & 1];
-#pragma unroll
-          for (int j = 0; j < C::HDB; ++j) {
-            const int db = half * C::HDB + j;
-            const elt8 ob = colfrag(dOs[buf], g, db);
-            const elt8 qbv = colfrag(Qs[buf], g, db);
-            dvacc[j] = E::mfma(pfrag, ob, dvacc[j]);
-            dkacc[j] = E::mfma(dsfrag, qbv, dkacc[j]);
-          }
-        }
-      } else if (half == 0) {
+      if constexpr (C::NDB % 2 == 0)
+        accumulate(std::integral_constant<int, C::HDB>{}, half * C::HDB);
+      else if (half == 0)
         accumulate(std::integral_constant<int, C::HDB>{}, 0);
-      } else {
+      else
         accumulate(std::integral_constant<int, C::NDB - C::HDB>{}, C::HDB);
-      }
     }
     // the next tile's row-major copy has landed once every wave passes here
     wait_vmem();
@@ -805,6 +830,10 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
   using elt8 = typename E::V8;
   using elt4 = typename E::V4;
   using C = DqCfg<D, NW, BC>;
+  // operand prefetch depth: with one wave per SIMD (d > 128) nothing else
+  // hides the LDS latency; with two, the plain in-order loops are kept (a
+  // ring measured 3-5 % slower there)
+  constexpr int kRing = NW >= 8 ? 1 : kPre;
   // row-major K and V tiles in two slots (one read, one being loaded)
   __shared__ __attribute__((aligned(16))) elt Ks[2][BC * D];
   __shared__ __attribute__((aligned(16))) elt Vs[2][BC * D];
@@ -926,17 +955,48 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
         sacc[c] = f32x16{};
         pacc[c] = f32x16{};
       }
+      if constexpr (kRing == 1) {
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
+        for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-        for (int c = 0; c < C::NCB; ++c) {
+          for (int c = 0; c < C::NCB; ++c) {
+            const int arow = c * 32 + l32;
+            const int ro = arow * D + ((2 * ks + hi) ^ tile_swizzle<D>(arow)) * 8;
+            const elt8 ka = *reinterpret_cast<const elt8*>(&Ks[slot][ro]);
+            const elt8 va = *reinterpret_cast<const elt8*>(&Vs[slot][ro]);
+            sacc[c] = E::mfma(ka, qf[ks], sacc[c]);
+            pacc[c] = E::mfma(va, of[ks], pacc[c]);
+          }
+      } else {
+        // fragments in MFMA order f = (ks, c, tensor), read kRing MFMAs ahead
+        constexpr int NF = C::KS * C::NCB * 2;
+        auto frag = [&](int f) FA_INLINE {
+          const int ks = f / (2 * C::NCB), c = (f / 2) % C::NCB;
           const int arow = c * 32 + l32;
           const int ro = arow * D + ((2 * ks + hi) ^ tile_swizzle<D>(arow)) * 8;
-          const elt8 ka = *reinterpret_cast<const elt8*>(&Ks[slot][ro]);
-          const elt8 va = *reinterpret_cast<const elt8*>(&Vs[slot][ro]);
-          sacc[c] = E::mfma(ka, qf[ks], sacc[c]);
-          pacc[c] = E::mfma(va, of[ks], pacc[c]);
+          return *reinterpret_cast<const elt8*>((f & 1) ? &Vs[slot][ro] : &Ks[slot][ro]);
+        };
+        elt8 ring[kRing];
+#pragma unroll
+        for (int f = 0; f < kRing; ++f) ring[f] = frag(f);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int ks = f / (2 * C::NCB), c = (f / 2) % C::NCB;
+          const elt8 fr = ring[f % kRing];
+          if (f + kRing < NF) ring[f % kRing] = frag(f + kRing);
+          if (f & 1)
+            pacc[c] = E::mfma(fr, of[ks], pacc[c]);
+          else
+            sacc[c] = E::mfma(fr, qf[ks], sacc[c]);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, kRing, 0);
+#pragma unroll
+        for (int f = 0; f < NF - kRing; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kRing, 0);
+      }
       // only tiles crossing the key length or the wave's diagonal are masked:
       // key key0 + 32c + 4hi + p, p = 8(v/4) + v%4, is visible iff it is at
       // most min(L - 1, this lane's query); S = -inf gives P = 0
@@ -960,12 +1020,33 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
           dsb[2 * c + (v >> 3)][v & 7] = E::cvt(p * (pacc[c][v] - drow));
         }
       // ---- dQ^T += K^T dS^T
+      if constexpr (kRing == 1) {
 #pragma unroll
-      for (int g = 0; g < C::NG; ++g)
+        for (int g = 0; g < C::NG; ++g)
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          dqacc[db] = E::mfma(colfrag(Ks[slot], g, db), dsb[g], dqacc[db]);
+          for (int db = 0; db < C::NDB; ++db)
+            dqacc[db] = E::mfma(colfrag(Ks[slot], g, db), dsb[g], dqacc[db]);
+      } else {
+        // K^T fragments in MFMA order (g, db), read kRing MFMAs ahead
+        constexpr int NF = C::NG * C::NDB;
+        auto frag = [&](int f) FA_INLINE { return colfrag(Ks[slot], f / C::NDB, f % C::NDB); };
+        elt8 ring[kRing];
+#pragma unroll
+        for (int f = 0; f < kRing; ++f) ring[f] = frag(f);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const elt8 fr = ring[f % kRing];
+          if (f + kRing < NF) ring[f % kRing] = frag(f + kRing);
+          dqacc[f % C::NDB] = E::mfma(fr, dsb[f / C::NDB], dqacc[f % C::NDB]);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kRing, 0);
+#pragma unroll
+        for (int f = 0; f < NF - kRing; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kRing, 0);
+      }
     }
     // the next tile has landed once every wave passes here
     wait_vmem();
