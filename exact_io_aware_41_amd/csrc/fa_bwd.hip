@@ -1068,6 +1068,15 @@ void fa_bwd_dq_kernel(const typename E::T* __restrict__ Q, const typename E::T* 
 }
 
 constexpr int kDqBC = FA_DQ_BC;
+// key tile of the dQ kernel per head dimension: at d = 64 its registers hold
+// twice the S/dP tile, which halves the barriers per key
+#ifndef FA_DQ_BC64
+#define FA_DQ_BC64 128
+#endif
+template <int D>
+struct DqTile {
+  static constexpr int BC = D == 64 ? FA_DQ_BC64 : kDqBC;
+};
 // waves per work-group of the two main backward kernels: up to d = 128 two
 // waves share a SIMD; at d = 256 one wave per SIMD holds the larger operands
 template <int D>
@@ -1116,11 +1125,11 @@ hipError_t launch_dkdv_d(const BwdArgs& a) {
 
 template <class E, int D>
 hipError_t launch_dq_d(const BwdArgs& a) {
-  using CQ = DqCfg<D, BwdWaves<D>::DQ, kDqBC>;
+  using CQ = DqCfg<D, BwdWaves<D>::DQ, DqTile<D>::BC>;
   using T = typename E::T;
   const int n_qtiles = (a.N + CQ::BR - 1) / CQ::BR;
   if (n_qtiles == 0) return hipSuccess;   // no queries: dQ has no rows
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, BwdWaves<D>::DQ, kDqBC>),
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, BwdWaves<D>::DQ, DqTile<D>::BC>),
                      dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(CQ::NT), 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
