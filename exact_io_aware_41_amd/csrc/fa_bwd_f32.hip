@@ -116,8 +116,13 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
   constexpr int NT = NW * 64;
   constexpr int BK = NW * 32;       // keys per work-group
   constexpr int QT = 32;            // query rows per tile
-  __shared__ __attribute__((aligned(16))) float Ks[BK * C::PITCH];
-  __shared__ __attribute__((aligned(16))) float Vs[BK * C::PITCH];
+  // up to d = 128 each lane keeps the K and V features of its key that it
+  // supplies to the MFMAs (2 ks + hi) in registers, so LDS holds only the
+  // Q and dO tiles and two work-groups share a CU; at d = 256 K and V stay
+  // in LDS
+  constexpr bool kRegKV = D <= 128;
+  __shared__ __attribute__((aligned(16))) float Ks[kRegKV ? 4 : BK * C::PITCH];
+  __shared__ __attribute__((aligned(16))) float Vs[kRegKV ? 4 : BK * C::PITCH];
   __shared__ __attribute__((aligned(16))) float Qs[QT * C::PITCH];
   __shared__ __attribute__((aligned(16))) float dOs[QT * C::PITCH];
   __shared__ float Ls[QT], Ds[QT];
@@ -148,8 +153,18 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
   const int kw0 = k0 + wave * 32;           // this wave's first key
   const int my_key = kw0 + l32;
 
-  load_rows<D>(Ks, Kh, k0, BK, kv_len, tid, NT);
-  load_rows<D>(Vs, Vh, k0, BK, kv_len, tid, NT);
+  float kreg[kRegKV ? C::KS : 1], vreg[kRegKV ? C::KS : 1];
+  if constexpr (kRegKV) {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bool live = my_key < kv_len;   // keys past the length never enter a product
+      kreg[ks] = live ? Kh[(size_t)my_key * D + 2 * ks + hi] : 0.f;
+      vreg[ks] = live ? Vh[(size_t)my_key * D + 2 * ks + hi] : 0.f;
+    }
+  } else {
+    load_rows<D>(Ks, Kh, k0, BK, kv_len, tid, NT);
+    load_rows<D>(Vs, Vh, k0, BK, kv_len, tid, NT);
+  }
 
   f32x16 dvacc[C::NDB], dkacc[C::NDB];
 #pragma unroll
@@ -184,13 +199,22 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
 
     // S[q][key] = Q K^T and dP[q][key] = dO V^T: lane = key, v = query row
     f32x16 sacc = f32x16{}, pacc = f32x16{};
+    if constexpr (kRegKV) {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const int col = 2 * ks + hi;
+        sacc = mfma_f32(Qs[l32 * C::PITCH + col], kreg[ks], sacc);
+        pacc = mfma_f32(dOs[l32 * C::PITCH + col], vreg[ks], pacc);
+      }
+    } else {
 #pragma unroll 8
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const int col = 2 * ks + hi;
-      const float kb_op = Kw[l32 * C::PITCH + col];
-      const float vb_op = Vw[l32 * C::PITCH + col];
-      sacc = mfma_f32(Qs[l32 * C::PITCH + col], kb_op, sacc);
-      pacc = mfma_f32(dOs[l32 * C::PITCH + col], vb_op, pacc);
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const int col = 2 * ks + hi;
+        const float kb_op = Kw[l32 * C::PITCH + col];
+        const float vb_op = Vw[l32 * C::PITCH + col];
+        sacc = mfma_f32(Qs[l32 * C::PITCH + col], kb_op, sacc);
+        pacc = mfma_f32(dOs[l32 * C::PITCH + col], vb_op, pacc);
+      }
     }
     const bool need_mask =
         (kw0 + 31 >= kv_len) || (causal && qt0 + off < kw0 + 31) || qt0 + QT > N;
