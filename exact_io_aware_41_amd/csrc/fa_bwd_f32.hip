@@ -260,8 +260,14 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
     }
 }
 
+// dQ: at d >= 192 one wave per SIMD holds the query's Q and dO rows in
+// registers (the loop below fully unrolled); below, two or three waves per
+// SIMD read them from scratch memory (L1-resident) in a loop unrolled by 8,
+// which measured faster there (d = 128: 27 against 24 TFLOP/s; d = 256: 17
+// against 23 the other way round)
 template <int D, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+__attribute__((amdgpu_waves_per_eu(1, D >= 192 ? 1 : 8)))
 void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                           const float* __restrict__ V, const float* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Dlt,
@@ -323,15 +329,22 @@ void fa_bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__
     const bool active = qw0 < N && (!causal || key0 <= qw0 + 31 + off);
     if (!active) continue;
 
-    // S^T = K Q^T, dP^T = V dO^T: lane = query, v = key.  Unrolled by 8: the
-    // Q and dO rows then sit in scratch memory (L1-resident), which measured
-    // 15 % faster at d = 128 than a full unroll holding them in registers
+    // S^T = K Q^T, dP^T = V dO^T: lane = query, v = key
     f32x16 sacc = f32x16{}, pacc = f32x16{};
+    if constexpr (D >= 192) {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const int col = 2 * ks + hi;
+        sacc = mfma_f32(Ks[l32 * C::PITCH + col], qf[ks], sacc);
+        pacc = mfma_f32(Vs[l32 * C::PITCH + col], of[ks], pacc);
+      }
+    } else {
 #pragma unroll 8
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const int col = 2 * ks + hi;
-      sacc = mfma_f32(Ks[l32 * C::PITCH + col], qf[ks], sacc);
-      pacc = mfma_f32(Vs[l32 * C::PITCH + col], of[ks], pacc);
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const int col = 2 * ks + hi;
+        sacc = mfma_f32(Ks[l32 * C::PITCH + col], qf[ks], sacc);
+        pacc = mfma_f32(Vs[l32 * C::PITCH + col], of[ks], pacc);
+      }
     }
     const bool need_mask = (key0 + BC > kv_len) || (causal && key0 + BC - 1 > qw0 + off);
     float ds[16];
