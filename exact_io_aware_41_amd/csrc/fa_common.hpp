@@ -337,9 +337,9 @@ struct WgOrder {
 };
 
 // Debug builds (FA_WG_PERMUTE) visit the work-group ids in a scrambled
-// order, id -> id * P mod n for a prime P (n the grid size; the reversed order
-// when P divides n).  Every kernel computes each tile independently of the
-// others, so results must not change by a single bit.
+// order, id -> id * P mod n for a prime P (n the number of ids; the reversed
+// order when P divides n).  Every kernel computes each tile independently of
+// the others, so results must not change by a single bit.
 #ifndef FA_WG_PERMUTE
 #define FA_WG_PERMUTE 0
 #endif
@@ -349,9 +349,8 @@ constexpr bool is_prime(unsigned n) {
     if (n % p == 0) return false;
   return true;
 }
-__device__ __forceinline__ int scheduled_wg(int wg) {
+__device__ __forceinline__ int scheduled_wg(int wg, unsigned n) {
 #if FA_WG_PERMUTE
-  const unsigned n = gridDim.x;
   constexpr unsigned kP = 40009u;
   static_assert(is_prime(kP), "id -> id * P mod n is a permutation only for P coprime with n");
   if (n % kP != 0) return (int)(((unsigned long long)(unsigned)wg * kP) % n);
@@ -362,7 +361,7 @@ __device__ __forceinline__ int scheduled_wg(int wg) {
 }
 
 __device__ __forceinline__ WgOrder wg_order(int wg_id, int bh_count, int n_tiles) {
-  const int wg = scheduled_wg(wg_id);
+  const int wg = scheduled_wg(wg_id, (unsigned)bh_count * (unsigned)n_tiles);
   WgOrder o;
   if (FA_XCD_GROUP > 0 && (bh_count & 7) == 0) {
     const int x = wg & 7, k = wg >> 3;
@@ -383,6 +382,42 @@ __device__ __forceinline__ WgOrder wg_order(int wg_id, int bh_count, int n_tiles
     o.bh = wg - o.rank * bh_count;
   }
   return o;
+}
+
+// Persistent kernels (one work-group per slot running a list of tiles) take
+// their arguments as one struct, which sits at the start of the
+// kernel-argument segment, and read the fields where each job needs them.
+// The segment pointer goes through an opaque copy, so the compiler issues
+// those scalar loads again per job instead of holding every argument in
+// scalar registers across the whole job loop.
+template <class A>
+__device__ __forceinline__ const __attribute__((address_space(4))) A* job_args() {
+  const unsigned long long u = (unsigned long long)__builtin_amdgcn_kernarg_segment_ptr();
+  unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+  unsigned up = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+  asm volatile("" : "+s"(lo), "+s"(up));
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  up = __builtin_amdgcn_readfirstlane(up);
+  return (const __attribute__((address_space(4))) A*)(((unsigned long long)up << 32) | lo);
+}
+// A pointer read from that struct, marked as global memory again (pointer
+// kernel arguments are; pointers loaded from memory are not)
+template <typename T>
+__device__ __forceinline__ T* global_ptr(T* p) {
+  return (T*)(__attribute__((address_space(1))) T*)p;
+}
+
+// Job j of a persistent launch with `slots` work-groups (a multiple of 8,
+// one per XCD lane): work-group w runs on XCD w % 8 and takes that XCD's ids
+// k = 0, 1, ... (job k * 8 + w % 8) in passes of slots / 8, alternating the
+// direction of each pass, so that with the ids ordered longest first every
+// work-group's list adds up to about the same work.  Returns -1 past the end.
+__device__ __forceinline__ int persistent_job(int pass, int n_jobs) {
+  const int per_xcd = (int)(gridDim.x >> 3);
+  const int x = (int)(blockIdx.x & 7u), i = (int)(blockIdx.x >> 3);
+  const int k = pass * per_xcd + ((pass & 1) ? per_xcd - 1 - i : i);
+  const long long j = (long long)k * 8 + x;
+  return j < n_jobs ? (int)j : -1;
 }
 
 struct TileCoord {

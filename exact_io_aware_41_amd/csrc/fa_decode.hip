@@ -123,7 +123,7 @@ void fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   __shared__ float red[KPS * D];
   __shared__ float scratch[4];
 
-  const int wg = scheduled_wg(blockIdx.x);
+  const int wg = scheduled_wg(blockIdx.x, gridDim.x);
   const int part = wg % n_parts;
   const int bh = wg / n_parts;
   const int b = bh / H;

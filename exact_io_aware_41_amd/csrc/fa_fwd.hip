@@ -96,15 +96,28 @@ struct FwdBf16Cfg {
 // accumulators are rescaled only when the maximum really jumps.
 constexpr float kRescaleThreshold = 8.0f;
 
+// Arguments of the 16-bit kernel, passed as one struct (see job_args).
+template <typename T>
+struct FwdHalfArgs {
+  const T* q;
+  const T* k;
+  const T* v;
+  const int32_t* seqlens_k;
+  T* o;
+  float* lse;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  float scale_log2;
+  int causal;
+  int B, H, n_q, n_k, n_qtiles, total_q, total_k;
+  int n_jobs;    // query tiles over every (sequence, head)
+  int persist;   // 1: work-group w runs jobs persistent_job(0..) instead of job w
+};
+
 template <class E, int D, int QB, int NW, int BC>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(QB == 1 && D <= 128 ? 2 : 1, QB == 1 && D <= 128 ? 2 : 1)))
-void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
-                        const typename E::T* __restrict__ V, const int32_t* __restrict__ seqlens_k,
-                        float scale_log2, int causal, typename E::T* __restrict__ O,
-                        float* __restrict__ LSE, int B, int H, int n_q, int n_k,
-                        int n_qtiles, const int32_t* __restrict__ cu_q,
-                        const int32_t* __restrict__ cu_k, int total_q, int total_k) {
+void fa_fwd_half_kernel(const FwdHalfArgs<typename E::T> args [[maybe_unused]]) {
   using elt = typename E::T;
   using elt8 = typename E::V8;
   using elt4 = typename E::V4;
@@ -129,10 +142,27 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
   const int hi = lane >> 5;
   const bool lagging = kPingPong && wave >= NW / 2;
 
-  const TileCoord tc = tile_coord(blockIdx.x, B, H, n_qtiles);
-  const SeqSpan sp = seq_span(tc.b, tc.h, H, n_q, n_k, cu_q, cu_k, total_q, total_k);
+  // one job (query tile) per pass; a persistent launch runs several
+  for (int pass = 0;; ++pass) {
+  const auto* ka = job_args<FwdHalfArgs<elt>>();
+  const int job = ka->persist ? persistent_job(pass, ka->n_jobs) : (pass == 0 ? (int)blockIdx.x : -1);
+  if (job < 0) break;
+  // every wave is done with the previous job's tiles before this one's copies
+  if (pass > 0) __syncthreads();
+  const elt* __restrict__ Q = global_ptr(ka->q);
+  const elt* __restrict__ K = global_ptr(ka->k);
+  const elt* __restrict__ V = global_ptr(ka->v);
+  const int32_t* __restrict__ seqlens_k = global_ptr(ka->seqlens_k);
+  elt* __restrict__ O = global_ptr(ka->o);
+  float* __restrict__ LSE = global_ptr(ka->lse);
+  const float scale_log2 = ka->scale_log2;
+  const int causal = ka->causal;
+  const int B = ka->B, H = ka->H;
+  const TileCoord tc = tile_coord(job, B, H, ka->n_qtiles);
+  const SeqSpan sp = seq_span(tc.b, tc.h, H, ka->n_q, ka->n_k, global_ptr(ka->cu_q),
+                              global_ptr(ka->cu_k), ka->total_q, ka->total_k);
   const int N = sp.nq, Nk = sp.nk;   // this sequence's query and key rows
-  if (tc.qt * C::BR >= N) return;    // a query tile past a shorter sequence
+  if (tc.qt * C::BR >= N) continue;  // a query tile past a shorter sequence
   const elt* Qh = Q + sp.q_row0 * D;
   const elt* Kh = K + sp.k_row0 * D;
   const elt* Vh = V + sp.k_row0 * D;
@@ -252,8 +282,18 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
   };
   auto no_dma = [](int) FA_INLINE {};
 
+  // defined at every job: left undefined, the previous job's values would be
+  // carried around the job loop and these registers never freed
   f32x16 sacc[C::NCB][QB];
   elt8 pf[C::NG][QB];
+#pragma unroll
+  for (int c = 0; c < C::NCB; ++c)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) sacc[c][qb] = f32x16{};
+#pragma unroll
+  for (int g = 0; g < C::NG; ++g)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) pf[g][qb] = elt8{};
 
   // S^T(t) = K(t) Q^T.  The K fragments are read from LDS kPre reads ahead of
   // the MFMA that consumes them, so LDS latency overlaps the MFMA pipeline.
@@ -491,6 +531,7 @@ void fa_fwd_half_kernel(const typename E::T* __restrict__ Q, const typename E::T
         Lh[q] = lt > 0.f ? (m[qb] + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
     }
   }
+  }  // job loop
 }
 
 // ---------------------------------------------------------------------------
@@ -819,12 +860,46 @@ hipError_t launch_half_d(const FwdArgs& a) {
   using C = FwdBf16Cfg<D, kBf16QB, NW, BC>;
   using T = typename E::T;
   const int n_qtiles = (a.N + C::BR - 1) / C::BR;
-  const dim3 grid((unsigned)((long long)n_qtiles * a.B * a.H));
+  const long long n_jobs = (long long)n_qtiles * a.B * a.H;
+  // Sequences of one length: a persistent launch, as many work-groups as fit
+  // on the chip at once, each running a fixed list of query tiles (no gaps
+  // between tiles waiting for the dispatcher).  Key lengths or packed
+  // sequences keep one work-group per tile, placed by the dispatcher.
+  static const int slots = [] {
+    int dev = 0, n_cu = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&fa_fwd_half_kernel<E, D, kBf16QB, NW, BC>),
+            C::NT, 0) != hipSuccess)
+      return 0;
+    return (n_cu * per_cu) / 8 * 8;
+  }();
+  const bool persist =
+      a.seqlens_k == nullptr && a.cu_q == nullptr && slots >= 8 && n_jobs > slots;
+  FwdHalfArgs<T> ka;
+  ka.q = static_cast<const T*>(a.q);
+  ka.k = static_cast<const T*>(a.k);
+  ka.v = static_cast<const T*>(a.v);
+  ka.seqlens_k = a.seqlens_k;
+  ka.o = static_cast<T*>(a.o);
+  ka.lse = a.lse;
+  ka.cu_q = a.cu_q;
+  ka.cu_k = a.cu_k;
+  ka.scale_log2 = a.scale * kLog2e;
+  ka.causal = a.causal;
+  ka.B = a.B;
+  ka.H = a.H;
+  ka.n_q = a.N;
+  ka.n_k = a.Nk;
+  ka.n_qtiles = n_qtiles;
+  ka.total_q = a.total_q;
+  ka.total_k = a.total_k;
+  ka.n_jobs = (int)n_jobs;
+  ka.persist = persist ? 1 : 0;
+  const dim3 grid((unsigned)(persist ? slots : n_jobs));
   hipLaunchKernelGGL((fa_fwd_half_kernel<E, D, kBf16QB, NW, BC>), grid, dim3(C::NT), 0,
-                     a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), a.seqlens_k, a.scale * kLog2e, a.causal,
-                     static_cast<T*>(a.o), a.lse, a.B, a.H, a.N, a.Nk, n_qtiles,
-                     a.cu_q, a.cu_k, a.total_q, a.total_k);
+                     a.stream, ka);
   return hipGetLastError();
 }
 
