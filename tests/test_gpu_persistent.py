@@ -7,7 +7,10 @@ the kernel's schedule must not change what it computes).  For every head
 dimension and both masks, at 20 heads and 8192 rows (640 to 1280 query tiles):
 
 * bit for bit against the same problem given as a packed batch of one
-  sequence, which keeps one work-group per query tile;
+  sequence, which keeps one work-group per query tile, and against the
+  race-check library (every copy destination filled with NaN before the copy,
+  jobs taken in a scrambled order), where a job that read a ring slot the
+  previous or next job of its work-group still used would show;
 * the first and last row of every 128-row block and a few random rows of
   three heads against the fp64 oracle, one row at a time (O <= 2e-2 for bf16,
   5e-3 for f16; LSE within the forward tolerances).
@@ -46,9 +49,14 @@ def test_persistent_forward_matches_per_tile_launch_and_oracle(dtype, d, causal,
     cu = torch.tensor([0, N], dtype=torch.int32, device="cuda")
     o_p, lse_p = fa.forward_varlen(dev["q"][0], dev["k"][0], dev["v"][0], cu, cu, N, N,
                                    scale=cfg.scale, causal=causal)
+    with fa.library(fa.load_debug_library()):
+        o_d, lse_d = fa.forward(dev["q"], dev["k"], dev["v"], scale=cfg.scale, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o[0], o_p), "O differs from the one-work-group-per-tile launch"
     assert torch.equal(lse[0], lse_p), "LSE differs from the one-work-group-per-tile launch"
+    assert not o_d.float().isnan().any().item(), "NaN under the race-check library"
+    assert torch.equal(o, o_d), "O differs under the race-check library"
+    assert torch.equal(lse, lse_d), "LSE differs under the race-check library"
 
     got_o, got_l = from_device(o[0], dtype), lse[0].cpu().numpy().astype(np.float64)
     rng = np.random.default_rng(d + 7 * H)
