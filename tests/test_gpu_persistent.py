@@ -4,7 +4,9 @@ A padded problem (no key lengths) with more query tiles than the chip holds
 work-groups at once runs one work-group per slot, each working through a
 fixed list of query tiles ("FlashAttention", "Checking it on a real system":
 the kernel's schedule must not change what it computes).  For every head
-dimension and both masks, at 20 heads and 8192 rows (640 to 1280 query tiles):
+dimension and both masks, at 16 to 24 heads and 8192 rows (512 to 1536 query
+tiles), and for ragged lengths, two sequences, and fewer or more keys than
+queries (so that some jobs see no key at all):
 
 * bit for bit against the same problem given as a packed batch of one
   sequence, which keeps one work-group per query tile, and against the
@@ -27,7 +29,50 @@ from tests.gpu_helpers import (LSE_TOL, check_lse, custom, from_device, lib, log
 pytestmark = pytest.mark.gpu
 
 O_TOL = {"bf16": 2e-2, "f16": 5e-3}
-N = 8192
+
+
+def _check(dtype, d, causal, B, H, Nq, Nk, seed=11):
+    torch = torch_cuda()
+    fa = lib()
+    log_case(test="persistent-forward", dtype=dtype, d=d, causal=causal, B=B, H=H, Nq=Nq, Nk=Nk)
+    cfg = custom(3, d=d, dtype=dtype, B=B, H=H, N=Nq)
+    t = {"q": fi.make_tensor(cfg, "q", seed=seed, d=d, N=Nq)}
+    t.update({n: fi.make_tensor(cfg, n, seed=seed, d=d, N=Nk) for n in ("k", "v")})
+    dev = {n: to_device(torch, t[n], dtype) for n in t}
+    o, lse = fa.forward(dev["q"], dev["k"], dev["v"], scale=cfg.scale, causal=causal)
+
+    # the same problem as a packed batch: one work-group per query tile
+    packed = {n: dev[n].permute(1, 0, 2, 3).reshape(H, -1, d).contiguous() for n in dev}
+    cu_q = torch.arange(0, B + 1, dtype=torch.int32, device="cuda") * Nq
+    cu_k = torch.arange(0, B + 1, dtype=torch.int32, device="cuda") * Nk
+    o_p, lse_p = fa.forward_varlen(packed["q"], packed["k"], packed["v"], cu_q, cu_k, Nq, Nk,
+                                   scale=cfg.scale, causal=causal)
+    with fa.library(fa.load_debug_library()):
+        o_d, lse_d = fa.forward(dev["q"], dev["k"], dev["v"], scale=cfg.scale, causal=causal)
+    torch.cuda.synchronize()
+    o_pb = o_p.reshape(H, B, Nq, d).permute(1, 0, 2, 3)
+    lse_pb = lse_p.reshape(H, B, Nq).permute(1, 0, 2)
+    assert torch.equal(o, o_pb), "O differs from the one-work-group-per-tile launch"
+    assert torch.equal(lse, lse_pb), "LSE differs from the one-work-group-per-tile launch"
+    assert not o_d.float().isnan().any().item(), "NaN under the race-check library"
+    assert torch.equal(o, o_d), "O differs under the race-check library"
+    assert torch.equal(lse, lse_d), "LSE differs under the race-check library"
+
+    got_o, got_l = from_device(o, dtype), lse.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(d + 7 * H + Nq + 3 * Nk)
+    edges = np.arange(0, Nq, 128)
+    rows = np.unique(np.concatenate([edges, np.minimum(edges + 127, Nq - 1), [Nq - 1],
+                                     rng.integers(0, Nq, 8)]))
+    for b, h in ((0, 0), (B - 1, int(rng.integers(1, H - 1))), (B - 1, H - 1)):
+        q = fi.widen(t["q"][b, h], dtype)
+        k = fi.widen(t["k"][b, h], dtype)
+        v = fi.widen(t["v"][b, h], dtype)
+        ref_o, ref_l = oracle.attention_rows(q, k, v, rows, cfg.scale, causal)
+        err = max_abs(got_o[b, h, rows], ref_o)
+        print(f"(b, h) = ({b}, {h}): max |O - ref| = {err:.3e} over {len(rows)} rows", flush=True)
+        assert err <= O_TOL[dtype]
+        check_lse(got_l[b, h, rows], ref_l, *LSE_TOL[dtype])
+        assert np.all(got_o[b, h, rows][np.isneginf(ref_l)] == 0.0)
 
 
 @pytest.mark.parametrize("dtype, d, causal, H", [
@@ -38,36 +83,15 @@ N = 8192
     ("bf16", 256, True, 20), ("bf16", 256, False, 16),
 ])
 def test_persistent_forward_matches_per_tile_launch_and_oracle(dtype, d, causal, H):
-    torch = torch_cuda()
-    fa = lib()
-    log_case(test="persistent-forward", dtype=dtype, d=d, causal=causal, H=H, N=N)
-    cfg = custom(3, d=d, dtype=dtype, H=H, N=N)
-    t = {n: fi.make_tensor(cfg, n, seed=11, d=d) for n in ("q", "k", "v")}
-    dev = {n: to_device(torch, t[n], dtype) for n in t}
-    o, lse = fa.forward(dev["q"], dev["k"], dev["v"], scale=cfg.scale, causal=causal)
+    _check(dtype, d, causal, 1, H, 8192, 8192)
 
-    cu = torch.tensor([0, N], dtype=torch.int32, device="cuda")
-    o_p, lse_p = fa.forward_varlen(dev["q"][0], dev["k"][0], dev["v"][0], cu, cu, N, N,
-                                   scale=cfg.scale, causal=causal)
-    with fa.library(fa.load_debug_library()):
-        o_d, lse_d = fa.forward(dev["q"], dev["k"], dev["v"], scale=cfg.scale, causal=causal)
-    torch.cuda.synchronize()
-    assert torch.equal(o[0], o_p), "O differs from the one-work-group-per-tile launch"
-    assert torch.equal(lse[0], lse_p), "LSE differs from the one-work-group-per-tile launch"
-    assert not o_d.float().isnan().any().item(), "NaN under the race-check library"
-    assert torch.equal(o, o_d), "O differs under the race-check library"
-    assert torch.equal(lse, lse_d), "LSE differs under the race-check library"
 
-    got_o, got_l = from_device(o[0], dtype), lse[0].cpu().numpy().astype(np.float64)
-    rng = np.random.default_rng(d + 7 * H)
-    edges = np.arange(0, N, 128)
-    rows = np.unique(np.concatenate([edges, edges + 127, rng.integers(0, N, 8)]))
-    for h in (0, int(rng.integers(1, H - 1)), H - 1):
-        q = fi.widen(t["q"][0, h], dtype)
-        k = fi.widen(t["k"][0, h], dtype)
-        v = fi.widen(t["v"][0, h], dtype)
-        ref_o, ref_l = oracle.attention_rows(q, k, v, rows, cfg.scale, causal)
-        err = max_abs(got_o[h, rows], ref_o)
-        print(f"head {h}: max |O - ref| = {err:.3e} over {len(rows)} rows", flush=True)
-        assert err <= O_TOL[dtype]
-        check_lse(got_l[h, rows], ref_l, *LSE_TOL[dtype])
+@pytest.mark.parametrize("d, causal, B, H, Nq, Nk", [
+    (128, True, 2, 12, 8000, 8000),    # ragged last query tile, two sequences (24 heads)
+    (128, True, 1, 20, 8192, 4096),    # fewer keys: the first 4096 queries see none
+    (128, True, 1, 20, 4096, 8192),    # more keys than queries
+    (96, False, 1, 20, 6000, 3000),
+    (256, True, 1, 16, 5000, 6000),
+])
+def test_persistent_forward_ragged_and_rectangular(d, causal, B, H, Nq, Nk):
+    _check("bf16", d, causal, B, H, Nq, Nk, seed=13)
