@@ -505,17 +505,9 @@ void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
   const int q_begin = causal ? (max(0, k0 - off) / BQ) * BQ : 0;
   const int n_qt = (k0 < kv_len && q_begin < N) ? (N - q_begin + BQ - 1) / BQ : 0;
 
+  // this pair's K and V rows as MFMA fragments (one key per lane), read from
+  // LDS in the prologue (see copy_kv)
   elt8 kf[C::KS], vf[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    if (my_key < kv_len) {
-      kf[ks] = *reinterpret_cast<const elt8*>(Kh + (size_t)my_key * D + ks * 16 + hi * 8);
-      vf[ks] = *reinterpret_cast<const elt8*>(Vh + (size_t)my_key * D + ks * 16 + hi * 8);
-    } else {
-      kf[ks] = elt8{};
-      vf[ks] = elt8{};
-    }
-  }
   f32x16 dkacc[C::HDB], dvacc[C::HDB];
 #pragma unroll
   for (int j = 0; j < C::HDB; ++j) {
@@ -559,6 +551,47 @@ void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
       const int voff = (qt0 + row) * (D * 2) + chunk * 16;
       elt* dst = (is_q ? Qs[slot] : dOs[slot]) + rb * 512;
       lds_dma16_tracked(is_q ? q_rsrc : o_rsrc, dst, voff);
+    }
+  };
+
+  // The work-group's K and V blocks (128 keys) go to LDS with the tiles'
+  // coalesced, swizzled direct loads, into the ring slots 1 and 2 of Qs and
+  // dOs that no tile uses before the second prologue barrier (one block
+  // fills exactly two slots), and each wave then reads its pair's fragments
+  // from there.  Loaded straight into registers, each load instruction took
+  // 32 rows x 32 bytes and the fragments landed about 10,700 cycles after
+  // the work-group started, against 1,900 for a tile copy.  Keys at or past
+  // the key length read as zeros (the descriptors end there).
+  static_assert(C::BK == 2 * BQ, "a key block fills two ring slots");
+  constexpr int kKvBlks = C::BK * D * 2 / 1024;            // 1 KiB blocks per tensor
+  constexpr int kKvBlksPerWave = 2 * kKvBlks / C::NW;
+  static_assert(2 * kKvBlks % C::NW == 0, "whole 1 KiB blocks per wave");
+  elt* const kblk = &Qs[1][0];
+  elt* const vblk = &dOs[1][0];
+  auto copy_kv = [&]() FA_INLINE {
+    const int kv_bytes = max(0, min(kv_len - k0, C::BK)) * D * 2;
+    const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(Kh + (size_t)k0 * D, kv_bytes);
+    const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(Vh + (size_t)k0 * D, kv_bytes);
+#pragma unroll
+    for (int j = 0; j < kKvBlksPerWave; ++j) {
+      const int blk = wave * kKvBlksPerWave + j;
+      const bool is_k = blk < kKvBlks;
+      const int rb = is_k ? blk : blk - kKvBlks;
+      const int pos = rb * 64 + lane;
+      const int row = pos / kChunksPerRow;
+      const int chunk = (pos % kChunksPerRow) ^ kSwz(row);
+      lds_dma16_tracked(is_k ? k_rsrc : v_rsrc, (is_k ? kblk : vblk) + rb * 512,
+                        row * (D * 2) + chunk * 16);
+    }
+  };
+  auto read_kv = [&]() FA_INLINE {
+    const int row = pr * 32 + l32;
+    const int sw = kSwz(row);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int at = row * D + ((2 * ks + hi) ^ sw) * 8;
+      kf[ks] = *reinterpret_cast<const elt8*>(&kblk[at]);
+      vf[ks] = *reinterpret_cast<const elt8*>(&vblk[at]);
     }
   };
 
@@ -720,8 +753,11 @@ void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
     f32x16 sacc, pacc;
     elt8 pa[2] = {}, dsa[2] = {};   // this wave's P and dS of its latest V stage
     if (lead) {
-      lds_barrier();   // tile 0 and its statistics
-      lds_barrier();   // stage P (the lagging group's M1(0))
+      copy_kv();
+      wait_vmem();
+      lds_barrier();   // the K/V block, tile 0 and its statistics
+      read_kv();
+      lds_barrier();   // stage P (the lagging group's M1(0)); the K/V block's slots are free again
       int slot = 0;  // tile t's slot, t % 3
       for (int t = 0; t < n_qt; ++t) {
         const int prev = slot == 0 ? 2 : slot - 1;
@@ -745,10 +781,12 @@ void fa_bwd_dkdv_pp_kernel(const typename E::T* __restrict__ Q,
            &XD[(n_qt - 1) & 1][pr][0][0]);
       lds_barrier();
     } else {
+      copy_kv();
       issue_tile(0, 0);
       wait_vmem();
       store_stats(0);
       lds_barrier();
+      read_kv();
       // ---- stage P: M1(0)
       m1(kLagHalf, 0, sacc, pacc);
       lds_barrier();
