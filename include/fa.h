@@ -141,6 +141,11 @@ const char* fa_status_string(fa_status s);
  *   stream     HIP stream the work is enqueued on (0 = default stream)
  * Rows that see no key get o = 0 and lse = -inf.  Nq = 0 writes nothing;
  * Nk = 0 writes those empty rows.
+ * Launch: bf16 and f16 problems without key lengths and with more query
+ * tiles than the device holds work-groups at once run a persistent grid (as
+ * many work-groups as fit, each working through a fixed list of query
+ * tiles); the result is bit for bit that of one work-group per tile.  Other
+ * work running on the device at the same time only delays it.
  */
 fa_status fa_forward(fa_dtype dtype, int B, int H, int Nq, int Nk, int d,
                      const void* q, const void* k, const void* v,
