@@ -43,6 +43,7 @@
 //    tiles that cross the diagonal or the key length apply the mask, on
 //    absolute positions.
 
+#include <atomic>
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -853,6 +854,29 @@ struct Bf16Tile {
 };
 constexpr int kF32NW = 2, kF32BC = 32;
 
+// Work-groups of `kernel` (`threads` each) resident at once on the device of
+// `stream`, rounded down to a multiple of 8 (one XCD lane each); 0 when the
+// runtime cannot tell.  Cached per device id in `cache` (0: not known yet,
+// -1: not available).
+constexpr int kSlotCacheDevices = 64;
+inline int persistent_slots(const void* kernel, int threads, hipStream_t stream,
+                            std::atomic<int>* cache) {
+  int dev = 0;
+  if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess) return 0;
+  const bool cached = dev >= 0 && dev < kSlotCacheDevices;
+  int v = cached ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (v == 0) {
+    int n_cu = 0, per_cu = 0;
+    v = (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) == hipSuccess)
+            ? (n_cu * per_cu) / 8 * 8
+            : 0;
+    if (v <= 0) v = -1;
+    if (cached) cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v > 0 ? v : 0;
+}
+
 template <class E, int D>
 hipError_t launch_half_d(const FwdArgs& a) {
   constexpr int BC = Bf16Tile<D>::BC;
@@ -865,16 +889,10 @@ hipError_t launch_half_d(const FwdArgs& a) {
   // on the chip at once, each running a fixed list of query tiles (no gaps
   // between tiles waiting for the dispatcher).  Key lengths or packed
   // sequences keep one work-group per tile, placed by the dispatcher.
-  static const int slots = [] {
-    int dev = 0, n_cu = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&fa_fwd_half_kernel<E, D, kBf16QB, NW, BC>),
-            C::NT, 0) != hipSuccess)
-      return 0;
-    return (n_cu * per_cu) / 8 * 8;
-  }();
+  static std::atomic<int> slots_cache[kSlotCacheDevices];
+  const int slots = persistent_slots(
+      reinterpret_cast<const void*>(&fa_fwd_half_kernel<E, D, kBf16QB, NW, BC>), C::NT, a.stream,
+      slots_cache);
   const bool persist =
       a.seqlens_k == nullptr && a.cu_q == nullptr && slots >= 8 && n_jobs > slots;
   FwdHalfArgs<T> ka;
