@@ -852,7 +852,14 @@ struct Bf16Tile {
   static constexpr int BC = D <= 128 ? FA_FWD_BC : 64;
   static constexpr int NW = D <= 128 ? FA_FWD_NW : 4;
 };
-constexpr int kF32NW = 2, kF32BC = 32;
+// fp32: 32-key tiles; two waves per work-group, four at d >= 192, where one
+// work-group's two K/V slots (100 and 133 KB) leave room for no second one on
+// the CU, so two waves would leave two SIMDs idle
+constexpr int kF32BC = 32;
+template <int D>
+struct F32Tile {
+  static constexpr int NW = D >= 192 ? 4 : 2;
+};
 
 // Work-groups of `kernel` (`threads` each) resident at once on the device of
 // `stream`, rounded down to a multiple of 8 (one XCD lane each); 0 when the
@@ -935,10 +942,11 @@ hipError_t launch_half_e(const FwdArgs& a) {
 
 template <int D, int KSPLIT>
 hipError_t launch_f32_split(const FwdArgs& a) {
-  using C = FwdF32Cfg<D, kF32NW, kF32BC, KSPLIT>;
+  constexpr int NW = F32Tile<D>::NW;
+  using C = FwdF32Cfg<D, NW, kF32BC, KSPLIT>;
   const int n_qtiles = (a.N + C::BR - 1) / C::BR;
   const dim3 grid((unsigned)((long long)n_qtiles * a.B * a.H));
-  hipLaunchKernelGGL((fa_fwd_f32_kernel<D, kF32NW, kF32BC, KSPLIT>), grid, dim3(C::NT), 0,
+  hipLaunchKernelGGL((fa_fwd_f32_kernel<D, NW, kF32BC, KSPLIT>), grid, dim3(C::NT), 0,
                      a.stream, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), a.seqlens_k, a.scale * kLog2e, a.causal,
                      static_cast<float*>(a.o), a.lse, a.B, a.H, a.N, a.Nk, n_qtiles,
@@ -953,7 +961,8 @@ constexpr long long kF32SplitBelow = 256;
 template <int D>
 hipError_t launch_f32_d(const FwdArgs& a) {
   if constexpr (D == 64) {
-    const long long grid = (long long)((a.N + kF32NW * 32 - 1) / (kF32NW * 32)) * a.B * a.H;
+    constexpr int NW = F32Tile<D>::NW;
+    const long long grid = (long long)((a.N + NW * 32 - 1) / (NW * 32)) * a.B * a.H;
     if (grid < kF32SplitBelow) return launch_f32_split<D, 4>(a);
   }
   return launch_f32_split<D, 1>(a);
@@ -967,8 +976,7 @@ long long fwd_half_grid(int B, int H, int N, int d) {
 }
 
 long long fwd_f32_grid(int B, int H, int N, int d) {
-  const int BR = kF32NW * 32;
-  (void)d;
+  const int BR = (d >= 192 ? F32Tile<256>::NW : F32Tile<128>::NW) * 32;
   return (long long)((N + BR - 1) / BR) * B * H;
 }
 
