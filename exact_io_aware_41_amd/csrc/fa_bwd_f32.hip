@@ -40,7 +40,7 @@ namespace {
 // one at d = 256, where K, V, Q and dO tiles of 64 rows would not fit in LDS
 template <int D>
 struct F32BwdWaves {
-  static constexpr int DKDV = D <= 128 ? 2 : 1;
+  static constexpr int DKDV = D <= 128 ? 2 : 1;   // d >= 192: the split kernel instead
   static constexpr int DQ = 2;
 };
 
@@ -118,7 +118,8 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
   constexpr int QT = 32;            // query rows per tile
   // up to d = 128 each lane keeps the K and V features of its key that it
   // supplies to the MFMAs (2 ks + hi) in registers, so LDS holds only the
-  // Q and dO tiles and two work-groups share a CU; at d = 256 K and V stay
+  // Q and dO tiles and two work-groups share a CU; above (a path the
+  // launcher no longer takes: d >= 192 runs the split kernel) K and V stay
   // in LDS
   constexpr bool kRegKV = D <= 128;
   __shared__ __attribute__((aligned(16))) float Ks[kRegKV ? 4 : BK * C::PITCH];
@@ -260,6 +261,183 @@ void fa_bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict
     }
 }
 
+// dK/dV at d >= 192.  A work-group of one wave per 32 keys would need K, V,
+// Q and dO tiles of 32 rows in LDS (100-133 KB), so one such work-group per
+// CU would leave three SIMDs idle.  Here four waves share the 32 keys and
+// split the feature dimension: wave w holds the K and V features of k-steps
+// w, w + 4, ... in registers and computes the partial S = Q K^T and
+// dP = dO V^T over them; the four partials meet in LDS and every wave adds
+// them in the same order (so all hold the same S and dP), forms P and dS,
+// and accumulates dV += P^T dO and dK += dS^T Q for its feature blocks
+// w, w + 4, ...  Three barriers per query tile.
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void fa_bwd_dkdv_f32_split_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                  const float* __restrict__ V, const float* __restrict__ dO,
+                                  const float* __restrict__ LSE, const float* __restrict__ Dlt,
+                                  const int32_t* __restrict__ seqlens_k, float scale,
+                                  float scale_log2, int causal, float* __restrict__ dK,
+                                  float* __restrict__ dV, int B, int H, int n_q, int n_k,
+                                  int n_kblocks, const int32_t* __restrict__ cu_q,
+                                  const int32_t* __restrict__ cu_k, int total_q, int total_k) {
+  using C = F32BwdCfg<D>;
+  constexpr int NW = 4;
+  constexpr int NT = NW * 64;
+  constexpr int BK = 32;              // keys per work-group
+  constexpr int QT = 32;              // query rows per tile
+  constexpr int KSW = C::KS / NW;     // k-steps per wave
+  constexpr int NBW = (C::NDB + NW - 1) / NW;   // feature blocks per wave (at most)
+  static_assert(C::KS % NW == 0, "k-steps split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) float Qs[QT * C::PITCH];
+  __shared__ __attribute__((aligned(16))) float dOs[QT * C::PITCH];
+  __shared__ float Ls[QT], Ds[QT];
+  // partial S and dP of each wave, [tensor][wave][chunk][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 Xp[2][NW][4][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // key blocks in order: under a causal mask block 0 sees every query tile
+  const WgOrder wo = wg_order(blockIdx.x, B * H, n_kblocks);
+  const int kb = wo.rank;
+  const int bh = wo.bh;
+  const int b = bh / H;
+  const SeqSpan sp = seq_span(b, bh - b * H, H, n_q, n_k, cu_q, cu_k, total_q, total_k);
+  const int N = sp.nq, Nk = sp.nk;   // this sequence's query and key rows
+  if (kb * BK >= Nk) return;         // a key block past a shorter sequence
+  const float* Qh = Q + sp.q_row0 * D;
+  const float* Kh = K + sp.k_row0 * D;
+  const float* Vh = V + sp.k_row0 * D;
+  const float* dOh = dO + sp.q_row0 * D;
+  const float* Lh = LSE + sp.q_row0;
+  const float* Dh = Dlt + sp.q_row0;
+  const int kv_len = key_length(seqlens_k, b, Nk);
+  const int off = Nk - N;   // query i sits at key position i + off
+  const int k0 = kb * BK;
+  const int my_key = k0 + l32;
+
+  // this wave's K and V features (k-steps ks = wave + 4 i) of this lane's key
+  float kreg[KSW], vreg[KSW];
+  {
+    const bool live = my_key < kv_len;   // keys past the length never enter a product
+#pragma unroll
+    for (int i = 0; i < KSW; ++i) {
+      const int col = 2 * (wave + NW * i) + hi;
+      kreg[i] = live ? Kh[(size_t)my_key * D + col] : 0.f;
+      vreg[i] = live ? Vh[(size_t)my_key * D + col] : 0.f;
+    }
+  }
+
+  f32x16 dvacc[NBW], dkacc[NBW];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    dvacc[i] = f32x16{};
+    dkacc[i] = f32x16{};
+  }
+
+  // query tiles that see any key of the block: under the causal mask the
+  // first is the one holding row k0; keys past the length are never visible
+  const int q_begin = causal ? (max(0, k0 - off) / QT) * QT : 0;
+  const bool block_live = k0 < kv_len && q_begin < N;
+  const int n_qt = block_live ? (N - q_begin + QT - 1) / QT : 0;
+
+  for (int qi = 0; qi < n_qt; ++qi) {
+    const int qt0 = q_begin + qi * QT;
+    __syncthreads();   // the previous tile's readers (Q, dO, partials) are done
+    load_rows<D>(Qs, Qh, qt0, QT, N, tid, NT);
+    load_rows<D>(dOs, dOh, qt0, QT, N, tid, NT);
+    if (tid < QT) {
+      const int row = qt0 + tid;
+      Ls[tid] = row < N ? Lh[row] : 0.f;
+      Ds[tid] = row < N ? Dh[row] : 0.f;
+    }
+    __syncthreads();
+
+    // partial S[q][key] and dP[q][key] over this wave's k-steps: lane = key,
+    // v = query row
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+    for (int i = 0; i < KSW; ++i) {
+      const int col = 2 * (wave + NW * i) + hi;
+      sacc = mfma_f32(Qs[l32 * C::PITCH + col], kreg[i], sacc);
+      pacc = mfma_f32(dOs[l32 * C::PITCH + col], vreg[i], pacc);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      Xp[0][wave][c][lane] = f32x4{sacc[4 * c], sacc[4 * c + 1], sacc[4 * c + 2], sacc[4 * c + 3]};
+      Xp[1][wave][c][lane] = f32x4{pacc[4 * c], pacc[4 * c + 1], pacc[4 * c + 2], pacc[4 * c + 3]};
+    }
+    __syncthreads();
+    // the full S and dP: the four partials added in wave order
+    float sf[16], pf[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f32x4 s4 = Xp[0][0][c][lane], p4 = Xp[1][0][c][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        s4 += Xp[0][w][c][lane];
+        p4 += Xp[1][w][c][lane];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sf[4 * c + e] = s4[e];
+        pf[4 * c + e] = p4[e];
+      }
+    }
+
+    const bool need_mask =
+        (k0 + BK - 1 >= kv_len) || (causal && qt0 + off < k0 + BK - 1) || qt0 + QT > N;
+    float p[16], ds[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = c_row(v, lane);
+      float x = fast_exp2(__builtin_fmaf(sf[v], scale_log2, -Ls[r] * kLog2e));
+      if (need_mask) {
+        const int q = qt0 + r;
+        const bool vis = my_key < kv_len && (!causal || my_key <= q + off) && q < N;
+        x = vis ? x : 0.f;
+      }
+      p[v] = x;
+      ds[v] = x * (pf[v] - Ds[r]);
+    }
+    // dV += P^T dO and dK += dS^T Q over this wave's feature blocks: step v
+    // contracts over rows c_row(v, .)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = c_row(v, lane);
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        const int db = wave + NW * i;
+        if (db < C::NDB) {
+          dvacc[i] = mfma_f32(p[v], dOs[r * C::PITCH + db * 32 + l32], dvacc[i]);
+          dkacc[i] = mfma_f32(ds[v], Qs[r * C::PITCH + db * 32 + l32], dkacc[i]);
+        }
+      }
+    }
+  }
+
+  // dV[key][feature], dK = scale * acc: accumulator lane l holds feature
+  // 32 db + l % 32 of keys k0 + c_row(v, l)
+  float* dKh = dK + sp.k_row0 * D;
+  float* dVh = dV + sp.k_row0 * D;
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const int db = wave + NW * i;
+    if (db >= C::NDB) break;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = k0 + c_row(v, lane);
+      if (key < Nk) {
+        dVh[(size_t)key * D + db * 32 + l32] = dvacc[i][v];
+        dKh[(size_t)key * D + db * 32 + l32] = dkacc[i][v] * scale;
+      }
+    }
+  }
+}
+
 // dQ: at d >= 192 one wave per SIMD holds the query's Q and dO rows in
 // registers (the loop below fully unrolled); below, two or three waves per
 // SIMD read them from scratch memory (L1-resident) in a loop unrolled by 8,
@@ -398,18 +576,30 @@ hipError_t launch_preprocess_f32_d(const BwdArgs& a) {
 
 template <int D>
 hipError_t launch_dkdv_f32_d(const BwdArgs& a) {
-  constexpr int NW = F32BwdWaves<D>::DKDV;
-  const int n_kblocks = (a.Nk + NW * 32 - 1) / (NW * 32);
-  if (n_kblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((fa_bwd_dkdv_f32_kernel<D, NW>),
-                     dim3((unsigned)((long long)n_kblocks * a.B * a.H)), dim3(NW * 64), 0,
-                     a.stream, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
-                     static_cast<const float*>(a.v), static_cast<const float*>(a.dout), a.lse,
-                     a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
-                     static_cast<float*>(a.dk), static_cast<float*>(a.dv), a.B, a.H, a.N, a.Nk,
-                     n_kblocks,
-                     a.cu_q, a.cu_k, a.total_q, a.total_k);
-  return hipGetLastError();
+  if constexpr (D >= 192) {
+    const int n_kblocks = (a.Nk + 31) / 32;
+    if (n_kblocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((fa_bwd_dkdv_f32_split_kernel<D>),
+                       dim3((unsigned)((long long)n_kblocks * a.B * a.H)), dim3(256), 0,
+                       a.stream, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                       static_cast<const float*>(a.v), static_cast<const float*>(a.dout), a.lse,
+                       a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
+                       static_cast<float*>(a.dk), static_cast<float*>(a.dv), a.B, a.H, a.N,
+                       a.Nk, n_kblocks, a.cu_q, a.cu_k, a.total_q, a.total_k);
+    return hipGetLastError();
+  } else {
+    constexpr int NW = F32BwdWaves<D>::DKDV;
+    const int n_kblocks = (a.Nk + NW * 32 - 1) / (NW * 32);
+    if (n_kblocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((fa_bwd_dkdv_f32_kernel<D, NW>),
+                       dim3((unsigned)((long long)n_kblocks * a.B * a.H)), dim3(NW * 64), 0,
+                       a.stream, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                       static_cast<const float*>(a.v), static_cast<const float*>(a.dout), a.lse,
+                       a.delta, a.seqlens_k, a.scale, a.scale * kLog2e, a.causal,
+                       static_cast<float*>(a.dk), static_cast<float*>(a.dv), a.B, a.H, a.N,
+                       a.Nk, n_kblocks, a.cu_q, a.cu_k, a.total_q, a.total_k);
+    return hipGetLastError();
+  }
 }
 
 template <int D>

@@ -188,7 +188,8 @@ def test_fp32_backward_phases_match_the_single_call():
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_head_dim_256_backward(dtype):
     """d = 256: four waves per work-group, one per SIMD, in the 16-bit
-    kernels; one-wave dK/dV blocks in the fp32 kernel."""
+    kernels; in the fp32 dK/dV kernel four waves share 32 keys and split the
+    feature dimension (partial S and dP added through LDS)."""
     torch = torch_cuda()
     for N in (1, 65, 200):
         for causal in (False, True):

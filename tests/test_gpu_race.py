@@ -63,6 +63,7 @@ CASES = [
     (5, dict(B=1, H=16, N=2048, d=128, causal=True, dtype="bf16"), None),
     (5, dict(B=2, H=3, N=333, d=96, causal=True, dtype="bf16"), [333, 200]),
     (5, dict(B=1, H=4, N=290, d=192, causal=False, dtype="f16"), None),
+    (5, dict(B=2, H=2, N=230, d=256, causal=True, dtype="f32"), [230, 97]),
 ]
 
 
